@@ -1,0 +1,20 @@
+"""CPU oracle of the sparse MoE FFN layer forward (numpy, float64).
+
+TEST INFRASTRUCTURE: a plain, slow, obviously correct implementation that the GPU path is
+checked against. Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+cpu_baseline leg may import it; the product path never does, and the oracle imports nothing
+from the product package.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py`` to something other
+than itself (closed forms, library routines, brute force, the pages' stated invariants,
+hand-worked fixtures under ``tests/golden/``). The Philox generator is pinned to rocRAND's
+Philox-4x32-10 called as a library.
+"""
+from . import philox
+from .moe_layer import (balance_stats, brute_dense, capacity, combine, dispatch, expert,
+                        expert_ffn, forward, forward_rows, gelu, logits, renormalise, route,
+                        scores, softmax, topk)
+
+__all__ = ["philox", "capacity", "logits", "scores", "softmax", "topk", "renormalise", "route",
+           "dispatch", "expert", "expert_ffn", "gelu", "combine", "balance_stats", "forward",
+           "forward_rows", "brute_dense"]

@@ -1,0 +1,268 @@
+"""Plain CPU oracle of the sparse MoE FFN layer's forward pass, in float64.
+
+TEST INFRASTRUCTURE. Nothing in the product path imports this module: only ``tests/``,
+``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline leg may use it. It shares no
+code with the HIP path. Inputs are the stored tensor values converted exactly to float64;
+nothing is rounded between steps except where a step below says so.
+
+Sources (pages cited by title or address and section):
+  [G]  the kwkr.cn page on sparse activation (news/623730; the page prints no title),
+       sections 2.1-2.3
+       (gate softmax, top-k on logits, second normalisation, combine, L_balance, capacity,
+       dropping) and 3.1-3.2 (Linear-GELU-Linear experts, stable sort by expert, per-expert
+       contiguous segments truncated at capacity, weighted scatter-add back to tokens).
+  [D]  "MoE模型：动态计算架构解析与实践指南" (intelliparadigm.com), sections 2.1 (expert =
+       Linear -> GeLU -> Linear), 2.3 (balance loss = E * sum(one-hot mean * softmax mean)),
+       3.1 (dense loop: every expert on every token, masked by routing).
+  [L]  "Mixture of Experts (MoE) 原理与工程落地全指南" (lpnh.cn), section 2.2 (Gumbel noise
+       added to the logits, divided by a temperature, then softmax).
+
+Readings taken where the pages leave a step open:
+  * top-k selects on the float32 scores s (logits, plus Gumbel noise, over tau); ties go to
+    the lower expert index; +0.0 and -0.0 are equal ([G] 2.1 says logits and probabilities
+    give the same order and that selection on logits is the safer one).
+  * the k selected probabilities are divided by their sum with no epsilon ([G] 2.1).
+  * C = ceil(c*k*T/E) from the exact value of the float c ([G] 2.3's formula).
+  * slots are ordered token-major (slot = t*k + j) and stably sorted by expert; within an
+    expert the first C slots (lowest token index) are kept ([G] 3.2).
+  * a dropped slot contributes 0 and the surviving weights are not renormalised ([G] 2.3).
+  * f_e = counts before dropping / (k*T); P_e = mean over tokens of the full softmax;
+    L = E * sum_e f_e * P_e, without the small outside coefficient ([G] 2.2, [D] 2.3).
+  * GeLU is the exact erf form 0.5 v (1 + erf(v / sqrt 2)) (nn.GELU's default; [G] 3.1).
+"""
+from __future__ import annotations
+
+import math
+from fractions import Fraction
+
+import numpy as np
+from scipy.special import erf
+
+from . import philox
+
+SQRT1_2 = 1.0 / math.sqrt(2.0)
+
+
+# ---------------------------------------------------------------- capacity ([G] 2.3)
+def capacity(T: int, E: int, k: int, c: float) -> int:
+    """C = ceil(c * k * T / E), in exact rational arithmetic on the float c."""
+    if not (T >= 1 and E >= 1 and k >= 1) or not (c > 0) or not math.isfinite(c):
+        raise ValueError("bad capacity arguments")
+    return math.ceil(Fraction(c) * k * T / E)
+
+
+# ---------------------------------------------------------------- router ([G] 2.1, [L] 2.2)
+def logits(x: np.ndarray, Wg: np.ndarray, bg: np.ndarray | None = None) -> np.ndarray:
+    """z[t, e] = sum_c x[t, c] * Wg[e, c] (+ bg[e]); Wg has nn.Linear's [out=E, in=d] layout."""
+    z = np.asarray(x, np.float64) @ np.asarray(Wg, np.float64).T
+    if bg is not None:
+        z = z + np.asarray(bg, np.float64)[None, :]
+    return z
+
+
+def scores(z32: np.ndarray, tau: float = 1.0, g32: np.ndarray | None = None) -> np.ndarray:
+    """float32 scores s = ((z + g) / tau), each operation rounded to float32.
+
+    z32 is the float32 logit; g32 the float32 Gumbel noise (None: no noise)."""
+    s = np.asarray(z32, np.float32)
+    if g32 is not None:
+        s = (s + np.asarray(g32, np.float32)).astype(np.float32)
+    if tau != 1.0:
+        s = (s / np.float32(tau)).astype(np.float32)
+    return s
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """Row softmax in float64: exp(s - max s) / sum exp(s - max s)."""
+    s = np.asarray(s, np.float64)
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def topk(s: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores per row, largest first, lower index first on ties."""
+    s = np.asarray(s)
+    T, E = s.shape
+    if not 1 <= k <= E:
+        raise ValueError("need 1 <= k <= E")
+    # Sort key (-s, e): a stable sort of -s keeps ascending e among equal values.
+    neg = -np.asarray(s, np.float64)
+    neg = np.where(neg == 0.0, 0.0, neg)          # fold -0.0 into +0.0
+    order = np.argsort(neg, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def renormalise(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """w[t, j] = p[t, idx[t, j]] / sum_j' p[t, idx[t, j']] (no epsilon)."""
+    sel = np.take_along_axis(np.asarray(p, np.float64), idx, axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None):
+    """Router step. Returns z (float64 logits), s (float32 scores), p, idx, w.
+
+    With ``given_scores`` (float32 [T,E]) the routing is re-derived from those scores
+    instead of the oracle's own logits (z is still the oracle's float64 logit)."""
+    z = logits(x, Wg, bg)
+    if given_scores is not None:
+        s = np.asarray(given_scores, np.float32)
+    else:
+        g32 = philox.gumbel_f32(seed, z.shape[0], z.shape[1]) if gumbel else None
+        s = scores(z.astype(np.float32), tau, g32)
+    p = softmax(s)
+    idx = topk(s, k)
+    w = renormalise(p, idx)
+    return {"z": z, "s": s, "p": p, "idx": idx, "w": w}
+
+
+# ---------------------------------------------------------------- dispatch ([G] 2.3, 3.2)
+def dispatch(idx: np.ndarray, E: int, C: int) -> dict:
+    """Capacity-limited stable dispatch of the flattened slots (slot = t*k + j).
+
+    Returns counts, kept, offsets, drops [E]; dest [T,k] (row in the expert-sorted buffer,
+    -1 when dropped); perm [sum kept] (source token of each row)."""
+    idx = np.asarray(idx, np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    order = np.argsort(flat, kind="stable")          # slots grouped by expert, token order kept
+    seg_start = np.concatenate([[0], np.cumsum(counts)[:-1]])
+    rank = np.empty(T * k, dtype=np.int64)
+    rank[order] = np.arange(T * k) - seg_start[flat[order]]
+    kept = np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(kept)[:-1]]).astype(np.int64)
+    keep = rank < C
+    dest = np.where(keep, offsets[flat] + rank, -1).reshape(T, k)
+    perm = np.empty(int(kept.sum()), dtype=np.int64)
+    tok = np.repeat(np.arange(T), k)
+    perm[dest.reshape(-1)[keep]] = tok[keep]
+    return {"counts": counts, "kept": kept, "offsets": offsets, "drops": counts - kept,
+            "dest": dest, "perm": perm, "C": C}
+
+
+# ---------------------------------------------------------------- experts ([G] 3.1, [D] 2.1)
+def gelu(v: np.ndarray) -> np.ndarray:
+    return 0.5 * v * (1.0 + erf(v * SQRT1_2))
+
+
+def expert(xr, W1e, b1e, W2e, b2e) -> np.ndarray:
+    """One expert on rows xr: Linear(d -> d_ffn) -> GeLU -> Linear(d_ffn -> d)."""
+    h = np.asarray(xr, np.float64) @ np.asarray(W1e, np.float64).T
+    if b1e is not None:
+        h = h + np.asarray(b1e, np.float64)
+    h = gelu(h)
+    y = h @ np.asarray(W2e, np.float64).T
+    if b2e is not None:
+        y = y + np.asarray(b2e, np.float64)
+    return y
+
+
+def expert_ffn(x_perm, kept, offsets, W1, b1, W2, b2) -> np.ndarray:
+    """Each expert e runs on its own contiguous segment of the expert-sorted rows."""
+    y_perm = np.zeros((x_perm.shape[0], W2.shape[1]), dtype=np.float64)
+    for e in range(len(kept)):
+        n = int(kept[e])
+        if n == 0:
+            continue
+        lo = int(offsets[e])
+        y_perm[lo:lo + n] = expert(x_perm[lo:lo + n], W1[e], None if b1 is None else b1[e],
+                                   W2[e], None if b2 is None else b2[e])
+    return y_perm
+
+
+# ---------------------------------------------------------------- combine ([G] 2.1, 3.2)
+def combine(y_perm: np.ndarray, dest: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y[t] = sum over kept slots j (in j order) of w[t, j] * y_perm[dest[t, j]]."""
+    T, k = dest.shape
+    y = np.zeros((T, y_perm.shape[1]), dtype=np.float64)
+    for j in range(k):
+        m = dest[:, j] >= 0
+        y[m] += w[m, j, None] * y_perm[dest[m, j]]
+    return y
+
+
+# ---------------------------------------------------------------- statistics ([G] 2.2, [D] 2.3)
+def balance_stats(counts: np.ndarray, p: np.ndarray, k: int) -> dict:
+    """f_e = counts_e / (k T); P_e = mean_t p[t, e]; L = E * sum_e f_e P_e."""
+    T, E = p.shape
+    f = np.asarray(counts, np.float64) / float(k * T)
+    P = np.asarray(p, np.float64).mean(axis=0)
+    return {"f": f, "P": P, "L": float(E * np.sum(f * P))}
+
+
+# ---------------------------------------------------------------- whole layer
+def forward(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=False,
+            seed=0, given_scores=None) -> dict:
+    """The layer: route -> dispatch -> gather -> experts -> combine, plus f, P, L."""
+    T, d = x.shape
+    E = Wg.shape[0]
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
+    C = capacity(T, E, k, capacity_factor)
+    dsp = dispatch(r["idx"], E, C)
+    x_perm = np.asarray(x, np.float64)[dsp["perm"]]
+    y_perm = expert_ffn(x_perm, dsp["kept"], dsp["offsets"], W1, b1, W2, b2)
+    y = combine(y_perm, dsp["dest"], r["w"])
+    st = balance_stats(dsp["counts"], r["p"], k)
+    out = dict(r)
+    out.update(dsp)
+    out.update(st)
+    out.update({"x_perm": x_perm, "y_perm": y_perm, "y": y})
+    return out
+
+
+def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0,
+                 gumbel=False, seed=0, given_scores=None) -> dict:
+    """The layer's output for selected tokens only, at any size.
+
+    Routing and dispatch are done for all tokens (they decide which slots survive); the
+    experts run only on the selected tokens' kept slots, one row at a time."""
+    T, d = x.shape
+    E = Wg.shape[0]
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
+    C = capacity(T, E, k, capacity_factor)
+    dsp = dispatch(r["idx"], E, C)
+    rows = np.asarray(rows, np.int64)
+    y = np.zeros((len(rows), W2.shape[1]), dtype=np.float64)
+    for i, t in enumerate(rows):
+        xt = np.asarray(x[t], np.float64)[None, :]
+        for j in range(k):
+            if dsp["dest"][t, j] < 0:
+                continue
+            e = int(r["idx"][t, j])
+            y[i] += r["w"][t, j] * expert(xt, W1[e], None if b1 is None else b1[e],
+                                          W2[e], None if b2 is None else b2[e])[0]
+    st = balance_stats(dsp["counts"], r["p"], k)
+    out = dict(r)
+    out.update(dsp)
+    out.update(st)
+    out["y_rows"] = y
+    return out
+
+
+# ---------------------------------------------------------------- brute force (tiny sizes)
+def brute_dense(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=False,
+                seed=0, given_scores=None) -> dict:
+    """Every expert on every token, masked by routing and capacity ([D] 3.1's dense loop).
+
+    Capacity is applied from its definition: slot (t, j) with expert e survives iff fewer
+    than C earlier tokens t' < t chose e. O(T^2 k^2); tiny inputs only."""
+    T, d = x.shape
+    E = Wg.shape[0]
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
+    C = capacity(T, E, k, capacity_factor)
+    idx, w = r["idx"], r["w"]
+    keep = np.zeros((T, k), dtype=bool)
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            earlier = sum(1 for t2 in range(t) if e in idx[t2])
+            keep[t, j] = earlier < C
+    y = np.zeros((T, W2.shape[1]), dtype=np.float64)
+    for e in range(E):
+        ye = expert(x, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+        mask = np.zeros(T, dtype=np.float64)
+        for j in range(k):
+            mask += np.where((idx[:, j] == e) & keep[:, j], w[:, j], 0.0)
+        y += mask[:, None] * ye
+    return {"y": y, "keep": keep, "idx": idx, "w": w, "C": C}
