@@ -1,0 +1,178 @@
+#!/usr/bin/env python3
+"""Throughput of the sparse MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_like]
+
+One step is one moe_forward call (router + softmax + top-k, capacity dispatch, grouped expert
+GEMMs with GeLU, combine and the balance statistic) over one batch of seeded synthetic input
+already resident in HBM. W untimed warm-up steps, then exactly K timed steps between two
+device synchronisations. Prints one JSON line:
+  value         tokens/s of the whole layer (T tokens per step);
+  stage_ms      per-stage means from HIP events recorded inside moe_forward on its stream;
+  roofline      the dominant expert GEMM kernel: algorithmic FLOPs (2 d d_ffn per kept row)
+                over its measured duration, against the bf16 dense MFMA peak (2.5 PFLOP/s);
+  cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def _args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_like")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512,
+                    help="tokens in the batch the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    return ap.parse_args()
+
+
+def cpu_baseline(shape, arrays, n_tokens: int) -> dict:
+    """The oracle as it stands, timed on the host cores on the first n_tokens tokens."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import oracle
+    from workloads import bf16_bits_to_f32
+
+    cores = len(os.sched_getaffinity(0))
+    dt = shape.dtype
+
+    def val(a):
+        if a is None:
+            return None
+        return bf16_bits_to_f32(a) if (dt == "bf16" and a.dtype == np.uint16) else np.asarray(a, np.float32)
+
+    x = val(arrays["x"])[:n_tokens]
+    args = (x, val(arrays["Wg"]), arrays["bg"], val(arrays["W1"]), val(arrays["b1"]), val(arrays["W2"]),
+            val(arrays["b2"]))
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        out = oracle.forward(*args, k=shape.k, capacity_factor=shape.capacity_factor, tau=shape.temperature,
+                             gumbel=shape.gumbel, seed=shape.seed)
+        t1 = time.perf_counter()
+        blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()]
+    assert np.isfinite(out["y"]).all()
+    return {"value": n_tokens / (t1 - t0), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of the {shape.name} input as one batch "
+                      f"(C recomputed for T={n_tokens}), numpy float64, {', '.join(blas)}",
+            "seconds": t1 - t0}
+
+
+def main() -> int:
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(no collectives or sharding are implemented).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_41_amd import ops
+    from workloads import CONFIGS, make_inputs
+
+    shape = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    arrays = make_inputs(shape)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+        return torch.from_numpy(a).cuda()
+
+    tensors = [dev(arrays[n]) for n in ("x", "Wg", "bg", "W1", "b1", "W2", "b2")]
+    cfg = ops.make_config(shape.T, shape.d, shape.E, shape.k, shape.d_ffn, shape.capacity_factor,
+                          shape.temperature, shape.gumbel, shape.seed, shape.dtype)
+    plan = ops.ForwardPlan(cfg, *tensors, keep_routing=False)
+    for _ in range(args.warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    events = [ops.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan.run(events=events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage = {n: 0.0 for n in ops.STAGE_NAMES}
+    for ev in events:
+        for n, v in zip(ops.STAGE_NAMES, ev.accumulate()):
+            stage[n] += v / args.steps
+        ev.close()
+
+    kept = int(plan.out["kept"].sum().item())
+    counts = plan.out["counts"].cpu().numpy()
+    T, d, E, k, dff = shape.T, shape.d, shape.E, shape.k, shape.d_ffn
+    sx = 2 if shape.dtype == "bf16" else 4
+    gemm_flops = 2.0 * d * dff * kept                       # per GEMM launch, kept rows only
+    g1, g2 = stage["expert_gemm1_gelu"], stage["expert_gemm2"]
+    dom_name, dom_ms = ("expert_gemm1_gelu", g1) if g1 >= g2 else ("expert_gemm2", g2)
+    achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(dom_name)
+    nb = (T + 63) // 64
+    router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + nb * E * 8
+    dispatch_bytes = T * k * 4 + T * k * 4 + kept * 4 + 2 * kept * d * sx
+    combine_bytes = kept * d * 4 + T * k * 8 + T * d * sx
+    disp_ms = stage["scan"] + stage["permute_gather"]
+    line = {
+        "metric": "MoE-layer tokens/sec (bf16, 1 GPU) + grouped-GEMM % of bf16 MFMA peak",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded; workloads.make_inputs)",
+        "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "d_ffn": dff,
+                   "capacity_factor": shape.capacity_factor, "temperature": shape.temperature,
+                   "gumbel": shape.gumbel, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "grouped_gemm": {"tflops": 2 * gemm_flops / ((g1 + g2) * 1e-3) / 1e12,
+                         "frac_of_peak": 2 * gemm_flops / ((g1 + g2) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "kept_rows": kept, "dropped_slots": int(k * T - kept)},
+        "hbm_stages": {
+            "router": {"GB/s": router_bytes / (stage["route"] * 1e-3) / 1e9, "bytes": router_bytes},
+            "dispatch": {"GB/s": dispatch_bytes / (disp_ms * 1e-3) / 1e9, "bytes": dispatch_bytes},
+            "combine": {"GB/s": combine_bytes / (stage["combine"] * 1e-3) / 1e9, "bytes": combine_bytes},
+            "peak_GB/s": PEAK_HBM_GBS,
+        },
+        "stage_ms": stage,
+        "counts_minmax": [int(counts.min()), int(counts.max())],
+    }
+    if args.cpu_sample_tokens > 0:
+        line["cpu_baseline"] = cpu_baseline(shape, arrays, min(args.cpu_sample_tokens, T))
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,163 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN layer forward.
+ *
+ * The layer (kwkr.cn page on sparse activation, news/623730, sections 2.1-2.3 and 3.1-3.2):
+ *   1. router:   z = x W_g^T (+ b_g), float32 logits; scores s = (z + g) / tau, with g the
+ *                Gumbel noise of the Gumbel-softmax router ("Mixture of Experts (MoE)
+ *                原理与工程落地全指南", lpnh.cn, section 2.2) when enabled, else s = z / tau;
+ *                p = softmax(s) in float32.
+ *   2. top-k:    the k largest scores per token, largest first, lower expert index first on
+ *                equal scores; weights w_j = p[idx_j] / sum_j' p[idx_j'] (sum to 1).
+ *   3. dispatch: C = ceil(c k T / E); slots (t, j) taken in token order; each expert keeps its
+ *                first C slots, later ones are dropped (contribute zero).
+ *   4. experts:  H = GeLU(x_e W1_e^T + b1_e) (exact erf GeLU), y_e = H W2_e^T + b2_e, run only on
+ *                each expert's own kept rows.
+ *   5. combine:  y[t] = sum over kept j of w[t,j] * y_e[t]; and the balance statistic
+ *                f_e = counts_e / (k T), P_e = mean_t p[t,e], L = E sum_e f_e P_e.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, row-major and contiguous, owned by the caller.
+ *     Weights use nn.Linear's [out, in] layout: W_g [E,d], W1 [E,d_ffn,d], W2 [E,d,d_ffn].
+ *   - "dtype" tensors (x, W_g, W1, b1, W2, b2, x_perm, y) are bfloat16 or float32 per
+ *     moe_config.dtype; b_g, logits, scores, weights, y_perm and statistics are float32;
+ *     indices and counts are int32.
+ *   - Alignment: dtype and float tensors 16 bytes, int32 arrays 4 bytes, the workspace 256
+ *     bytes. Optional (nullable) pointers are marked.
+ *   - Every call is asynchronous on `stream` (NULL = the default stream) and does no host
+ *     synchronisation; results are valid once the caller synchronises the stream. The
+ *     library allocates nothing and keeps no state between calls.
+ *   - Arguments are validated before anything is enqueued; on any error nothing is enqueued
+ *     and a status is returned (never printed, never aborted). Detail: moe_last_error().
+ *   - Rows of the expert-sorted buffers (x_perm, y_perm, perm) beyond sum(kept) are left
+ *     untouched.
+ *   - Results are deterministic: no floating-point atomics; every sum has a fixed order.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque handles; these are hipStream_t and hipEvent_t. */
+typedef struct ihipStream_t* moe_stream_t;
+typedef struct ihipEvent_t* moe_event_t;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null required pointer, bad size, k > E, c or tau <= 0 / not finite,
+                            misaligned pointer, k*T >= 2^31 */
+  MOE_EUNSUPPORTED = 2,  /* E > 64, k > 8, bf16 with d or d_ffn not a multiple of 64, float32
+                            beyond its size limits, c > 2^20 */
+  MOE_EWORKSPACE = 3,    /* workspace smaller than moe_workspace_size() */
+  MOE_EHIP = 4           /* a HIP launch error; text in moe_last_error() */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Layer configuration (kwkr.cn page, section 2: T tokens, d model dim, E experts, top-k,
+ * capacity factor c; section 3.1: expert hidden width d_ffn). */
+typedef struct moe_config {
+  int64_t T;               /* tokens (a [B,S,d] batch flattened to [T,d]; t = b*S + s)      */
+  int64_t d;               /* model dimension                                              */
+  int64_t E;               /* experts, 1..64                                               */
+  int64_t k;               /* experts per token, 1..min(E, 8)                              */
+  int64_t d_ffn;           /* expert hidden dimension                                      */
+  double capacity_factor;  /* c > 0; C = ceil(c*k*T/E) from the exact value of this double */
+  float temperature;       /* tau > 0; 1 = plain softmax                                   */
+  int32_t gumbel;          /* 0: s = z/tau. 1: s = (z + g)/tau, g = -log(-log u) with u from
+                              Philox-4x32-10, key = (seed mod 2^32, seed >> 32),
+                              counter = (t, e, 0, 0), u = (word0 + 1/2) 2^-32, computed in
+                              float64 and rounded once to float32                          */
+  uint64_t seed;           /* Philox key when gumbel = 1                                    */
+  int32_t dtype;           /* moe_dtype: storage of x, weights, x_perm, H and y            */
+  int32_t reserved;        /* must be 0                                                    */
+} moe_config;
+
+/* Number of kernel stages of moe_forward (route, scan, permute+gather, expert GEMM1+GeLU,
+ * expert GEMM2, combine); moe_forward_aux.stage_events takes MOE_FORWARD_STAGES + 1 events. */
+#define MOE_FORWARD_STAGES 6
+
+/* Optional extra outputs of moe_forward. Every pointer may be NULL. */
+typedef struct moe_forward_aux {
+  float* logits;           /* [T,E] float32 z                                               */
+  float* scores;           /* [T,E] float32 s (equal to the logits when gumbel = 0, tau = 1) */
+  int32_t* topk_idx;       /* [T,k]                                                         */
+  float* topk_w;           /* [T,k]                                                         */
+  int32_t* offsets;        /* [E] exclusive prefix sum of kept                              */
+  int32_t* dest;           /* [T,k] row of slot (t,j) in the expert-sorted buffer, -1 = dropped */
+  int32_t* perm;           /* [min(k*T, E*C)] source token of each expert-sorted row        */
+  float* prob_colsum;      /* [E] sum_t p[t,e]                                              */
+  moe_event_t* stage_events; /* NULL, or MOE_FORWARD_STAGES+1 created events, recorded on
+                                `stream` before each stage and after the last              */
+} moe_forward_aux;
+
+/* C = ceil(c*k*T/E) (kwkr.cn page, section 2.3), exact integer arithmetic on the double c.
+ * Host only. Returns -1 when the configuration is invalid. */
+int64_t moe_capacity(const moe_config* cfg);
+
+/* Workspace bytes that every entry point below needs for `cfg` (the largest is moe_forward's:
+ * per-block partial sums and histograms, routing arrays, x_perm, H and y_perm). Host only. */
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Router: steps 1-2 (kwkr.cn page, section 2.1; lpnh.cn page, section 2.2).
+ *   x [T,d] dtype, Wg [E,d] dtype, bg [E] float32 (nullable)
+ *   -> logits [T,E] f32; scores [T,E] f32 (nullable; written when non-NULL);
+ *      topk_idx [T,k] i32; topk_w [T,k] f32; prob_colsum [E] f32 = sum_t p[t,e]. */
+moe_status moe_route(const moe_config* cfg, const void* x, const void* Wg, const float* bg,
+                     float* logits, float* scores, int32_t* topk_idx, float* topk_w,
+                     float* prob_colsum, void* ws, size_t ws_bytes, moe_stream_t stream);
+
+/* Dispatch: step 3 (kwkr.cn page, sections 2.3 and 3.2): per-expert histogram, prefix scan,
+ * capacity truncation and the stable permutation, then the row gather x_perm[r] = x[perm[r]].
+ *   topk_idx [T,k] i32 (each row k distinct experts in [0,E)), x [T,d] dtype
+ *   -> counts, kept, offsets [E] i32; dest [T,k] i32 (-1 = dropped);
+ *      perm [min(k*T, E*C)] i32; x_perm [min(k*T, E*C), d] dtype. */
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* x,
+                        int32_t* counts, int32_t* kept, int32_t* offsets, int32_t* dest,
+                        int32_t* perm, void* x_perm, void* ws, size_t ws_bytes,
+                        moe_stream_t stream);
+
+/* Experts: step 4 (kwkr.cn page, section 3.1; intelliparadigm.com page, section 2.1):
+ * rows [offsets[e], offsets[e]+kept[e]) of x_perm go through expert e.
+ *   x_perm [R,d] dtype, kept/offsets [E] i32 (as moe_dispatch writes them),
+ *   W1 [E,d_ffn,d], b1 [E,d_ffn] (nullable), W2 [E,d,d_ffn], b2 [E,d] (nullable), all dtype
+ *   -> y_perm [R,d] f32. H [R,d_ffn] lives in the workspace. */
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* kept,
+                          const int32_t* offsets, const void* W1, const void* b1, const void* W2,
+                          const void* b2, float* y_perm, void* ws, size_t ws_bytes,
+                          moe_stream_t stream);
+
+/* Combine and statistics: step 5 (kwkr.cn page, sections 2.1, 2.2 and 3.2; intelliparadigm.com
+ * page, section 2.3). y[t] = sum_j w[t,j] * y_perm[dest[t,j]] over kept slots, in j order, in
+ * float32, rounded once to dtype; a token whose slots were all dropped gets y = 0.
+ *   y_perm [R,d] f32, dest [T,k] i32, topk_w [T,k] f32, counts [E] i32, prob_colsum [E] f32
+ *   -> y [T,d] dtype; f [E], P [E], L [1] f32 (f, P, L nullable together). */
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* dest,
+                       const float* topk_w, const int32_t* counts, const float* prob_colsum,
+                       void* y, float* f, float* P, float* L, void* ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* The whole layer, steps 1-5, on one stream with no host synchronisation.
+ *   x, Wg, bg, W1, b1, W2, b2 as above -> y [T,d] dtype; f, P [E] f32; L [1] f32;
+ *   counts, kept [E] i32; aux (nullable) for the intermediate results and stage timing. */
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, const float* bg,
+                       const void* W1, const void* b1, const void* W2, const void* b2,
+                       void* y, float* f, float* P, float* L, int32_t* counts, int32_t* kept,
+                       const moe_forward_aux* aux, void* ws, size_t ws_bytes,
+                       moe_stream_t stream);
+
+/* Static text of a status code. */
+const char* moe_status_str(moe_status status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

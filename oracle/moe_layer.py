@@ -99,6 +99,15 @@ def renormalise(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return sel / sel.sum(axis=1, keepdims=True)
 
 
+def route_from_scores(s: np.ndarray, k: int) -> dict:
+    """Softmax, top-k and renormalised weights from float32 scores s [T,E]."""
+    s = np.asarray(s, np.float32)
+    p = softmax(s)
+    idx = topk(s, k)
+    w = renormalise(p, idx)
+    return {"s": s, "p": p, "idx": idx, "w": w}
+
+
 def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None):
     """Router step. Returns z (float64 logits), s (float32 scores), p, idx, w.
 
@@ -110,10 +119,9 @@ def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None):
     else:
         g32 = philox.gumbel_f32(seed, z.shape[0], z.shape[1]) if gumbel else None
         s = scores(z.astype(np.float32), tau, g32)
-    p = softmax(s)
-    idx = topk(s, k)
-    w = renormalise(p, idx)
-    return {"z": z, "s": s, "p": p, "idx": idx, "w": w}
+    out = route_from_scores(s, k)
+    out["z"] = z
+    return out
 
 
 # ---------------------------------------------------------------- dispatch ([G] 2.3, 3.2)
@@ -215,23 +223,28 @@ def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0
                  gumbel=False, seed=0, given_scores=None) -> dict:
     """The layer's output for selected tokens only, at any size.
 
-    Routing and dispatch are done for all tokens (they decide which slots survive); the
-    experts run only on the selected tokens' kept slots, one row at a time."""
+    Routing and dispatch are done for all tokens (they decide which slots survive); each
+    expert then runs only on the selected tokens' kept slots that chose it, and each
+    selected token sums its slots in j order."""
     T, d = x.shape
     E = Wg.shape[0]
     r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
     C = capacity(T, E, k, capacity_factor)
     dsp = dispatch(r["idx"], E, C)
     rows = np.asarray(rows, np.int64)
+    contrib = np.zeros((len(rows), k, W2.shape[1]), dtype=np.float64)
+    for e in range(E):
+        sel = [(i, j) for i, t in enumerate(rows) for j in range(k)
+               if r["idx"][t, j] == e and dsp["dest"][t, j] >= 0]
+        if not sel:
+            continue
+        xe = np.asarray(x[[rows[i] for i, _ in sel]], np.float64)
+        ye = expert(xe, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+        for n, (i, j) in enumerate(sel):
+            contrib[i, j] = r["w"][rows[i], j] * ye[n]
     y = np.zeros((len(rows), W2.shape[1]), dtype=np.float64)
-    for i, t in enumerate(rows):
-        xt = np.asarray(x[t], np.float64)[None, :]
-        for j in range(k):
-            if dsp["dest"][t, j] < 0:
-                continue
-            e = int(r["idx"][t, j])
-            y[i] += r["w"][t, j] * expert(xt, W1[e], None if b1 is None else b1[e],
-                                          W2[e], None if b2 is None else b2[e])[0]
+    for j in range(k):
+        y += contrib[:, j]
     st = balance_stats(dsp["counts"], r["p"], k)
     out = dict(r)
     out.update(dsp)

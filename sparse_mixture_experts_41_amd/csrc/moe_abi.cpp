@@ -1,0 +1,445 @@
+// C ABI of the MoE layer: argument validation, workspace carving and stage orchestration.
+// Every check happens before the first HIP call, so an invalid call enqueues nothing.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <string>
+
+#include "moe_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+struct Derived {
+  int T, d, E, k, dff;
+  int64_t C;
+  int R;       // rows of the expert-sorted buffers: min(k*T, E*C)
+  int nb;      // 64-token routing blocks
+  bool bf16;
+  size_t esize;
+  float tau;
+  int gumbel;
+  uint32_t key0, key1;
+};
+
+struct Layout {
+  size_t probsum, hist, blockbase, colsum, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm, total;
+};
+
+// C = ceil(c*k*T/E) for the exact value of the double c = m * 2^sh (m a 53-bit integer).
+int64_t capacity_exact(int64_t T, int64_t E, int64_t k, double c) {
+  int q = 0;
+  const double fr = std::frexp(c, &q);                     // c = fr * 2^q, fr in [0.5, 1)
+  const uint64_t m = static_cast<uint64_t>(std::ldexp(fr, 53));
+  const int sh = q - 53;
+  const unsigned __int128 num = static_cast<unsigned __int128>(m) * static_cast<uint64_t>(k * T);
+  if (sh >= 0) {                                           // c >= 2^53: far beyond any token count
+    return INT64_MAX;
+  }
+  if (-sh > 100) return 1;                                 // c*k*T/E < 2^84 / 2^100 < 1, and > 0
+  const unsigned __int128 den = static_cast<unsigned __int128>(E) << (-sh);
+  const unsigned __int128 C = (num + den - 1) / den;
+  return C > static_cast<unsigned __int128>(INT64_MAX) ? INT64_MAX : static_cast<int64_t>(C);
+}
+
+moe_status check_config(const moe_config* cfg, Derived* D) {
+  if (cfg == nullptr) return fail(MOE_EINVAL, "cfg is NULL");
+  const int64_t T = cfg->T, d = cfg->d, E = cfg->E, k = cfg->k, dff = cfg->d_ffn;
+  if (T < 1 || d < 1 || E < 1 || k < 1 || dff < 1) return fail(MOE_EINVAL, "T, d, E, k and d_ffn must be >= 1");
+  if (k > E) return fail(MOE_EINVAL, "k must not exceed E");
+  if (!(cfg->capacity_factor > 0.0) || !std::isfinite(cfg->capacity_factor))
+    return fail(MOE_EINVAL, "capacity_factor must be finite and > 0");
+  if (!(cfg->temperature > 0.0f) || !std::isfinite(cfg->temperature))
+    return fail(MOE_EINVAL, "temperature must be finite and > 0");
+  if (cfg->gumbel != 0 && cfg->gumbel != 1) return fail(MOE_EINVAL, "gumbel must be 0 or 1");
+  if (cfg->dtype != MOE_F32 && cfg->dtype != MOE_BF16) return fail(MOE_EINVAL, "unknown dtype");
+  if (cfg->reserved != 0) return fail(MOE_EINVAL, "reserved must be 0");
+  if (T > (int64_t(1) << 31) || T * k >= (int64_t(1) << 31)) return fail(MOE_EINVAL, "k*T must be below 2^31");
+  if (E > 64) return fail(MOE_EUNSUPPORTED, "at most 64 experts");
+  if (k > 8) return fail(MOE_EUNSUPPORTED, "at most k = 8");
+  if (d > 65536 || dff > 65536) return fail(MOE_EUNSUPPORTED, "d and d_ffn are limited to 65536");
+  if (cfg->capacity_factor > 1048576.0) return fail(MOE_EUNSUPPORTED, "capacity_factor above 2^20");
+  const bool bf16 = cfg->dtype == MOE_BF16;
+  if (bf16) {
+    if (d % 64 != 0 || dff % 64 != 0) return fail(MOE_EUNSUPPORTED, "bf16 needs d and d_ffn multiples of 64");
+  } else {
+    if (d % 8 != 0 || dff % 8 != 0) return fail(MOE_EUNSUPPORTED, "float32 needs d and d_ffn multiples of 8");
+    if (T > 65536 || d > 4096 || dff > 16384)
+      return fail(MOE_EUNSUPPORTED, "float32 is a correctness path: T <= 65536, d <= 4096, d_ffn <= 16384");
+  }
+  D->T = static_cast<int>(T);
+  D->d = static_cast<int>(d);
+  D->E = static_cast<int>(E);
+  D->k = static_cast<int>(k);
+  D->dff = static_cast<int>(dff);
+  D->C = capacity_exact(T, E, k, cfg->capacity_factor);
+  const int64_t ecap = D->C >= T ? E * T : E * D->C;        // an expert never gets more than T slots
+  const int64_t R = (k * T < ecap) ? k * T : ecap;
+  D->R = static_cast<int>(R);
+  D->nb = static_cast<int>((T + 63) / 64);
+  D->bf16 = bf16;
+  D->esize = bf16 ? 2 : 4;
+  D->tau = cfg->temperature;
+  D->gumbel = cfg->gumbel;
+  D->key0 = static_cast<uint32_t>(cfg->seed & 0xffffffffull);
+  D->key1 = static_cast<uint32_t>(cfg->seed >> 32);
+  return MOE_OK;
+}
+
+Layout layout_of(const Derived& D) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~static_cast<size_t>(255);
+    return o;
+  };
+  const size_t T = D.T, E = D.E, k = D.k, nb = D.nb, R = D.R;
+  L.probsum = take(nb * E * 4);
+  L.hist = take(nb * E * 4);
+  L.blockbase = take(nb * E * 4);
+  L.colsum = take(E * 4);
+  L.logits = take(T * E * 4);
+  L.scores = take(T * E * 4);
+  L.idx = take(T * k * 4);
+  L.w = take(T * k * 4);
+  L.offsets = take(E * 4);
+  L.dest = take(T * k * 4);
+  L.perm = take(R * 4);
+  L.x_perm = take(R * static_cast<size_t>(D.d) * D.esize);
+  L.H = take(R * static_cast<size_t>(D.dff) * D.esize);
+  L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
+  L.total = off;
+  return L;
+}
+
+moe_status need(const void* p, size_t align, const char* name, bool nullable = false) {
+  if (p == nullptr) {
+    if (nullable) return MOE_OK;
+    return fail(MOE_EINVAL, std::string(name) + " is NULL");
+  }
+  if ((reinterpret_cast<uintptr_t>(p) & (align - 1)) != 0)
+    return fail(MOE_EINVAL, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+  return MOE_OK;
+}
+
+moe_status need_ws(const Derived& D, const void* ws, size_t ws_bytes, Layout* L) {
+  *L = layout_of(D);
+  if (ws_bytes < L->total)
+    return fail(MOE_EWORKSPACE, "workspace needs " + std::to_string(L->total) + " bytes, got " + std::to_string(ws_bytes));
+  return need(ws, 256, "ws");
+}
+
+moe_status hip_fail(hipError_t e, const char* where) {
+  return fail(MOE_EHIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+#define MOE_CHECK(expr)                 \
+  do {                                  \
+    const moe_status s_ = (expr);       \
+    if (s_ != MOE_OK) return s_;        \
+  } while (0)
+
+#define MOE_HIP(expr, where)                             \
+  do {                                                   \
+    const hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return hip_fail(e_, where);    \
+  } while (0)
+
+moe::RouterArgs router_args(const Derived& D, const void* x, const void* Wg, const float* bg, float* logits,
+                            float* scores, int32_t* idx, float* w, float* probsum, int32_t* hist) {
+  moe::RouterArgs a{};
+  a.x = x;
+  a.Wg = Wg;
+  a.bg = bg;
+  a.T = D.T;
+  a.d = D.d;
+  a.E = D.E;
+  a.k = D.k;
+  a.bf16 = D.bf16 ? 1 : 0;
+  a.tau = D.tau;
+  a.gumbel = D.gumbel;
+  a.key0 = D.key0;
+  a.key1 = D.key1;
+  a.logits = logits;
+  a.scores = scores;
+  a.idx = idx;
+  a.w = w;
+  a.probsum_part = probsum;
+  a.hist = hist;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(const moe_config* cfg) {
+  Derived D;
+  if (check_config(cfg, &D) != MOE_OK) return -1;
+  return D.C;
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+  Derived D;
+  MOE_CHECK(check_config(cfg, &D));
+  if (bytes == nullptr) return fail(MOE_EINVAL, "bytes is NULL");
+  *bytes = layout_of(D).total;
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const void* Wg, const float* bg, float* logits,
+                     float* scores, int32_t* topk_idx, float* topk_w, float* prob_colsum, void* ws, size_t ws_bytes,
+                     moe_stream_t stream) {
+  Derived D;
+  Layout L;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(need(x, 16, "x"));
+  MOE_CHECK(need(Wg, 16, "Wg"));
+  MOE_CHECK(need(bg, 4, "bg", true));
+  MOE_CHECK(need(logits, 4, "logits"));
+  MOE_CHECK(need(scores, 4, "scores", true));
+  MOE_CHECK(need(topk_idx, 4, "topk_idx"));
+  MOE_CHECK(need(topk_w, 4, "topk_w"));
+  MOE_CHECK(need(prob_colsum, 4, "prob_colsum"));
+  MOE_CHECK(need_ws(D, ws, ws_bytes, &L));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const moe::RouterArgs a = router_args(D, x, Wg, bg, logits, scores, topk_idx, topk_w, at<float>(ws, L.probsum),
+                                        at<int32_t>(ws, L.hist));
+  MOE_HIP(moe::launch_router(a, st), "router");
+  MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.nb, D.E, prob_colsum, st), "colsum");
+  return MOE_OK;
+}
+
+moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const void* x, int32_t* counts,
+                        int32_t* kept, int32_t* offsets, int32_t* dest, int32_t* perm, void* x_perm, void* ws,
+                        size_t ws_bytes, moe_stream_t stream) {
+  Derived D;
+  Layout L;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(need(topk_idx, 4, "topk_idx"));
+  MOE_CHECK(need(x, 16, "x"));
+  MOE_CHECK(need(counts, 4, "counts"));
+  MOE_CHECK(need(kept, 4, "kept"));
+  MOE_CHECK(need(offsets, 4, "offsets"));
+  MOE_CHECK(need(dest, 4, "dest"));
+  MOE_CHECK(need(perm, 4, "perm"));
+  MOE_CHECK(need(x_perm, 16, "x_perm"));
+  MOE_CHECK(need_ws(D, ws, ws_bytes, &L));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  int32_t* hist = at<int32_t>(ws, L.hist);
+  int32_t* blockbase = at<int32_t>(ws, L.blockbase);
+  MOE_HIP(moe::launch_histogram(topk_idx, D.T, D.E, D.k, hist, st), "histogram");
+  moe::ScanArgs s{};
+  s.hist = hist;
+  s.nb = D.nb;
+  s.E = D.E;
+  s.k = D.k;
+  s.T = D.T;
+  s.C = static_cast<int>(D.C < D.T ? D.C : D.T);
+  s.counts = counts;
+  s.kept = kept;
+  s.offsets = offsets;
+  s.blockbase = blockbase;
+  MOE_HIP(moe::launch_scan(s, st), "scan");
+  MOE_HIP(moe::launch_permute(topk_idx, blockbase, offsets, D.T, D.E, D.k, s.C, dest, perm, st), "permute");
+  MOE_HIP(moe::launch_gather(x, perm, kept, offsets, D.E, D.R, static_cast<int>(D.d * D.esize), x_perm, st),
+          "gather");
+  return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32_t* kept, const int32_t* offsets,
+                          const void* W1, const void* b1, const void* W2, const void* b2, float* y_perm, void* ws,
+                          size_t ws_bytes, moe_stream_t stream) {
+  Derived D;
+  Layout L;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(need(x_perm, 16, "x_perm"));
+  MOE_CHECK(need(kept, 4, "kept"));
+  MOE_CHECK(need(offsets, 4, "offsets"));
+  MOE_CHECK(need(W1, 16, "W1"));
+  MOE_CHECK(need(b1, D.esize, "b1", true));
+  MOE_CHECK(need(W2, 16, "W2"));
+  MOE_CHECK(need(b2, D.esize, "b2", true));
+  MOE_CHECK(need(y_perm, 16, "y_perm"));
+  MOE_CHECK(need_ws(D, ws, ws_bytes, &L));
+  moe::FfnArgs a{};
+  a.x_perm = x_perm;
+  a.kept = kept;
+  a.offsets = offsets;
+  a.W1 = W1;
+  a.b1 = b1;
+  a.W2 = W2;
+  a.b2 = b2;
+  a.H = at<void>(ws, L.H);
+  a.y_perm = y_perm;
+  a.E = D.E;
+  a.d = D.d;
+  a.d_ffn = D.dff;
+  a.R = D.R;
+  a.C = static_cast<int>(D.C < D.T ? D.C : D.T);
+  a.bf16 = D.bf16 ? 1 : 0;
+  MOE_HIP(moe::launch_expert_ffn(a, reinterpret_cast<hipStream_t>(stream), nullptr), "expert_ffn");
+  return MOE_OK;
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t* dest, const float* topk_w,
+                       const int32_t* counts, const float* prob_colsum, void* y, float* f, float* P, float* L,
+                       void* ws, size_t ws_bytes, moe_stream_t stream) {
+  Derived D;
+  Layout Lw;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(need(y_perm, 16, "y_perm"));
+  MOE_CHECK(need(dest, 4, "dest"));
+  MOE_CHECK(need(topk_w, 4, "topk_w"));
+  MOE_CHECK(need(y, 16, "y"));
+  const bool stats = f != nullptr || P != nullptr || L != nullptr;
+  if (stats) {
+    MOE_CHECK(need(f, 4, "f"));
+    MOE_CHECK(need(P, 4, "P"));
+    MOE_CHECK(need(L, 4, "L"));
+    MOE_CHECK(need(counts, 4, "counts"));
+    MOE_CHECK(need(prob_colsum, 4, "prob_colsum"));
+  }
+  MOE_CHECK(need_ws(D, ws, ws_bytes, &Lw));
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  MOE_HIP(moe::launch_combine(y_perm, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
+  if (stats) MOE_HIP(moe::launch_stats(counts, prob_colsum, D.E, D.k, D.T, f, P, L, st), "stats");
+  return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, const float* bg, const void* W1,
+                       const void* b1, const void* W2, const void* b2, void* y, float* f, float* P, float* L,
+                       int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  Derived D;
+  Layout Lw;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(need(x, 16, "x"));
+  MOE_CHECK(need(Wg, 16, "Wg"));
+  MOE_CHECK(need(bg, 4, "bg", true));
+  MOE_CHECK(need(W1, 16, "W1"));
+  MOE_CHECK(need(b1, D.esize, "b1", true));
+  MOE_CHECK(need(W2, 16, "W2"));
+  MOE_CHECK(need(b2, D.esize, "b2", true));
+  MOE_CHECK(need(y, 16, "y"));
+  MOE_CHECK(need(f, 4, "f"));
+  MOE_CHECK(need(P, 4, "P"));
+  MOE_CHECK(need(L, 4, "L"));
+  MOE_CHECK(need(counts, 4, "counts"));
+  MOE_CHECK(need(kept, 4, "kept"));
+  moe_forward_aux none{};
+  const moe_forward_aux& ax = aux != nullptr ? *aux : none;
+  MOE_CHECK(need(ax.logits, 4, "aux.logits", true));
+  MOE_CHECK(need(ax.scores, 4, "aux.scores", true));
+  MOE_CHECK(need(ax.topk_idx, 4, "aux.topk_idx", true));
+  MOE_CHECK(need(ax.topk_w, 4, "aux.topk_w", true));
+  MOE_CHECK(need(ax.offsets, 4, "aux.offsets", true));
+  MOE_CHECK(need(ax.dest, 4, "aux.dest", true));
+  MOE_CHECK(need(ax.perm, 4, "aux.perm", true));
+  MOE_CHECK(need(ax.prob_colsum, 4, "aux.prob_colsum", true));
+  if (ax.stage_events != nullptr)
+    for (int i = 0; i <= MOE_FORWARD_STAGES; ++i)
+      if (ax.stage_events[i] == nullptr) return fail(MOE_EINVAL, "aux.stage_events has a NULL event");
+  MOE_CHECK(need_ws(D, ws, ws_bytes, &Lw));
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(ax.stage_events);
+  float* logits = ax.logits ? ax.logits : at<float>(ws, Lw.logits);
+  const bool has_scores = D.gumbel != 0 || D.tau != 1.0f;
+  float* scores = ax.scores ? ax.scores : (has_scores ? at<float>(ws, Lw.scores) : nullptr);
+  int32_t* idx = ax.topk_idx ? ax.topk_idx : at<int32_t>(ws, Lw.idx);
+  float* w = ax.topk_w ? ax.topk_w : at<float>(ws, Lw.w);
+  int32_t* offsets = ax.offsets ? ax.offsets : at<int32_t>(ws, Lw.offsets);
+  int32_t* dest = ax.dest ? ax.dest : at<int32_t>(ws, Lw.dest);
+  int32_t* perm = ax.perm ? ax.perm : at<int32_t>(ws, Lw.perm);
+  float* colsum = ax.prob_colsum ? ax.prob_colsum : at<float>(ws, Lw.colsum);
+  float* probsum = at<float>(ws, Lw.probsum);
+  int32_t* hist = at<int32_t>(ws, Lw.hist);
+  int32_t* blockbase = at<int32_t>(ws, Lw.blockbase);
+  void* x_perm = at<void>(ws, Lw.x_perm);
+  float* y_perm = at<float>(ws, Lw.y_perm);
+  const int C = static_cast<int>(D.C < D.T ? D.C : D.T);
+
+  if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
+  // 1-2. router: logits, scores, softmax, top-k, weights, block partials
+  const moe::RouterArgs ra = router_args(D, x, Wg, bg, logits, scores, idx, w, probsum, hist);
+  MOE_HIP(moe::launch_router(ra, st), "router");
+  if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
+  // 3a. counts, capacity, offsets, block bases; f, P, L
+  moe::ScanArgs s{};
+  s.hist = hist;
+  s.nb = D.nb;
+  s.E = D.E;
+  s.k = D.k;
+  s.T = D.T;
+  s.C = C;
+  s.counts = counts;
+  s.kept = kept;
+  s.offsets = offsets;
+  s.blockbase = blockbase;
+  s.probsum_part = probsum;
+  s.colsum = colsum;
+  s.f = f;
+  s.P = P;
+  s.L = L;
+  MOE_HIP(moe::launch_scan(s, st), "scan");
+  if (ev) MOE_HIP(hipEventRecord(ev[2], st), "event");
+  // 3b. stable permutation with the drop mask, then the row gather
+  MOE_HIP(moe::launch_permute(idx, blockbase, offsets, D.T, D.E, D.k, C, dest, perm, st), "permute");
+  MOE_HIP(moe::launch_gather(x, perm, kept, offsets, D.E, D.R, static_cast<int>(D.d * D.esize), x_perm, st),
+          "gather");
+  if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
+  // 4. experts
+  moe::FfnArgs fa{};
+  fa.x_perm = x_perm;
+  fa.kept = kept;
+  fa.offsets = offsets;
+  fa.W1 = W1;
+  fa.b1 = b1;
+  fa.W2 = W2;
+  fa.b2 = b2;
+  fa.H = at<void>(ws, Lw.H);
+  fa.y_perm = y_perm;
+  fa.E = D.E;
+  fa.d = D.d;
+  fa.d_ffn = D.dff;
+  fa.R = D.R;
+  fa.C = C;
+  fa.bf16 = D.bf16 ? 1 : 0;
+  MOE_HIP(moe::launch_expert_ffn(fa, st, ev ? ev[4] : nullptr), "expert_ffn");
+  if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
+  // 5. combine
+  MOE_HIP(moe::launch_combine(y_perm, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
+  if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");
+  return MOE_OK;
+}
+
+const char* moe_status_str(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: configuration not supported";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP runtime error";
+  }
+  return "unknown moe_status";
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Device-side helpers shared by the MoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kBlockTokens = 64;   // tokens per routing block (one wave, one histogram row)
+constexpr int kMaxE = 64;
+constexpr int kMaxK = 8;
+
+__device__ __forceinline__ float bf16_to_f32(u16 b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even (NaN stays a quiet NaN).
+__device__ __forceinline__ u16 f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<u16>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<u16>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): word 0 of the block for counter
+// (c0, c1, 0, 0) and key (k0, k1).
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+  uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t hi0 = __umulhi(0xD2511F53u, x0), lo0 = 0xD2511F53u * x0;
+    const uint32_t hi1 = __umulhi(0xCD9E8D57u, x2), lo1 = 0xCD9E8D57u * x2;
+    const uint32_t n0 = hi1 ^ x1 ^ k0;
+    const uint32_t n2 = hi0 ^ x3 ^ k1;
+    x0 = n0;
+    x1 = lo1;
+    x2 = n2;
+    x3 = lo0;
+  }
+  return x0;
+}
+
+// Gumbel(0,1) noise for (token t, expert e): u = (w0 + 1/2) 2^-32 in float64, strictly inside
+// (0,1); g = -log(-log u) in float64, rounded once to float32.
+__device__ __forceinline__ float gumbel_noise(uint32_t t, uint32_t e, uint32_t k0, uint32_t k1) {
+  const uint32_t w0 = philox_word0(t, e, k0, k1);
+  const double u = (static_cast<double>(w0) + 0.5) * 0x1p-32;
+  return static_cast<float>(-log(-log(u)));
+}
+
+__device__ __forceinline__ float gelu_erf(float v) {
+  return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace moe

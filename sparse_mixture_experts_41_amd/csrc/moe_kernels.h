@@ -1,0 +1,79 @@
+// Host-side launchers of the MoE kernels. Internal to the library; the public ABI is moe.h.
+// Each launcher enqueues on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  const void* x;          // [T,d] dtype
+  const void* Wg;         // [E,d] dtype
+  const float* bg;        // [E] or null
+  int T, d, E, k;
+  int bf16;               // 1 = bfloat16 storage, 0 = float32
+  float tau;
+  int gumbel;
+  uint32_t key0, key1;
+  float* logits;          // [T,E]
+  float* scores;          // [T,E] or null
+  int32_t* idx;           // [T,k]
+  float* w;               // [T,k]
+  float* probsum_part;    // [nb,E], nb = ceil(T/64)
+  int32_t* hist;          // [nb,E]
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+
+// Per-block expert histogram of top-k indices ([nb,E], 64 tokens per block).
+hipError_t launch_histogram(const int32_t* idx, int T, int E, int k, int32_t* hist, hipStream_t stream);
+
+// Fixed-order column sums of per-block partials [nb,E] -> [E].
+hipError_t launch_colsum(const float* part, int nb, int E, float* out, hipStream_t stream);
+
+struct ScanArgs {
+  const int32_t* hist;    // [nb,E]
+  int nb, E, k, T;
+  int C;
+  int32_t* counts;        // [E]
+  int32_t* kept;          // [E]
+  int32_t* offsets;       // [E]
+  int32_t* blockbase;     // [nb,E]
+  // optional statistics (all null or all set)
+  const float* probsum_part;  // [nb,E]
+  float* colsum;          // [E]
+  float* f;               // [E]
+  float* P;               // [E]
+  float* L;               // [1]
+};
+hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+
+hipError_t launch_permute(const int32_t* idx, const int32_t* blockbase, const int32_t* offsets,
+                          int T, int E, int k, int C, int32_t* dest, int32_t* perm, hipStream_t stream);
+
+hipError_t launch_gather(const void* x, const int32_t* perm, const int32_t* kept, const int32_t* offsets,
+                         int E, int R, int row_bytes, void* x_perm, hipStream_t stream);
+
+struct FfnArgs {
+  const void* x_perm;     // [R,d]
+  const int32_t* kept;    // [E]
+  const int32_t* offsets; // [E]
+  const void* W1;         // [E,d_ffn,d]
+  const void* b1;         // [E,d_ffn] or null
+  const void* W2;         // [E,d,d_ffn]
+  const void* b2;         // [E,d] or null
+  void* H;                // [R,d_ffn]
+  float* y_perm;          // [R,d]
+  int E, d, d_ffn, R, C;
+  int bf16;
+};
+// GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid);
+
+hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w, int T, int d, int k, int R,
+                          int bf16, void* y, hipStream_t stream);
+
+hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,
+                        float* L, hipStream_t stream);
+
+}  // namespace moe

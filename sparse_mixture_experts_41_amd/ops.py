@@ -1,0 +1,257 @@
+"""Torch-facing binding of the MoE C ABI: argument marshalling only.
+
+torch supplies device memory and the current HIP stream; every step of the layer runs in the
+library's HIP kernels. Each function mirrors one entry point of include/moe.h and allocates
+its outputs (and, unless one is passed, a workspace) with torch on the inputs' device.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MOE_FORWARD_STAGES, STAGE_NAMES, MoeConfig, MoeForwardAux, make_config
+
+__all__ = ["make_config", "capacity", "workspace_size", "workspace", "route", "dispatch", "expert_ffn", "combine",
+           "forward", "ForwardPlan", "StageEvents", "STAGE_NAMES", "MoeConfig"]
+
+
+def _storage_dtype(cfg: MoeConfig) -> torch.dtype:
+    return torch.bfloat16 if cfg.dtype == _lib.MOE_BF16 else torch.float32
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("MoE tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("MoE tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _expect(t: torch.Tensor | None, name: str, shape, dtype, optional=False) -> None:
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def capacity(cfg: MoeConfig) -> int:
+    c = _lib.load().moe_capacity(ctypes.byref(cfg))
+    if c < 0:
+        _lib.check(_lib.load().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(ctypes.c_size_t())))
+    return int(c)
+
+
+def workspace_size(cfg: MoeConfig) -> int:
+    n = ctypes.c_size_t()
+    _lib.check(_lib.load().moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace(cfg: MoeConfig, device) -> torch.Tensor:
+    return torch.empty(workspace_size(cfg), dtype=torch.uint8, device=device)
+
+
+def rows_max(cfg: MoeConfig) -> int:
+    """Rows of the expert-sorted buffers: min(k*T, E*C)."""
+    C = min(capacity(cfg), cfg.T)
+    return min(cfg.k * cfg.T, cfg.E * C)
+
+
+def route(cfg: MoeConfig, x, Wg, bg=None, ws=None, want_scores=True) -> dict:
+    sd = _storage_dtype(cfg)
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    _expect(x, "x", (T, d), sd)
+    _expect(Wg, "Wg", (E, d), sd)
+    _expect(bg, "bg", (E,), torch.float32, optional=True)
+    dev = x.device
+    ws = workspace(cfg, dev) if ws is None else ws
+    out = {
+        "logits": torch.empty((T, E), dtype=torch.float32, device=dev),
+        "scores": torch.empty((T, E), dtype=torch.float32, device=dev) if want_scores else None,
+        "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "prob_colsum": torch.empty((E,), dtype=torch.float32, device=dev),
+    }
+    _lib.check(_lib.load().moe_route(
+        ctypes.byref(cfg), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(out["logits"]), _ptr(out["scores"]),
+        _ptr(out["topk_idx"]), _ptr(out["topk_w"]), _ptr(out["prob_colsum"]), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def dispatch(cfg: MoeConfig, topk_idx, x, ws=None) -> dict:
+    sd = _storage_dtype(cfg)
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    _expect(topk_idx, "topk_idx", (T, k), torch.int32)
+    _expect(x, "x", (T, d), sd)
+    dev = x.device
+    ws = workspace(cfg, dev) if ws is None else ws
+    R = rows_max(cfg)
+    out = {
+        "counts": torch.empty((E,), dtype=torch.int32, device=dev),
+        "kept": torch.empty((E,), dtype=torch.int32, device=dev),
+        "offsets": torch.empty((E,), dtype=torch.int32, device=dev),
+        "dest": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "perm": torch.full((R,), -1, dtype=torch.int32, device=dev),
+        "x_perm": torch.zeros((R, d), dtype=sd, device=dev),
+    }
+    _lib.check(_lib.load().moe_dispatch(
+        ctypes.byref(cfg), _ptr(topk_idx), _ptr(x), _ptr(out["counts"]), _ptr(out["kept"]), _ptr(out["offsets"]),
+        _ptr(out["dest"]), _ptr(out["perm"]), _ptr(out["x_perm"]), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def expert_ffn(cfg: MoeConfig, x_perm, kept, offsets, W1, b1, W2, b2, ws=None) -> torch.Tensor:
+    sd = _storage_dtype(cfg)
+    E, d, dff = cfg.E, cfg.d, cfg.d_ffn
+    R = rows_max(cfg)
+    _expect(x_perm, "x_perm", (R, d), sd)
+    _expect(kept, "kept", (E,), torch.int32)
+    _expect(offsets, "offsets", (E,), torch.int32)
+    _expect(W1, "W1", (E, dff, d), sd)
+    _expect(b1, "b1", (E, dff), sd, optional=True)
+    _expect(W2, "W2", (E, d, dff), sd)
+    _expect(b2, "b2", (E, d), sd, optional=True)
+    dev = x_perm.device
+    ws = workspace(cfg, dev) if ws is None else ws
+    y_perm = torch.zeros((R, d), dtype=torch.float32, device=dev)
+    _lib.check(_lib.load().moe_expert_ffn(
+        ctypes.byref(cfg), _ptr(x_perm), _ptr(kept), _ptr(offsets), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+        _ptr(y_perm), _ptr(ws), ws.numel(), _stream()))
+    return y_perm
+
+
+def combine(cfg: MoeConfig, y_perm, dest, topk_w, counts=None, prob_colsum=None, ws=None) -> dict:
+    sd = _storage_dtype(cfg)
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    _expect(y_perm, "y_perm", (rows_max(cfg), d), torch.float32)
+    _expect(dest, "dest", (T, k), torch.int32)
+    _expect(topk_w, "topk_w", (T, k), torch.float32)
+    stats = counts is not None
+    dev = y_perm.device
+    ws = workspace(cfg, dev) if ws is None else ws
+    out = {"y": torch.empty((T, d), dtype=sd, device=dev)}
+    if stats:
+        _expect(counts, "counts", (E,), torch.int32)
+        _expect(prob_colsum, "prob_colsum", (E,), torch.float32)
+        out.update(f=torch.empty((E,), dtype=torch.float32, device=dev),
+                   P=torch.empty((E,), dtype=torch.float32, device=dev),
+                   L=torch.empty((1,), dtype=torch.float32, device=dev))
+    _lib.check(_lib.load().moe_combine(
+        ctypes.byref(cfg), _ptr(y_perm), _ptr(dest), _ptr(topk_w), _ptr(counts), _ptr(prob_colsum), _ptr(out["y"]),
+        _ptr(out.get("f")), _ptr(out.get("P")), _ptr(out.get("L")), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+class StageEvents:
+    """MOE_FORWARD_STAGES + 1 HIP events for moe_forward's per-stage timing."""
+
+    def __init__(self):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.array = (ctypes.c_void_p * (MOE_FORWARD_STAGES + 1))()
+        for i in range(MOE_FORWARD_STAGES + 1):
+            ev = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.array[i] = ev
+        self.totals = [0.0] * MOE_FORWARD_STAGES
+        self.samples = 0
+
+    def accumulate(self) -> list[float]:
+        """Per-stage milliseconds of the last recorded forward (synchronises on the last event)."""
+        if self._hip.hipEventSynchronize(self.array[MOE_FORWARD_STAGES]) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = []
+        for i in range(MOE_FORWARD_STAGES):
+            t = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(t), self.array[i], self.array[i + 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            ms.append(t.value)
+            self.totals[i] += t.value
+        self.samples += 1
+        return ms
+
+    def mean_ms(self) -> dict:
+        n = max(1, self.samples)
+        return {name: self.totals[i] / n for i, name in enumerate(STAGE_NAMES)}
+
+    def close(self):
+        for i in range(MOE_FORWARD_STAGES + 1):
+            if self.array[i]:
+                self._hip.hipEventDestroy(self.array[i])
+                self.array[i] = None
+
+
+class ForwardPlan:
+    """Preallocated outputs and workspace for repeated moe_forward calls on fixed tensors."""
+
+    def __init__(self, cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True):
+        sd = _storage_dtype(cfg)
+        T, d, E, k, dff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ffn
+        _expect(x, "x", (T, d), sd)
+        _expect(Wg, "Wg", (E, d), sd)
+        _expect(bg, "bg", (E,), torch.float32, optional=True)
+        _expect(W1, "W1", (E, dff, d), sd)
+        _expect(b1, "b1", (E, dff), sd, optional=True)
+        _expect(W2, "W2", (E, d, dff), sd)
+        _expect(b2, "b2", (E, d), sd, optional=True)
+        dev = x.device
+        self.cfg = cfg
+        self.inputs = (x, Wg, bg, W1, b1, W2, b2)
+        self.ws = workspace(cfg, dev)
+        f32, i32 = torch.float32, torch.int32
+        self.out = {
+            "y": torch.empty((T, d), dtype=sd, device=dev),
+            "f": torch.empty((E,), dtype=f32, device=dev),
+            "P": torch.empty((E,), dtype=f32, device=dev),
+            "L": torch.empty((1,), dtype=f32, device=dev),
+            "counts": torch.empty((E,), dtype=i32, device=dev),
+            "kept": torch.empty((E,), dtype=i32, device=dev),
+        }
+        self.aux = MoeForwardAux()
+        if keep_routing:
+            R = rows_max(cfg)
+            self.out.update(
+                logits=torch.empty((T, E), dtype=f32, device=dev),
+                scores=torch.empty((T, E), dtype=f32, device=dev),
+                topk_idx=torch.empty((T, k), dtype=i32, device=dev),
+                topk_w=torch.empty((T, k), dtype=f32, device=dev),
+                offsets=torch.empty((E,), dtype=i32, device=dev),
+                dest=torch.empty((T, k), dtype=i32, device=dev),
+                perm=torch.full((R,), -1, dtype=i32, device=dev),
+                prob_colsum=torch.empty((E,), dtype=f32, device=dev),
+            )
+            for name in ("logits", "scores", "topk_idx", "topk_w", "offsets", "dest", "perm", "prob_colsum"):
+                setattr(self.aux, name, self.out[name].data_ptr())
+        self._args = None
+
+    def run(self, events: StageEvents | None = None, stream=None) -> dict:
+        self.aux.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value if events is not None else None
+        x, Wg, bg, W1, b1, W2, b2 = self.inputs
+        o = self.out
+        _lib.check(_lib.load().moe_forward(
+            ctypes.byref(self.cfg), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+            _ptr(o["y"]), _ptr(o["f"]), _ptr(o["P"]), _ptr(o["L"]), _ptr(o["counts"]), _ptr(o["kept"]),
+            ctypes.byref(self.aux), _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        return o
+
+
+def forward(cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True) -> dict:
+    """The whole layer (moe_forward); returns y, f, P, L, counts, kept (+ routing arrays)."""
+    return ForwardPlan(cfg, x, Wg, bg, W1, b1, W2, b2, keep_routing=keep_routing).run()
