@@ -14,6 +14,8 @@
 //   grouped_gemv_bf16: at most 16 rows per expert (decode-sized batches): no LDS, the weight
 //                      rows stream from HBM straight into v_mfma_f32_16x16x32_bf16 operands.
 //   grouped_gemm_f32:  float32 storage, plain FMA (small sizes only).
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -30,6 +32,8 @@ struct GemmArgs {
   const int32_t* offsets; // [E]
   int E, N, K;
   int R, C;               // rows of A/out and the capacity: segments outside them are skipped
+  int splits;             // K is split into this many equal parts (1 or 2)
+  void* out2;             // [R,N] float partial sums of the second K part (splits == 2)
 };
 
 enum { kEpiGelu = 0, kEpiLinear = 1 };
@@ -63,112 +67,241 @@ __device__ __forceinline__ float load_bias(const void* bias, size_t i, bool bf16
   return bf16 ? bf16_to_f32(static_cast<const u16*>(bias)[i]) : static_cast<const float*>(bias)[i];
 }
 
-// ---------------------------------------------------------------------------------------
-// bf16 grouped GEMM: 128x128 tile, K step 64, 4 waves in a 2x2 grid of 64x64 wave tiles,
-// each wave 2x2 MFMA 32x32x16 tiles. LDS rows padded by 16 bytes against bank conflicts;
-// the next K step's global loads are in flight while the current one is multiplied.
-constexpr int GBM = 128, GBN = 128, GBK = 64, GLDK = GBK + 8;
+// Number of (expert, row tile, column tile) tiles.
+__device__ __forceinline__ int count_tiles(const GemmArgs& g, int BM, int tiles_n) {
+  int n = 0;
+  for (int e = 0; e < g.E; ++e) n += (segment_rows(g, e) + BM - 1) / BM * tiles_n;
+  return n;
+}
 
-template <int EPI>
+// The hardware hands workgroup b to XCD (b mod 8). Workgroups are renumbered so that each XCD
+// takes bundles of kBundle consecutive tiles (tiles that share an expert's operand panels, so
+// they meet in that XCD's L2), and bundles go round-robin over the 8 XCDs (so experts of very
+// different sizes still spread evenly over the chip). Covers [0, 8*kBundle*ceil(n/(8*kBundle))).
+constexpr int kBundle = 8;
+__device__ __forceinline__ int xcd_tile_id(int bid) {
+  const int x = bid & 7, j = bid >> 3;
+  return ((j / kBundle) * 8 + x) * kBundle + j % kBundle;
+}
+
+int round_grid(int n) {
+  const int g = 8 * kBundle;
+  return (n + g - 1) / g * g;
+}
+
+// s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte global -> LDS load per lane (global_load_lds_dwordx4): lane i writes bytes
+// [16 i, 16 i + 16) of the wave's 1 KB block at `lds` (which must be the same for every lane).
+__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------
+// bf16 grouped GEMM C[r, n] = sum_k A[r, k] B_e[n, k] over each expert's row segment.
+// 256 x 256 workgroup tile, 4 waves in a 2x2 grid of 128 x 128 wave tiles, each a 4x4 grid of
+// v_mfma_f32_32x32x16_bf16 tiles (256 accumulators per lane). Operand tiles go from global
+// memory straight into LDS (global_load_lds_dwordx4: 64 lanes fill one contiguous 1 KB block)
+// through a ring of NS K-steps of BK; the 16-byte chunks of each row are XOR-swizzled so that
+// the 16-byte fragment reads of any 16 consecutive rows hit all 64 banks once.
+// The workgroup barrier sits before the last MFMA substep of each K step: after it, step s+1
+// is complete in LDS (its first fragments are read during step s's last MFMAs) and the buffer
+// of step s-1 is free for step s+NS-1, so NS-3 steps of loads stay in flight while waiting.
+// Loads past the last K step re-read the last step into buffers nobody reads again, which keeps
+// the number of loads in flight the same in every iteration.
+// Rows past the segment (or past N) are loaded from the last valid row: they only feed output
+// rows (columns) that are never stored.
+template <int EPI, int BK, int NS>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) u16 As[GBM * GLDK];
-  __shared__ __attribute__((aligned(16))) u16 Bs[GBN * GLDK];
-  const int tiles_n = (g.N + GBN - 1) / GBN;
+  constexpr int BM = 256, BN = 256;
+  constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
+  constexpr int RPI = 64 / CPR;              // tile rows per 1 KB wave load
+  constexpr int RPS = 256 / (BK * 2);        // tile rows per 256-byte bank sweep
+  constexpr int ROWB = BK * 2;               // bytes per tile row
+  constexpr int TILE = BM * ROWB;            // bytes of the A (or B) tile of one K step
+  constexpr int STAGE = 2 * TILE;
+  constexpr int LOADS = BM / RPI / 4;        // 1 KB loads per wave per operand per K step
+  constexpr int PER_STAGE = 2 * LOADS;       // vm operations per thread per K step
+  constexpr int KK = BK / 16;                // MFMA K substeps per K step
+  static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS ring");
+  static_assert(KK % 2 == 0, "fragment double buffer parity");
+  static_assert(LOADS * 2 <= 8, "one load per interleave slot");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
+
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const int n_tiles = count_tiles(g, BM, tiles_n);
+  const int n_units = n_tiles * g.splits;
+  const int unit = xcd_tile_id(blockIdx.x);
+  if (unit >= n_units) return;
+  const int kpart = unit / n_tiles;
   int e, mt, nt;
-  if (!decode_tile(blockIdx.x, g, GBM, tiles_n, e, mt, nt)) return;
+  decode_tile(unit - kpart * n_tiles, g, BM, tiles_n, e, mt, nt);
   const int m_e = segment_rows(g, e);
   const int row0 = g.offsets[e];
-  const int m0 = mt * GBM, n0 = nt * GBN;
+  const int m0 = mt * BM, n0 = nt * BN;
   const int N = g.N, K = g.K;
-  const u16* __restrict__ A = static_cast<const u16*>(g.A);
-  const u16* __restrict__ B = static_cast<const u16*>(g.B) + static_cast<size_t>(e) * N * K;
-  const int tid = threadIdx.x;
+  const int nk = K / BK / g.splits;          // K steps of this part
+  const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + static_cast<size_t>(row0 + m0) * K) +
+                   static_cast<size_t>(kpart) * nk * ROWB;
+  const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
+                                                 (static_cast<size_t>(e) * N + n0) * K) +
+                   static_cast<size_t>(kpart) * nk * ROWB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  // global -> register staging: 4 x 16 B of A and of B per thread per K step
-  const u16* ap[4];
-  const u16* bp[4];
-  bool av_ok[4], bv_ok[4];
-  int soff[4];
+  // direct loads: wave w fills 1 KB blocks w, w+4, ... of each operand tile
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  uint32_t aoff[LOADS], boff[LOADS];
+  const int a_last = m_e - 1 - m0, b_last = N - 1 - n0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c >> 3, kc = (c & 7) * 8;
-    av_ok[i] = (m0 + r) < m_e;
-    bv_ok[i] = (n0 + r) < N;
-    ap[i] = A + static_cast<size_t>(row0 + (av_ok[i] ? m0 + r : 0)) * K + kc;
-    bp[i] = B + static_cast<size_t>(bv_ok[i] ? n0 + r : 0) * K + kc;
-    soff[i] = r * GLDK + kc;
+  for (int i = 0; i < LOADS; ++i) {
+    const int r = (wave + 4 * i) * RPI + lrow;
+    const int c = lslot ^ ((r / RPS) % CPR);
+    aoff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < a_last ? r : a_last) * K + c * 8) * 2);
+    boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * K + c * 8) * 2);
   }
-  u32x4 ra[4], rb[4];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  auto issue = [&](int st) {   // loads of K step min(st, nk-1) into buffer st % NS
+    char* dst = smem + (st % NS) * STAGE + wave * 1024;
+    const uint32_t kb = static_cast<uint32_t>(st < nk ? st : nk - 1) * ROWB;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = av_ok[i] ? *reinterpret_cast<const u32x4*>(ap[i]) : zero;
-    rb[i] = bv_ok[i] ? *reinterpret_cast<const u32x4*>(bp[i]) : zero;
-  }
+    for (int i = 0; i < LOADS; ++i) load_lds16(Ab + aoff[i] + kb, dst + i * 4096);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) load_lds16(Bb + boff[i] + kb, dst + TILE + i * 4096);
+  };
 
-  const int wave = tid >> 6, lane = tid & 63;
+  // fragment addressing: lane reads row (wave-tile row + l32), logical chunk 2 kk + hi
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, lk = 8 * (lane >> 5);
-  floatx16 acc[2][2];
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int swz = (l32 / RPS) % CPR;
+  int slot[KK];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int kk = 0; kk < KK; ++kk) slot[kk] = ((2 * kk + hi) ^ swz) * 16;
+  const int a_frag = (wm * 128 + l32) * ROWB;
+  const int b_frag = TILE + (wn * 128 + l32) * ROWB;
+  floatx16 acc[4][4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = floatx16{};
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  for (int k0 = 0; k0 < K; k0 += GBK) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(As + soff[i]) = ra[i];
-      *reinterpret_cast<u32x4*>(Bs + soff[i]) = rb[i];
-    }
-    __syncthreads();
-    if (k0 + GBK < K) {
+  // The wave multiplies only the 32-row blocks of its 128 rows that hold segment rows (2 or 4
+  // of them; rows past the segment are never stored). Every wave still issues its share of
+  // the loads and takes every barrier.
+  auto mainloop = [&](auto ni_const) {
+    constexpr int NI = decltype(ni_const)::value;
+    bf16x8 fa[2][4], fb[2][4];
+    auto read_frags = [&](int st, int kk, int f) {
+      const char* buf = smem + (st % NS) * STAGE;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ra[i] = av_ok[i] ? *reinterpret_cast<const u32x4*>(ap[i] + k0 + GBK) : zero;
-        rb[i] = bv_ok[i] ? *reinterpret_cast<const u32x4*>(bp[i] + k0 + GBK) : zero;
+        if (i < NI) fa[f][i] = *reinterpret_cast<const bf16x8*>(buf + a_frag + i * 32 * ROWB + slot[kk]);
+        if (NI > 0) fb[f][i] = *reinterpret_cast<const bf16x8*>(buf + b_frag + i * 32 * ROWB + slot[kk]);
       }
-    }
+    };
+    auto mfmas = [&](int f) {
 #pragma unroll
-    for (int kk = 0; kk < GBK / 16; ++kk) {
-      bf16x8 a[2], b[2];
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(As + (wm * 64 + i * 32 + l32) * GLDK + kk * 16 + lk);
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+    };
+    // per substep: one fragment read (and, after the barrier, one operand load) after each
+    // of the first MFMAs, then the remaining MFMAs
+    auto schedule = [&](bool with_loads) {
+      constexpr int NR = NI + (NI > 0 ? 4 : 0);     // fragment reads per substep
+      constexpr int NM = NI * 4;                     // MFMAs per substep
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8*>(Bs + (wn * 64 + j * 32 + l32) * GLDK + kk * 16 + lk);
+      for (int q = 0; q < 8; ++q) {
+        if (q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      if (NM > 8) __builtin_amdgcn_sched_group_barrier(0x008, NM - 8, 0);
+    };
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+    for (int st = 0; st < NS - 1; ++st) issue(st);
+    wait_vmcnt<(NS - 2) * PER_STAGE>();
     __syncthreads();
-  }
+    read_frags(0, 0, 0);
+    for (int s = 0; s < nk; ++s) {
+#pragma unroll
+      for (int kk = 0; kk + 1 < KK; ++kk) {
+        read_frags(s, kk + 1, (kk + 1) & 1);
+        mfmas(kk & 1);
+      }
+      schedule(false);
+      wait_vmcnt<(NS - 3) * PER_STAGE>();   // this thread's loads of step s+1 have landed
+      __syncthreads();                      // everyone's have; step s-1's buffer is free
+      issue(s + NS - 1);
+      read_frags(s + 1, 0, 0);              // past the last step this reads unused data
+      mfmas((KK - 1) & 1);
+      schedule(true);
+    }
+  };
+  const int valid = m_e - m0 - wm * 128;     // segment rows in this wave's 128 rows
+  if (valid > 64)
+    mainloop(std::integral_constant<int, 4>{});
+  else if (valid > 0)
+    mainloop(std::integral_constant<int, 2>{});
+  else
+    mainloop(std::integral_constant<int, 0>{});
+  wait_vmcnt<0>();     // the trailing re-loads must land before LDS is reused
+  __syncthreads();   // LDS is reused below
 
-  // C layout of the 32x32 tile: lane holds column (lane & 31), rows 8*(v/4) + 4*(lane/32) + v%4.
+  // Epilogue through LDS, one 32-row block of the wave tile at a time: the 32x128 float block
+  // goes to this wave's LDS region, then every lane turns 8 consecutive values of a row into
+  // one 16-byte bf16 store (GeLU) or two 16-byte float stores.
+  constexpr int LDE = 128 + 4;
+  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * LDE;
+  const int cg = lane & 15;                  // this lane's column group (8 columns)
+  const int ccol = n0 + wn * 128 + cg * 8;
+  float bias[8];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = n0 + wn * 64 + j * 32 + l32;
-    if (c >= N) continue;
-    const float bias = load_bias(g.bias, static_cast<size_t>(e) * N + c, true);
+  for (int q = 0; q < 8; ++q)
+    bias[q] = (kpart == 0 && ccol + q < N) ? load_bias(g.bias, static_cast<size_t>(e) * N + ccol + q, true) : 0.0f;
+  float* fout = static_cast<float*>(kpart == 0 ? g.out : g.out2);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (r < m_e) {
-          const size_t o = static_cast<size_t>(row0 + r) * N + c;
-          const float val = acc[i][j][v] + bias;
-          if (EPI == kEpiGelu)
-            static_cast<u16*>(g.out)[o] = f32_to_bf16(gelu_erf(val));
-          else
-            static_cast<float*>(g.out)[o] = val;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ep[(8 * (v >> 2) + 4 * hi + (v & 3)) * LDE + j * 32 + l32] = acc[i][j][v];
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int rr = it * 4 + (lane >> 4);   // row within the 32-row block
+      const int r = m0 + wm * 128 + i * 32 + rr;
+      const floatx4 v0 = *reinterpret_cast<const floatx4*>(ep + rr * LDE + cg * 8);
+      const floatx4 v1 = *reinterpret_cast<const floatx4*>(ep + rr * LDE + cg * 8 + 4);
+      if (r < m_e && ccol < N) {
+        float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const size_t off = static_cast<size_t>(row0 + r) * N + ccol;
+        if (EPI == kEpiGelu) {
+          u32x4 pk;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            pk[q] = pack_bf16x2(gelu_bf16_path(o[2 * q] + bias[2 * q]), gelu_bf16_path(o[2 * q + 1] + bias[2 * q + 1]));
+          *reinterpret_cast<u32x4*>(static_cast<u16*>(g.out) + off) = pk;
+        } else {
+          floatx4 w0, w1;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            w0[q] = o[q] + bias[q];
+            w1[q] = o[4 + q] + bias[4 + q];
+          }
+          floatx4* dst = reinterpret_cast<floatx4*>(fout + off);
+          dst[0] = w0;
+          dst[1] = w1;
         }
       }
     }
+    __syncthreads();
   }
 }
 
@@ -211,7 +344,7 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
       const size_t o = static_cast<size_t>(row0 + r) * N + n;
       const float val = acc[i] + bias;
       if (EPI == kEpiGelu)
-        static_cast<u16*>(g.out)[o] = f32_to_bf16(gelu_erf(val));
+        static_cast<u16*>(g.out)[o] = f32_to_bf16(gelu_bf16_path(val));
       else
         static_cast<float*>(g.out)[o] = val;
     }
@@ -261,9 +394,15 @@ int tile_grid(int R, int E, int C, int BM, int N, int BN) {
 
 }  // namespace
 
+int ffn_splits(const FfnArgs& a) {
+  if (!a.bf16 || a.C <= 16) return 1;
+  const int tiles2 = tile_grid(a.R, a.E, a.C, 256, a.d, 256);
+  return (tiles2 < 4 * 256 && a.d_ffn % 64 == 0 && a.d_ffn >= 1024) ? 2 : 1;
+}
+
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
-  GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C};
-  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C};
+  GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr};
+  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2};
   hipError_t err;
   if (!a.bf16) {
     const int grid1 = tile_grid(a.R, a.E, a.C, FBM, a.d_ffn, 16);
@@ -281,12 +420,35 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
     hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiLinear>, dim3(a.E * (a.d / 64)), dim3(256), 0, stream, g2);
     return hipGetLastError();
   }
-  const int grid1 = tile_grid(a.R, a.E, a.C, GBM, a.d_ffn, GBN);
-  const int grid2 = tile_grid(a.R, a.E, a.C, GBM, a.d, GBN);
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kEpiGelu>, dim3(grid1), dim3(256), 0, stream, g1);
+  const int grid1 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d_ffn, 256));
+  const int grid2 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d, 256) * g2.splits);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiGelu, 32, 4>), dim3(grid1), dim3(256), 0, stream, g1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<kEpiLinear>, dim3(grid2), dim3(256), 0, stream, g2);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void add_partials_kernel(float* __restrict__ y, const float* __restrict__ y2,
+                                                           const int32_t* __restrict__ kept,
+                                                           const int32_t* __restrict__ offsets, int E, int R, int d) {
+  const int total = min(offsets[E - 1] + kept[E - 1], R);
+  const long long n4 = static_cast<long long>(total) * d / 4;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
+       i += static_cast<long long>(gridDim.x) * blockDim.x) {
+    floatx4 a = reinterpret_cast<floatx4*>(y)[i];
+    const floatx4 b = reinterpret_cast<const floatx4*>(y2)[i];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = a[q] + b[q];
+    reinterpret_cast<floatx4*>(y)[i] = a;
+  }
+}
+}  // namespace
+
+hipError_t launch_add_partials(float* y_perm, const float* y_perm2, const int32_t* kept, const int32_t* offsets,
+                               int E, int R, int d, hipStream_t stream) {
+  hipLaunchKernelGGL(add_partials_kernel, dim3(4096), dim3(256), 0, stream, y_perm, y_perm2, kept, offsets, E, R, d);
   return hipGetLastError();
 }
 

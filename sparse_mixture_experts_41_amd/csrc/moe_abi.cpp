@@ -32,7 +32,8 @@ struct Derived {
 };
 
 struct Layout {
-  size_t probsum, hist, blockbase, colsum, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm, total;
+  size_t probsum, hist, blockbase, colsum, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm, y_perm2,
+      total;
 };
 
 // C = ceil(c*k*T/E) for the exact value of the double c = m * 2^sh (m a 53-bit integer).
@@ -118,6 +119,7 @@ Layout layout_of(const Derived& D) {
   L.x_perm = take(R * static_cast<size_t>(D.d) * D.esize);
   L.H = take(R * static_cast<size_t>(D.dff) * D.esize);
   L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
+  L.y_perm2 = take(D.bf16 ? R * static_cast<size_t>(D.d) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -293,7 +295,11 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
   a.R = D.R;
   a.C = static_cast<int>(D.C < D.T ? D.C : D.T);
   a.bf16 = D.bf16 ? 1 : 0;
-  MOE_HIP(moe::launch_expert_ffn(a, reinterpret_cast<hipStream_t>(stream), nullptr), "expert_ffn");
+  a.y_perm2 = at<float>(ws, L.y_perm2);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  MOE_HIP(moe::launch_expert_ffn(a, st, nullptr), "expert_ffn");
+  if (moe::ffn_splits(a) == 2)
+    MOE_HIP(moe::launch_add_partials(y_perm, a.y_perm2, kept, offsets, D.E, D.R, D.d, st), "add_partials");
   return MOE_OK;
 }
 
@@ -317,7 +323,7 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   }
   MOE_CHECK(need_ws(D, ws, ws_bytes, &Lw));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  MOE_HIP(moe::launch_combine(y_perm, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
+  MOE_HIP(moe::launch_combine(y_perm, nullptr, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
   if (stats) MOE_HIP(moe::launch_stats(counts, prob_colsum, D.E, D.k, D.T, f, P, L, st), "stats");
   return MOE_OK;
 }
@@ -421,10 +427,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   fa.R = D.R;
   fa.C = C;
   fa.bf16 = D.bf16 ? 1 : 0;
+  fa.y_perm2 = at<float>(ws, Lw.y_perm2);
   MOE_HIP(moe::launch_expert_ffn(fa, st, ev ? ev[4] : nullptr), "expert_ffn");
   if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
-  // 5. combine
-  MOE_HIP(moe::launch_combine(y_perm, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
+  // 5. combine (adding the two K halves of GEMM2 when it was split)
+  const float* y_perm2 = moe::ffn_splits(fa) == 2 ? fa.y_perm2 : nullptr;
+  MOE_HIP(moe::launch_combine(y_perm, y_perm2, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
   if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");
   return MOE_OK;
 }

@@ -64,14 +64,22 @@ struct FfnArgs {
   const void* b2;         // [E,d] or null
   void* H;                // [R,d_ffn]
   float* y_perm;          // [R,d]
+  float* y_perm2;         // [R,d] second K half of GEMM2 when ffn_splits() == 2
   int E, d, d_ffn, R, C;
   int bf16;
 };
+// Number of K parts GEMM2 is split into (1 or 2): 2 when its tiles would fill fewer than four
+// rounds of the 256 CUs. With 2, y_perm + y_perm2 (summed in float32) is the GEMM2 result.
+int ffn_splits(const FfnArgs& a);
 // GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid);
+// y_perm[r] += y_perm2[r] for the sum(kept) valid rows (standalone expert FFN with 2 parts).
+hipError_t launch_add_partials(float* y_perm, const float* y_perm2, const int32_t* kept, const int32_t* offsets,
+                               int E, int R, int d, hipStream_t stream);
 
-hipError_t launch_combine(const float* y_perm, const int32_t* dest, const float* w, int T, int d, int k, int R,
-                          int bf16, void* y, hipStream_t stream);
+// y_perm2 (nullable): second GEMM2 partial, added to y_perm before weighting.
+hipError_t launch_combine(const float* y_perm, const float* y_perm2, const int32_t* dest, const float* w, int T,
+                          int d, int k, int R, int bf16, void* y, hipStream_t stream);
 
 hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,
                         float* L, hipStream_t stream);
