@@ -32,8 +32,8 @@ struct Derived {
 };
 
 struct Layout {
-  size_t probsum, hist, blockbase, colsum, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm, y_perm2,
-      total;
+  size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
+      y_perm2, total;
 };
 
 // C = ceil(c*k*T/E) for the exact value of the double c = m * 2^sh (m a 53-bit integer).
@@ -109,6 +109,7 @@ Layout layout_of(const Derived& D) {
   L.hist = take(nb * E * 4);
   L.blockbase = take(nb * E * 4);
   L.colsum = take(E * 4);
+  L.zpart = take(D.bf16 ? static_cast<size_t>(moe::router_plan(D.T, D.d, D.E).ks) * T * E * 4 : 0);
   L.logits = take(T * E * 4);
   L.scores = take(T * E * 4);
   L.idx = take(T * k * 4);
@@ -222,7 +223,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* Wg, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const moe::RouterArgs a = router_args(D, x, Wg, bg, logits, scores, topk_idx, topk_w, at<float>(ws, L.probsum),
                                         at<int32_t>(ws, L.hist));
-  MOE_HIP(moe::launch_router(a, st), "router");
+  MOE_HIP(moe::launch_router(a, at<float>(ws, L.zpart), st), "router");
   MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.nb, D.E, prob_colsum, st), "colsum");
   return MOE_OK;
 }
@@ -384,7 +385,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
   // 1-2. router: logits, scores, softmax, top-k, weights, block partials
   const moe::RouterArgs ra = router_args(D, x, Wg, bg, logits, scores, idx, w, probsum, hist);
-  MOE_HIP(moe::launch_router(ra, st), "router");
+  MOE_HIP(moe::launch_router(ra, at<float>(ws, Lw.zpart), st), "router");
   if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
   // 3a. counts, capacity, offsets, block bases; f, P, L
   moe::ScanArgs s{};

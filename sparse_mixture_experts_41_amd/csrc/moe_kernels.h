@@ -23,7 +23,13 @@ struct RouterArgs {
   float* probsum_part;    // [nb,E], nb = ceil(T/64)
   int32_t* hist;          // [nb,E]
 };
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+// Logit kernel shape for bf16: tokens per workgroup 16*mt, K split into ks slices.
+struct RouterPlan {
+  int mt = 1, ks = 1;
+};
+RouterPlan router_plan(int T, int d, int E);
+// zpart: float [ks, T, E] workspace of the logit partial sums (unused for float32).
+hipError_t launch_router(const RouterArgs& a, float* zpart, hipStream_t stream);
 
 // Per-block expert histogram of top-k indices ([nb,E], 64 tokens per block).
 hipError_t launch_histogram(const int32_t* idx, int T, int E, int k, int32_t* hist, hipStream_t stream);
