@@ -35,11 +35,39 @@ def _args():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_like")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512,
-                    help="tokens in the batch the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=-1,
+                    help="tokens in the batch the CPU oracle is timed on (-1 = the whole batch, 0 = skip)")
     ap.add_argument("--traffic", default=None,
-                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+                    help="JSON with rocprofv3-measured HBM bytes per launch "
+                         "(default: profiles/traffic_<workload>.json)")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (3 times) and exit: the "
+                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+# Sources whose change invalidates a stored traffic measurement of the expert GEMMs.
+GEMM_SOURCES = ("sparse_mixture_experts_41_amd/csrc/expert_gemm.hip", "sparse_mixture_experts_41_amd/csrc/moe_common.h")
+
+
+def gemm_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(path: str, kernel: str):
+    """Measured HBM bytes per launch of `kernel`, or None if absent or taken on other code."""
+    if not path or not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("gemm_source_sha256") != gemm_source_digest():
+        return None
+    return rec.get("bytes_per_launch", {}).get(kernel)
 
 
 def cpu_baseline(shape, arrays, n_tokens: int) -> dict:
@@ -69,8 +97,9 @@ def cpu_baseline(shape, arrays, n_tokens: int) -> dict:
         blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()]
     assert np.isfinite(out["y"]).all()
     return {"value": n_tokens / (t1 - t0), "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of the {shape.name} input as one batch "
-                      f"(C recomputed for T={n_tokens}), numpy float64, {', '.join(blas)}",
+            "sample": (f"the whole {shape.name} batch ({n_tokens} tokens)" if n_tokens == shape.T else
+                       f"first {n_tokens} tokens of the {shape.name} input as one batch (C recomputed)")
+                      + f", numpy float64, {', '.join(blas)}",
             "seconds": t1 - t0}
 
 
@@ -87,8 +116,18 @@ def main() -> int:
     from sparse_mixture_experts_41_amd import ops
     from workloads import CONFIGS, make_inputs
 
-    shape = CONFIGS[args.workload]
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "copies": 3}), flush=True)
+        return 0
+    shape = CONFIGS[args.workload]
     arrays = make_inputs(shape)
 
     def dev(a):
@@ -127,10 +166,8 @@ def main() -> int:
     g1, g2 = stage["expert_gemm1_gelu"], stage["expert_gemm2"]
     dom_name, dom_ms = ("expert_gemm1_gelu", g1) if g1 >= g2 else ("expert_gemm2", g2)
     achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get(dom_name)
+    traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{shape.name}.json")
+    traffic = stored_traffic(traffic_path, dom_name)
     nb = (T + 63) // 64
     router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + nb * E * 8
     dispatch_bytes = T * k * 4 + T * k * 4 + kept * 4 + 2 * kept * d * sx
@@ -166,8 +203,9 @@ def main() -> int:
         "stage_ms": stage,
         "counts_minmax": [int(counts.min()), int(counts.max())],
     }
-    if args.cpu_sample_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(shape, arrays, min(args.cpu_sample_tokens, T))
+    if args.cpu_sample_tokens != 0:
+        n_cpu = T if args.cpu_sample_tokens < 0 else min(args.cpu_sample_tokens, T)
+        line["cpu_baseline"] = cpu_baseline(shape, arrays, n_cpu)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
