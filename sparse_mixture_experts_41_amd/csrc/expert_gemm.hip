@@ -306,12 +306,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------------------
-// bf16 grouped GEMV-like kernel for experts with at most 16 rows. Workgroup = one expert x 64
-// output columns; wave = 16 columns over the full K. Each lane group (16 lanes) reads 32
-// contiguous bytes of a weight row per K step of 64, so a row is read in 128-byte runs.
+// bf16 grouped GEMV-like kernel for experts with at most 16 rows (decode-sized batches): the
+// weights are streamed from HBM exactly once, straight into v_mfma_f32_16x16x32_bf16 operands.
+// Workgroup = one expert x 128 output columns; each wave owns 2 tiles of 16 columns over the
+// full K. K goes in chunks of 64: lane group g (16 lanes) takes elements [kc + 16 g, kc + 16 g
+// + 16) of its row as two 8-element pieces, and MFMA step i takes piece i of both operands (the
+// k order of A and B agrees); each load instruction then covers 16 rows x 64 bytes. GV_BATCH
+// chunks of loads are issued ahead of their MFMAs. Rows past the expert's segment are read
+// from its last row: they only feed output rows that are never stored.
+constexpr int GV_COLS = 128, GV_BATCH = 4;
+
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
-  const int nblk_n = g.N / 64;
+  const int nblk_n = (g.N + GV_COLS - 1) / GV_COLS;
   const int e = blockIdx.x / nblk_n, nb = blockIdx.x - e * nblk_n;
   const int m_e = segment_rows(g, e);
   if (m_e == 0) return;
@@ -319,34 +326,65 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
   const int N = g.N, K = g.K;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int n = nb * 64 + wave * 16 + r16;
-  const bool arow = r16 < m_e;
-  const u16* __restrict__ ap = static_cast<const u16*>(g.A) + static_cast<size_t>(row0 + (arow ? r16 : 0)) * K + 16 * grp;
-  const u16* __restrict__ bp = static_cast<const u16*>(g.B) + (static_cast<size_t>(e) * N + n) * K + 16 * grp;
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int kc = 0; kc < K; kc += 64) {
-    bf16x8 a0 = bf16x8{}, a1 = bf16x8{};
-    if (arow) {
-      a0 = *reinterpret_cast<const bf16x8*>(ap + kc);
-      a1 = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
-    }
-    const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bp + kc);
-    const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bp + kc + 8);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc, 0, 0, 0);
-  }
-  const float bias = load_bias(g.bias, static_cast<size_t>(e) * N + n, true);
+  const int nbase = nb * GV_COLS + wave * 32;
+  const u16* __restrict__ ap =
+      static_cast<const u16*>(g.A) + static_cast<size_t>(row0 + (r16 < m_e ? r16 : m_e - 1)) * K + 16 * grp;
+  const u16* bp[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * grp + i;
-    if (r < m_e) {
-      const size_t o = static_cast<size_t>(row0 + r) * N + n;
-      const float val = acc[i] + bias;
-      if (EPI == kEpiGelu)
-        static_cast<u16*>(g.out)[o] = f32_to_bf16(gelu_bf16_path(val));
-      else
-        static_cast<float*>(g.out)[o] = val;
+  for (int t = 0; t < 2; ++t) {
+    const int n = min(nbase + t * 16 + r16, N - 1);
+    bp[t] = static_cast<const u16*>(g.B) + (static_cast<size_t>(e) * N + n) * K + 16 * grp;
+  }
+  floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  int kc = 0;
+  for (; kc + GV_BATCH * 64 <= K; kc += GV_BATCH * 64) {
+    bf16x8 a[GV_BATCH][2], b[GV_BATCH][2][2];
+#pragma unroll
+    for (int c = 0; c < GV_BATCH; ++c) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        b[c][t][0] = *reinterpret_cast<const bf16x8*>(bp[t] + kc + c * 64);
+        b[c][t][1] = *reinterpret_cast<const bf16x8*>(bp[t] + kc + c * 64 + 8);
+      }
+      a[c][0] = *reinterpret_cast<const bf16x8*>(ap + kc + c * 64);
+      a[c][1] = *reinterpret_cast<const bf16x8*>(ap + kc + c * 64 + 8);
+    }
+#pragma unroll
+    for (int c = 0; c < GV_BATCH; ++c)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][0], b[c][t][0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][1], b[c][t][1], acc[t], 0, 0, 0);
+      }
+  }
+  for (; kc < K; kc += 64) {
+    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap + kc);
+    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bp[t] + kc);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bp[t] + kc + 8);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
+      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+    }
+  }
+  // C layout of the 16x16 tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = nbase + t * 16 + r16;
+    if (n >= N) continue;
+    const float bias = load_bias(g.bias, static_cast<size_t>(e) * N + n, true);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 4 * grp + i;
+      if (r < m_e) {
+        const size_t o = static_cast<size_t>(row0 + r) * N + n;
+        const float val = acc[t][i] + bias;
+        if (EPI == kEpiGelu)
+          static_cast<u16*>(g.out)[o] = f32_to_bf16(gelu_bf16_path(val));
+        else
+          static_cast<float*>(g.out)[o] = val;
+      }
     }
   }
 }
@@ -414,10 +452,12 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
     return hipGetLastError();
   }
   if (a.C <= 16) {
-    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiGelu>, dim3(a.E * (a.d_ffn / 64)), dim3(256), 0, stream, g1);
+    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiGelu>, dim3(a.E * ((a.d_ffn + GV_COLS - 1) / GV_COLS)), dim3(256),
+                       0, stream, g1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiLinear>, dim3(a.E * (a.d / 64)), dim3(256), 0, stream, g2);
+    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiLinear>, dim3(a.E * ((a.d + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
+                       stream, g2);
     return hipGetLastError();
   }
   const int grid1 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d_ffn, 256));
