@@ -98,17 +98,29 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One 16-byte global -> LDS load per lane (global_load_lds_dwordx4): lane i writes bytes
-// [16 i, 16 i + 16) of the wave's 1 KB block at `lds` (which must be the same for every lane).
-__device__ __forceinline__ void load_lds16(const void* src, void* lds) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+// Raw buffer resource over [base, base + bytes): stride 0, dword 3 = 0x00020000 (32-bit data
+// format, the gfx9 raw-buffer setting); offsets at or past `bytes` read as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes, 0x00020000);
 }
+
+// One 16-byte buffer -> LDS load per lane (buffer_load_dwordx4 ... lds): lane i reads
+// base + voff_i and writes bytes [16 i, 16 i + 16) of the wave's 1 KB block at `lds` (which
+// must be the same for every lane; it goes to M0).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Workgroup barrier without the LDS-read wait that __syncthreads adds: the callers order
+// their own LDS traffic (vmcnt waits for the direct loads, register dependences for reads).
+__device__ __forceinline__ void barrier_no_lds_wait() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------
 // bf16 grouped GEMM C[r, n] = sum_k A[r, k] B_e[n, k] over each expert's row segment.
 // 256 x 256 workgroup tile, 4 waves in a 2x2 grid of 128 x 128 wave tiles, each a 4x4 grid of
 // v_mfma_f32_32x32x16_bf16 tiles (256 accumulators per lane). Operand tiles go from global
-// memory straight into LDS (global_load_lds_dwordx4: 64 lanes fill one contiguous 1 KB block)
+// memory straight into LDS (buffer_load_dwordx4 ... lds: 64 lanes fill one contiguous 1 KB
+// block; per-lane offsets are fixed, the K step moves the resource base in scalar registers)
 // through a ring of NS K-steps of BK; the 16-byte chunks of each row are XOR-swizzled so that
 // the 16-byte fragment reads of any 16 consecutive rows hit all 64 banks once.
 // The workgroup barrier sits before the last MFMA substep of each K step: after it, step s+1
@@ -153,7 +165,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
                                                  (static_cast<size_t>(e) * N + n0) * K) +
                    static_cast<size_t>(kpart) * nk * ROWB;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
 
   // direct loads: wave w fills 1 KB blocks w, w+4, ... of each operand tile
   const int lrow = lane / CPR, lslot = lane % CPR;
@@ -166,13 +179,16 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     aoff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < a_last ? r : a_last) * K + c * 8) * 2);
     boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * K + c * 8) * 2);
   }
+  // the clamped offsets stay below 256 rows of K elements past the resource base
+  const int span = BM * K * 2;
   auto issue = [&](int st) {   // loads of K step min(st, nk-1) into buffer st % NS
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
     const uint32_t kb = static_cast<uint32_t>(st < nk ? st : nk - 1) * ROWB;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(Ab + kb, span), rb = buffer_rsrc(Bb + kb, span);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) load_lds16(Ab + aoff[i] + kb, dst + i * 4096);
+    for (int i = 0; i < LOADS; ++i) load_lds16(ra, aoff[i], dst + i * 4096);
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) load_lds16(Bb + boff[i] + kb, dst + TILE + i * 4096);
+    for (int i = 0; i < LOADS; ++i) load_lds16(rb, boff[i], dst + TILE + i * 4096);
   };
 
   // fragment addressing: lane reads row (wave-tile row + l32), logical chunk 2 kk + hi
@@ -189,6 +205,47 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+
+  // Epilogue straight from the accumulators. The MFMAs take the B fragment as their first
+  // operand, so block (i, j) holds the transposed 32x32 result: lane (l32, hi) has tile row
+  // wm*128 + 32 i + l32 at columns wn*128 + 32 j + 8 q + 4 hi + (0..3), q = 0..3, i.e. four
+  // consecutive outputs of one row, stored as 8 bytes of bf16 (GeLU) or 16 bytes of float.
+  // N is a multiple of 64, so each 32-column block lies wholly inside or outside [0, N).
+  // Only the NI row blocks the wave multiplied can hold segment rows.
+  auto epilogue = [&](auto ni_const, auto bias_const) {
+    constexpr int NI = decltype(ni_const)::value;
+    constexpr bool BIAS = decltype(bias_const)::value;
+    float* fout = static_cast<float*>(kpart == 0 ? g.out : g.out2);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r = m0 + wm * 128 + i * 32 + l32;
+      if (r >= m_e) continue;
+      const size_t rowoff = static_cast<size_t>(row0 + r) * N;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cj = n0 + wn * 128 + j * 32;
+        if (cj >= N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cj + 8 * q + 4 * hi;
+          float o[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)   // one addition either way: GeLU then needs no canonicalisation
+            o[u] = acc[i][j][4 * q + u] + (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + c + u, true) : 0.0f);
+          if (EPI == kEpiGelu) {
+            bf16x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) pk[u] = static_cast<__bf16>(gelu_bf16_path(o[u]));
+            *reinterpret_cast<bf16x4*>(static_cast<u16*>(g.out) + rowoff + c) = pk;
+          } else {
+            *reinterpret_cast<floatx4*>(fout + rowoff + c) = floatx4{o[0], o[1], o[2], o[3]};
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time: bounded register use
+      }
+    }
+  };
+  const bool add_bias = kpart == 0 && g.bias != nullptr;
 
   // The wave multiplies only the 32-row blocks of its 128 rows that hold segment rows (2 or 4
   // of them; rows past the segment are never stored). Every wave still issues its share of
@@ -209,13 +266,28 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[f][i], fb[f][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
     };
-    // per substep: one fragment read (and, after the barrier, one operand load) after each
-    // of the first MFMAs, then the remaining MFMAs
+    // Before the barrier: one fragment read after each of the first MFMAs of the substep.
+    // After it, with full tiles (16 MFMAs): one operand load after each of the first 8 MFMAs,
+    // one fragment read after each of the last 8 (reads issued last are needed last); with
+    // fewer MFMAs, a read and a load after each MFMA.
     auto schedule = [&](bool with_loads) {
       constexpr int NR = NI + (NI > 0 ? 4 : 0);     // fragment reads per substep
       constexpr int NM = NI * 4;                     // MFMAs per substep
+      if (with_loads && NM == 16) {
+#pragma unroll
+        for (int q = 0; q < PER_STAGE; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < 16 - PER_STAGE; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        return;
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         if (q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -237,12 +309,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       }
       schedule(false);
       wait_vmcnt<(NS - 3) * PER_STAGE>();   // this thread's loads of step s+1 have landed
-      __syncthreads();                      // everyone's have; step s-1's buffer is free
+      // Everyone's have, and step s-1's buffer is free: every wave consumed its reads of step
+      // s-1 (issued before the previous barrier) in the MFMAs it ran before arriving here.
+      barrier_no_lds_wait();
       issue(s + NS - 1);
       read_frags(s + 1, 0, 0);              // past the last step this reads unused data
       mfmas((KK - 1) & 1);
       schedule(true);
     }
+    wait_vmcnt<0>();     // the trailing re-loads must land before the workgroup's LDS is released
+    if (add_bias)
+      epilogue(ni_const, std::true_type{});
+    else
+      epilogue(ni_const, std::false_type{});
   };
   const int valid = m_e - m0 - wm * 128;     // segment rows in this wave's 128 rows
   if (valid > 64)
@@ -251,58 +330,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     mainloop(std::integral_constant<int, 2>{});
   else
     mainloop(std::integral_constant<int, 0>{});
-  wait_vmcnt<0>();     // the trailing re-loads must land before LDS is reused
-  __syncthreads();   // LDS is reused below
-
-  // Epilogue through LDS, one 32-row block of the wave tile at a time: the 32x128 float block
-  // goes to this wave's LDS region, then every lane turns 8 consecutive values of a row into
-  // one 16-byte bf16 store (GeLU) or two 16-byte float stores.
-  constexpr int LDE = 128 + 4;
-  float* ep = reinterpret_cast<float*>(smem) + wave * 32 * LDE;
-  const int cg = lane & 15;                  // this lane's column group (8 columns)
-  const int ccol = n0 + wn * 128 + cg * 8;
-  float bias[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-    bias[q] = (kpart == 0 && ccol + q < N) ? load_bias(g.bias, static_cast<size_t>(e) * N + ccol + q, true) : 0.0f;
-  float* fout = static_cast<float*>(kpart == 0 ? g.out : g.out2);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) ep[(8 * (v >> 2) + 4 * hi + (v & 3)) * LDE + j * 32 + l32] = acc[i][j][v];
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rr = it * 4 + (lane >> 4);   // row within the 32-row block
-      const int r = m0 + wm * 128 + i * 32 + rr;
-      const floatx4 v0 = *reinterpret_cast<const floatx4*>(ep + rr * LDE + cg * 8);
-      const floatx4 v1 = *reinterpret_cast<const floatx4*>(ep + rr * LDE + cg * 8 + 4);
-      if (r < m_e && ccol < N) {
-        float o[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        const size_t off = static_cast<size_t>(row0 + r) * N + ccol;
-        if (EPI == kEpiGelu) {
-          u32x4 pk;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            pk[q] = pack_bf16x2(gelu_bf16_path(o[2 * q] + bias[2 * q]), gelu_bf16_path(o[2 * q + 1] + bias[2 * q + 1]));
-          *reinterpret_cast<u32x4*>(static_cast<u16*>(g.out) + off) = pk;
-        } else {
-          floatx4 w0, w1;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            w0[q] = o[q] + bias[q];
-            w1[q] = o[4 + q] + bias[4 + q];
-          }
-          floatx4* dst = reinterpret_cast<floatx4*>(fout + off);
-          dst[0] = w0;
-          dst[1] = w1;
-        }
-      }
-    }
-    __syncthreads();
-  }
 }
 
 // ---------------------------------------------------------------------------------------

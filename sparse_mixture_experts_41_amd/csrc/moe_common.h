@@ -8,6 +8,7 @@ namespace moe {
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -67,18 +68,21 @@ __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erff(v * 0.70710678118654752440f));
 }
 
-// GeLU(v) = v/2 (1 + erf(v / sqrt 2)) with erf from Abramowitz & Stegun, Handbook of
-// Mathematical Functions, formula 7.1.26: for x >= 0, 1 - erf(x) = t (a1 + a2 t + ... + a5 t^4)
-// e^(-x^2), t = 1 / (1 + p x), |error| <= 1.5e-7. Written for 1 + erf(v/sqrt 2) directly (no
-// cancellation for v < 0). |GeLU error| <= 2.2e-7 everywhere, and the relative error stays
-// below half a bf16 step (2^-9) for v >= -5; used only where the result is rounded to bf16.
+// GeLU(v) = v Phi(v) with the normal tail h = Phi(-|v|) = (1 - erf(|v| / sqrt 2)) / 2 from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26: for x >= 0,
+// 1 - erf(x) = t (a1 + a2 t + ... + a5 t^4) e^(-x^2), t = 1 / (1 + p x), |error| <= 1.5e-7.
+// Here x = |v| / sqrt 2, the coefficients are halved and e^(-x^2) = 2^(-v^2 / (2 ln 2)); then
+// GeLU(v) = max(v, 0) - |v| h for both signs (no cancellation for v < 0). The error is at most
+// 0.75e-7 |v| plus float32 rounding (3.3e-7 absolute over [-12, 12]), and the relative error
+// stays below half a bf16 step (2^-9) for v >= -5; used only where the result is rounded to
+// bf16. |v| is capped at FLT_MAX in the last product so that GeLU(+inf) = +inf.
 __device__ __forceinline__ float gelu_bf16_path(float v) {
-  const float x = fabsf(v) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  const float a = fabsf(v);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189f, a, 1.0f));     // p / sqrt 2
   const float poly =
-      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 1.061405429f, -1.453152027f), 1.421413741f), -0.284496736f), 0.254829592f);
-  const float q = poly * __expf(-x * x);   // 1 - erf(x)
-  return 0.5f * v * (v >= 0.0f ? 2.0f - q : q);
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5307027f, -0.72657603f), 0.7107069f), -0.14224836f), 0.1274148f);
+  const float h = poly * __builtin_amdgcn_exp2f((v * v) * -0.7213475f);   // -1 / (2 ln 2)
+  return fmaf(-fminf(a, 3.4028235e38f), h, fmaxf(v, 0.0f));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
