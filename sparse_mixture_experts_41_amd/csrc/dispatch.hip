@@ -5,10 +5,10 @@
 // token index), counted per expert, and each expert keeps only the first C = ceil(c k T / E)
 // of its slots; the rest are dropped and contribute nothing. The page's version sorts the
 // slots; here the same order comes from a counting sort that needs no sort at all:
-//   per-block histograms (64 tokens per block, written by the router or by the histogram
-//   kernel) -> a one-workgroup scan giving, for every (block, expert), the number of earlier
-//   slots of that expert -> in each block, a slot's rank among its expert's slots is that base
-//   plus the number of lower lanes of the wave that chose the same expert (wave ballot).
+//   per-group histograms (16 tokens per group, written by the router or by the histogram
+//   kernel) -> a one-workgroup scan giving, for every (group, expert), the number of earlier
+//   slots of that expert -> a slot's rank among its expert's slots is that base plus the
+//   number of lower lanes of its 16-lane group that chose the same expert (wave ballot).
 // A token never picks an expert twice, so ranks are unique and the result is bit-exact.
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -25,18 +25,26 @@ __device__ __forceinline__ int pow2_at_least(int v) {
   return p;
 }
 
-// Fixed-order column sums of part [nb,E]: group g of threads sums a contiguous run of blocks
-// in ascending order, then group sums are added in ascending group order. Needs all
+// Fixed-order column sums of part [ng,E]: group g of threads sums a contiguous run of rows
+// in ascending order, then the group sums are added in ascending group order. Needs all
 // kScanThreads threads of the workgroup; `lds` holds kScanThreads floats.
-__device__ void blocked_colsum(const float* __restrict__ part, int nb, int E, float* __restrict__ out, float* lds) {
+__device__ void blocked_colsum(const float* __restrict__ part, int ng, int E, float* __restrict__ out, float* lds) {
   const int E2 = pow2_at_least(E);
   const int G = kScanThreads / E2;
-  const int chunk = (nb + G - 1) / G;
+  const int chunk = (ng + G - 1) / G;
   const int e = threadIdx.x % E2, g = threadIdx.x / E2;
   float s = 0.0f;
   if (e < E) {
-    const int b0 = g * chunk, b1 = min(nb, b0 + chunk);
-    for (int b = b0; b < b1; ++b) s += part[static_cast<size_t>(b) * E + e];
+    const int b0 = g * chunk, b1 = min(ng, b0 + chunk);
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {            // eight independent loads in flight, added in order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += part[static_cast<size_t>(b) * E + e];
   }
   lds[threadIdx.x] = s;
   __syncthreads();
@@ -48,42 +56,60 @@ __device__ void blocked_colsum(const float* __restrict__ part, int nb, int E, fl
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kScanThreads) void colsum_kernel(const float* __restrict__ part, int nb, int E,
+__global__ __launch_bounds__(kScanThreads) void colsum_kernel(const float* __restrict__ part, int ng, int E,
                                                               float* __restrict__ out) {
   __shared__ float lds[kScanThreads];
-  blocked_colsum(part, nb, E, out, lds);
+  blocked_colsum(part, ng, E, out, lds);
 }
 
-__device__ __forceinline__ void write_stats(const int32_t* counts, const float* colsum, int E, int k, int T,
-                                            float* f, float* P, float* L) {
-  // f_e = counts_e / (k T) and P_e = colsum_e / T, each rounded once from float64;
-  // L = E * sum_e f_e P_e accumulated in float64 in expert order.
-  const double kT = static_cast<double>(k) * static_cast<double>(T);
-  double acc = 0.0;
-  for (int e = 0; e < E; ++e) {
+// f_e = counts_e / (k T) and P_e = colsum_e / T, each rounded once from float64, one expert
+// per lane of wave 0; L = E * sum_e f_e P_e accumulated in float64 in expert order by lane 0.
+// `prod` is LDS scratch of kMaxE doubles. Called by all threads of the workgroup.
+__device__ void write_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,
+                            float* L, double* prod) {
+  const int e = threadIdx.x;
+  if (e < E) {
+    const double kT = static_cast<double>(k) * static_cast<double>(T);
     const float fe = static_cast<float>(static_cast<double>(counts[e]) / kT);
     const float pe = static_cast<float>(static_cast<double>(colsum[e]) / static_cast<double>(T));
     f[e] = fe;
     P[e] = pe;
-    acc += static_cast<double>(fe) * static_cast<double>(pe);
+    prod[e] = static_cast<double>(fe) * static_cast<double>(pe);
   }
-  L[0] = static_cast<float>(static_cast<double>(E) * acc);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int ee = 0; ee < E; ++ee) acc += prod[ee];
+    L[0] = static_cast<float>(static_cast<double>(E) * acc);
+  }
 }
 
+// Counts, capacity truncation, expert offsets and the per-(group, expert) base ranks, plus the
+// balance statistics when the probability partials are given. One workgroup.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __shared__ int ilds[kScanThreads];
   __shared__ float flds[kScanThreads];
   __shared__ int tot[kMaxE];
   __shared__ float csum[kMaxE];
-  const int E = a.E, nb = a.nb;
+  __shared__ double prod[kMaxE];
+  const int E = a.E, ng = a.ng;
   const int E2 = pow2_at_least(E);
   const int G = kScanThreads / E2;
-  const int chunk = (nb + G - 1) / G;
+  const int chunk = (ng + G - 1) / G;
   const int e = threadIdx.x % E2, g = threadIdx.x / E2;
-  const int b0 = g * chunk, b1 = min(nb, b0 + chunk);
+  const int b0 = g * chunk, b1 = min(ng, b0 + chunk);
   int s = 0;
-  if (e < E)
-    for (int b = b0; b < b1; ++b) s += a.hist[static_cast<size_t>(b) * E + e];
+  if (e < E) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.hist[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += a.hist[static_cast<size_t>(b) * E + e];
+  }
   ilds[threadIdx.x] = s;
   __syncthreads();
   if (e < E) {
@@ -91,38 +117,54 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     for (int gg = 0; gg < g; ++gg) pre += ilds[gg * E2 + e];
     if (g == G - 1) tot[e] = pre + s;
     int run = pre;
-    for (int b = b0; b < b1; ++b) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.hist[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a.blockbase[static_cast<size_t>(b + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; b < b1; ++b) {
       a.blockbase[static_cast<size_t>(b) * E + e] = run;
       run += a.hist[static_cast<size_t>(b) * E + e];
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int off = 0;
-    for (int ee = 0; ee < E; ++ee) {
-      const int c = tot[ee];
-      const int kp = c < a.C ? c : a.C;
+  if (threadIdx.x < kWave) {                 // wave 0: one expert per lane, exclusive scan of kept
+    const int ee = threadIdx.x;
+    const int c = ee < E ? tot[ee] : 0;
+    const int kp = c < a.C ? c : a.C;
+    int incl = kp;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int n = __shfl_up(incl, off);
+      if (ee >= off) incl += n;
+    }
+    if (ee < E) {
       a.counts[ee] = c;
       a.kept[ee] = kp;
-      a.offsets[ee] = off;
-      off += kp;
+      a.offsets[ee] = incl - kp;
     }
   }
   if (a.probsum_part != nullptr) {
-    blocked_colsum(a.probsum_part, nb, E, csum, flds);   // contains __syncthreads
-    if (threadIdx.x == 0) {
-      for (int ee = 0; ee < E; ++ee) a.colsum[ee] = csum[ee];
-      write_stats(tot, csum, E, a.k, a.T, a.f, a.P, a.L);
-    }
+    blocked_colsum(a.probsum_part, ng, E, csum, flds);   // contains __syncthreads
+    if (threadIdx.x < E) a.colsum[threadIdx.x] = csum[threadIdx.x];
+    write_stats(tot, csum, E, a.k, a.T, a.f, a.P, a.L, prod);
   }
 }
 
 __global__ __launch_bounds__(64) void stats_kernel(const int32_t* __restrict__ counts, const float* __restrict__ colsum,
                                                    int E, int k, int T, float* f, float* P, float* L) {
-  if (threadIdx.x == 0) write_stats(counts, colsum, E, k, T, f, P, L);
+  __shared__ double prod[kMaxE];
+  write_stats(counts, colsum, E, k, T, f, P, L, prod);
 }
 
-// One wave per 64-token block: stable ranks by wave ballot, capacity test, dest and perm.
+// One wave per 64 tokens: stable ranks by wave ballot within each 16-token group, capacity
+// test, dest and perm.
 __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ blockbase,
                                                     const int32_t* __restrict__ offsets, int T, int E, int k,
@@ -150,6 +192,8 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
   __syncthreads();
   if (!valid) return;
   const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t gmask = 0xFFFFull << (lane & ~(kGroupTokens - 1));   // this lane's 16-lane group
+  const int grp = t / kGroupTokens;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
@@ -158,7 +202,7 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
         dest[static_cast<size_t>(t) * k + j] = -1;
         continue;
       }
-      const int r = blockbase[static_cast<size_t>(blk) * E + e] + __popcll(emask[e] & below);
+      const int r = blockbase[static_cast<size_t>(grp) * E + e] + __popcll(emask[e] & below & gmask);
       int dst = -1;
       if (r < C) {
         dst = offsets[e] + r;
@@ -186,8 +230,8 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_colsum(const float* part, int nb, int E, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(colsum_kernel, dim3(1), dim3(kScanThreads), 0, stream, part, nb, E, out);
+hipError_t launch_colsum(const float* part, int ng, int E, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(colsum_kernel, dim3(1), dim3(kScanThreads), 0, stream, part, ng, E, out);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ struct Derived {
   int T, d, E, k, dff;
   int64_t C;
   int R;       // rows of the expert-sorted buffers: min(k*T, E*C)
-  int nb;      // 64-token routing blocks
+  int ng;      // 16-token routing groups
   bool bf16;
   size_t esize;
   float tau;
@@ -32,7 +32,7 @@ struct Derived {
 };
 
 struct Layout {
-  size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
+  size_t probsum, hist, blockbase, colsum, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
       y_perm2, total;
 };
 
@@ -86,7 +86,7 @@ moe_status check_config(const moe_config* cfg, Derived* D) {
   const int64_t ecap = D->C >= T ? E * T : E * D->C;        // an expert never gets more than T slots
   const int64_t R = (k * T < ecap) ? k * T : ecap;
   D->R = static_cast<int>(R);
-  D->nb = static_cast<int>((T + 63) / 64);
+  D->ng = static_cast<int>((T + 15) / 16);
   D->bf16 = bf16;
   D->esize = bf16 ? 2 : 4;
   D->tau = cfg->temperature;
@@ -104,12 +104,11 @@ Layout layout_of(const Derived& D) {
     off += (bytes + 255) & ~static_cast<size_t>(255);
     return o;
   };
-  const size_t T = D.T, E = D.E, k = D.k, nb = D.nb, R = D.R;
-  L.probsum = take(nb * E * 4);
-  L.hist = take(nb * E * 4);
-  L.blockbase = take(nb * E * 4);
+  const size_t T = D.T, E = D.E, k = D.k, ng = D.ng, R = D.R;
+  L.probsum = take(ng * E * 4);
+  L.hist = take(ng * E * 4);
+  L.blockbase = take(ng * E * 4);
   L.colsum = take(E * 4);
-  L.zpart = take(D.bf16 ? static_cast<size_t>(moe::router_plan(D.T, D.d, D.E).ks) * T * E * 4 : 0);
   L.logits = take(T * E * 4);
   L.scores = take(T * E * 4);
   L.idx = take(T * k * 4);
@@ -184,6 +183,7 @@ moe::RouterArgs router_args(const Derived& D, const void* x, const void* Wg, con
   a.w = w;
   a.probsum_part = probsum;
   a.hist = hist;
+  a.ng = D.ng;
   return a;
 }
 
@@ -223,8 +223,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* Wg, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const moe::RouterArgs a = router_args(D, x, Wg, bg, logits, scores, topk_idx, topk_w, at<float>(ws, L.probsum),
                                         at<int32_t>(ws, L.hist));
-  MOE_HIP(moe::launch_router(a, at<float>(ws, L.zpart), st), "router");
-  MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.nb, D.E, prob_colsum, st), "colsum");
+  MOE_HIP(moe::launch_router(a, st), "router");
+  MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.ng, D.E, prob_colsum, st), "colsum");
   return MOE_OK;
 }
 
@@ -249,7 +249,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
   MOE_HIP(moe::launch_histogram(topk_idx, D.T, D.E, D.k, hist, st), "histogram");
   moe::ScanArgs s{};
   s.hist = hist;
-  s.nb = D.nb;
+  s.ng = D.ng;
   s.E = D.E;
   s.k = D.k;
   s.T = D.T;
@@ -385,12 +385,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
   // 1-2. router: logits, scores, softmax, top-k, weights, block partials
   const moe::RouterArgs ra = router_args(D, x, Wg, bg, logits, scores, idx, w, probsum, hist);
-  MOE_HIP(moe::launch_router(ra, at<float>(ws, Lw.zpart), st), "router");
+  MOE_HIP(moe::launch_router(ra, st), "router");
   if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
   // 3a. counts, capacity, offsets, block bases; f, P, L
   moe::ScanArgs s{};
   s.hist = hist;
-  s.nb = D.nb;
+  s.ng = D.ng;
   s.E = D.E;
   s.k = D.k;
   s.T = D.T;

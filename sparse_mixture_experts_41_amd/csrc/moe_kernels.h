@@ -20,33 +20,28 @@ struct RouterArgs {
   float* scores;          // [T,E] or null
   int32_t* idx;           // [T,k]
   float* w;               // [T,k]
-  float* probsum_part;    // [nb,E], nb = ceil(T/64)
-  int32_t* hist;          // [nb,E]
+  float* probsum_part;    // [ng,E], ng = ceil(T/16) token groups
+  int32_t* hist;          // [ng,E]
+  int ng;
 };
-// Logit kernel shape for bf16: tokens per workgroup 16*mt, K split into ks slices.
-struct RouterPlan {
-  int mt = 1, ks = 1;
-};
-RouterPlan router_plan(int T, int d, int E);
-// zpart: float [ks, T, E] workspace of the logit partial sums (unused for float32).
-hipError_t launch_router(const RouterArgs& a, float* zpart, hipStream_t stream);
+hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
 
-// Per-block expert histogram of top-k indices ([nb,E], 64 tokens per block).
+// Per-group expert histogram of top-k indices ([ng,E], 16 tokens per group).
 hipError_t launch_histogram(const int32_t* idx, int T, int E, int k, int32_t* hist, hipStream_t stream);
 
-// Fixed-order column sums of per-block partials [nb,E] -> [E].
-hipError_t launch_colsum(const float* part, int nb, int E, float* out, hipStream_t stream);
+// Fixed-order column sums of per-group partials [ng,E] -> [E].
+hipError_t launch_colsum(const float* part, int ng, int E, float* out, hipStream_t stream);
 
 struct ScanArgs {
-  const int32_t* hist;    // [nb,E]
-  int nb, E, k, T;
+  const int32_t* hist;    // [ng,E]
+  int ng, E, k, T;
   int C;
   int32_t* counts;        // [E]
   int32_t* kept;          // [E]
   int32_t* offsets;       // [E]
-  int32_t* blockbase;     // [nb,E]
+  int32_t* blockbase;     // [ng,E] earlier slots of each expert before each group
   // optional statistics (all null or all set)
-  const float* probsum_part;  // [nb,E]
+  const float* probsum_part;  // [ng,E]
   float* colsum;          // [E]
   float* f;               // [E]
   float* P;               // [E]

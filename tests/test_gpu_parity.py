@@ -36,7 +36,7 @@ SMALL = {
     # float32 with Gumbel noise and a temperature
     "f32_gumbel": (MoEShape("f32_gumbel", T=300, d=96, E=6, k=2, d_ffn=200, capacity_factor=0.9, temperature=0.5,
                             gumbel=True, dtype="f32", seed=7), 0.1),
-    # tokens spanning many 64-token routing blocks, E not a multiple of 16
+    # tokens spanning many 16-token routing groups and 64-token permutation waves, E not a multiple of 16
     "many_blocks": (MoEShape("many_blocks", T=3000, d=128, E=37, k=4, d_ffn=128, capacity_factor=1.1,
                              wg_std=None), 0.0),
 }
