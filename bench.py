@@ -168,9 +168,13 @@ def main() -> int:
     achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{shape.name}.json")
     traffic = stored_traffic(traffic_path, dom_name)
-    nb = (T + 63) // 64
-    router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + nb * E * 8
-    dispatch_bytes = T * k * 4 + T * k * 4 + kept * 4 + 2 * kept * d * sx
+    ng = (T + 15) // 16
+    router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + ng * E * 8
+    # GEMM1 reads the token rows through the permutation (no gathered copy) on the bf16 MFMA
+    # path while x is addressable by 32-bit offsets; otherwise dispatch also copies the rows
+    C = ops.capacity(cfg)
+    gather_fused = shape.dtype == "bf16" and min(C, T) > 16 and T * d * 2 < 2 ** 31
+    dispatch_bytes = T * k * 4 + T * k * 4 + kept * 4 + (0 if gather_fused else 2 * kept * d * sx)
     combine_bytes = kept * d * 4 + T * k * 8 + T * d * sx
     disp_ms = stage["scan"] + stage["permute_gather"]
     line = {
@@ -196,7 +200,8 @@ def main() -> int:
                          "kept_rows": kept, "dropped_slots": int(k * T - kept)},
         "hbm_stages": {
             "router": {"GB/s": router_bytes / (stage["route"] * 1e-3) / 1e9, "bytes": router_bytes},
-            "dispatch": {"GB/s": dispatch_bytes / (disp_ms * 1e-3) / 1e9, "bytes": dispatch_bytes},
+            "dispatch": {"GB/s": dispatch_bytes / (disp_ms * 1e-3) / 1e9, "bytes": dispatch_bytes,
+                         "gather_fused_into_gemm1": gather_fused},
             "combine": {"GB/s": combine_bytes / (stage["combine"] * 1e-3) / 1e9, "bytes": combine_bytes},
             "peak_GB/s": PEAK_HBM_GBS,
         },

@@ -25,9 +25,9 @@ __device__ __forceinline__ int pow2_at_least(int v) {
   return p;
 }
 
-// Fixed-order column sums of part [ng,E]: group g of threads sums a contiguous run of rows
-// in ascending order, then the group sums are added in ascending group order. Needs all
-// kScanThreads threads of the workgroup; `lds` holds kScanThreads floats.
+// Fixed-order column sums of part [ng,E]: thread group g sums a contiguous run of rows in
+// ascending order, then the group sums are added by a pairwise tree over g (a fixed order).
+// Needs all kScanThreads threads of the workgroup; `lds` holds kScanThreads floats.
 __device__ void blocked_colsum(const float* __restrict__ part, int ng, int E, float* __restrict__ out, float* lds) {
   const int E2 = pow2_at_least(E);
   const int G = kScanThreads / E2;
@@ -48,11 +48,11 @@ __device__ void blocked_colsum(const float* __restrict__ part, int ng, int E, fl
   }
   lds[threadIdx.x] = s;
   __syncthreads();
-  if (g == 0 && e < E) {
-    float t = 0.0f;
-    for (int gg = 0; gg < G; ++gg) t += lds[gg * E2 + e];
-    out[e] = t;
+  for (int h = G >> 1; h > 0; h >>= 1) {     // G is a power of two
+    if (g < h) lds[threadIdx.x] += lds[threadIdx.x + h * E2];
+    __syncthreads();
   }
+  if (g == 0 && e < E) out[e] = lds[e];
   __syncthreads();
 }
 
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   int s = 0;
   if (e < E) {
     int b = b0;
-    for (; b + 8 <= b1; b += 8) {
+    for (; b + 8 <= b1; b += 8) {            // eight independent loads in flight, added in order
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = a.hist[static_cast<size_t>(b + u) * E + e];
@@ -112,9 +112,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   }
   ilds[threadIdx.x] = s;
   __syncthreads();
+  for (int off = 1; off < G; off <<= 1) {    // inclusive scan over the thread groups
+    const int v = g >= off ? ilds[threadIdx.x - off * E2] : 0;
+    __syncthreads();
+    ilds[threadIdx.x] += v;
+    __syncthreads();
+  }
   if (e < E) {
-    int pre = 0;
-    for (int gg = 0; gg < g; ++gg) pre += ilds[gg * E2 + e];
+    const int pre = ilds[threadIdx.x] - s;
     if (g == G - 1) tot[e] = pre + s;
     int run = pre;
     int b = b0;

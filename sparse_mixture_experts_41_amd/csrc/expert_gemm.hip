@@ -24,7 +24,7 @@ namespace moe {
 namespace {
 
 struct GemmArgs {
-  const void* A;          // [R,K] expert-sorted rows
+  const void* A;          // [R,K] expert-sorted rows, or [a_rows,K] rows picked by `rows`
   const void* B;          // [E,N,K] weights
   const void* bias;       // [E,N] or null (dtype)
   void* out;              // [R,N]
@@ -34,6 +34,8 @@ struct GemmArgs {
   int R, C;               // rows of A/out and the capacity: segments outside them are skipped
   int splits;             // K is split into this many equal parts (1 or 2)
   void* out2;             // [R,N] float partial sums of the second K part (splits == 2)
+  const int32_t* rows;    // [R] or null: A row of expert-sorted row r is rows[r] (fused gather)
+  int a_rows;             // rows of A when `rows` is set (a_rows * K * 2 < 2^31)
 };
 
 enum { kEpiGelu = 0, kEpiLinear = 1 };
@@ -160,7 +162,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int N = g.N, K = g.K;
   const int nk = K / BK / g.splits;          // K steps of this part
-  const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + static_cast<size_t>(row0 + m0) * K) +
+  const bool gathered = g.rows != nullptr;
+  const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) +
+                                                 (gathered ? 0 : static_cast<size_t>(row0 + m0) * K)) +
                    static_cast<size_t>(kpart) * nk * ROWB;
   const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
                                                  (static_cast<size_t>(e) * N + n0) * K) +
@@ -176,15 +180,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   for (int i = 0; i < LOADS; ++i) {
     const int r = (wave + 4 * i) * RPI + lrow;
     const int c = lslot ^ ((r / RPS) % CPR);
-    aoff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < a_last ? r : a_last) * K + c * 8) * 2);
+    const int ra = r < a_last ? r : a_last;
+    const uint32_t arow = gathered ? static_cast<uint32_t>(g.rows[row0 + m0 + ra]) : static_cast<uint32_t>(ra);
+    aoff[i] = static_cast<uint32_t>((arow * K + c * 8) * 2);
     boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * K + c * 8) * 2);
   }
-  // the clamped offsets stay below 256 rows of K elements past the resource base
-  const int span = BM * K * 2;
+  // the clamped offsets stay below 256 rows of K elements past the B resource base and below
+  // the tile's (or, gathered, all of A's) rows past the A base; anything beyond reads as zero
+  const int span = BM * K * 2, span_a = gathered ? g.a_rows * K * 2 : span;
   auto issue = [&](int st) {   // loads of K step min(st, nk-1) into buffer st % NS
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
     const uint32_t kb = static_cast<uint32_t>(st < nk ? st : nk - 1) * ROWB;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(Ab + kb, span), rb = buffer_rsrc(Bb + kb, span);
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(Ab + kb, span_a), rb = buffer_rsrc(Bb + kb, span);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) load_lds16(ra, aoff[i], dst + i * 4096);
 #pragma unroll
@@ -459,6 +466,10 @@ int tile_grid(int R, int E, int C, int BM, int N, int BN) {
 
 }  // namespace
 
+bool ffn_gathers(const FfnArgs& a) {
+  return a.bf16 && a.C > 16 && static_cast<long long>(a.T) * a.d * 2 < (1ll << 31);
+}
+
 int ffn_splits(const FfnArgs& a) {
   if (!a.bf16 || a.C <= 16) return 1;
   const int tiles2 = tile_grid(a.R, a.E, a.C, 256, a.d, 256);
@@ -466,8 +477,9 @@ int ffn_splits(const FfnArgs& a) {
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
-  GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr};
-  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2};
+  GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr, nullptr, 0};
+  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2,
+              nullptr, 0};
   hipError_t err;
   if (!a.bf16) {
     const int grid1 = tile_grid(a.R, a.E, a.C, FBM, a.d_ffn, 16);
@@ -486,6 +498,11 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
     hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiLinear>, dim3(a.E * ((a.d + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
                        stream, g2);
     return hipGetLastError();
+  }
+  if (a.rows != nullptr) {                   // GEMM1 reads the token rows of x directly
+    g1.A = a.x;
+    g1.rows = a.rows;
+    g1.a_rows = a.T;
   }
   const int grid1 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d_ffn, 256));
   const int grid2 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d, 256) * g2.splits);

@@ -32,7 +32,7 @@ struct Derived {
 };
 
 struct Layout {
-  size_t probsum, hist, blockbase, colsum, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
+  size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
       y_perm2, total;
 };
 
@@ -109,6 +109,8 @@ Layout layout_of(const Derived& D) {
   L.hist = take(ng * E * 4);
   L.blockbase = take(ng * E * 4);
   L.colsum = take(E * 4);
+  const int ks = D.bf16 ? moe::router_slices(D.T, D.d, D.E) : 1;
+  L.zpart = take(ks > 1 ? static_cast<size_t>(ks) * T * E * 4 : 0);
   L.logits = take(T * E * 4);
   L.scores = take(T * E * 4);
   L.idx = take(T * k * 4);
@@ -223,7 +225,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* Wg, const
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const moe::RouterArgs a = router_args(D, x, Wg, bg, logits, scores, topk_idx, topk_w, at<float>(ws, L.probsum),
                                         at<int32_t>(ws, L.hist));
-  MOE_HIP(moe::launch_router(a, st), "router");
+  MOE_HIP(moe::launch_router(a, at<float>(ws, L.zpart), st), "router");
   MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.ng, D.E, prob_colsum, st), "colsum");
   return MOE_OK;
 }
@@ -385,7 +387,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
   // 1-2. router: logits, scores, softmax, top-k, weights, block partials
   const moe::RouterArgs ra = router_args(D, x, Wg, bg, logits, scores, idx, w, probsum, hist);
-  MOE_HIP(moe::launch_router(ra, st), "router");
+  MOE_HIP(moe::launch_router(ra, at<float>(ws, Lw.zpart), st), "router");
   if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
   // 3a. counts, capacity, offsets, block bases; f, P, L
   moe::ScanArgs s{};
@@ -406,13 +408,14 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   s.L = L;
   MOE_HIP(moe::launch_scan(s, st), "scan");
   if (ev) MOE_HIP(hipEventRecord(ev[2], st), "event");
-  // 3b. stable permutation with the drop mask, then the row gather
-  MOE_HIP(moe::launch_permute(idx, blockbase, offsets, D.T, D.E, D.k, C, dest, perm, st), "permute");
-  MOE_HIP(moe::launch_gather(x, perm, kept, offsets, D.E, D.R, static_cast<int>(D.d * D.esize), x_perm, st),
-          "gather");
-  if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
-  // 4. experts
+  // 3b. stable permutation with the drop mask, then the row gather (unless GEMM1 reads the
+  // token rows through the permutation itself)
   moe::FfnArgs fa{};
+  fa.x = x;
+  fa.T = D.T;
+  fa.rows = nullptr;
+  MOE_HIP(moe::launch_permute(idx, blockbase, offsets, D.T, D.E, D.k, C, dest, perm, st), "permute");
+  // 4. experts
   fa.x_perm = x_perm;
   fa.kept = kept;
   fa.offsets = offsets;
@@ -429,6 +432,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   fa.C = C;
   fa.bf16 = D.bf16 ? 1 : 0;
   fa.y_perm2 = at<float>(ws, Lw.y_perm2);
+  if (moe::ffn_gathers(fa))
+    fa.rows = perm;
+  else
+    MOE_HIP(moe::launch_gather(x, perm, kept, offsets, D.E, D.R, static_cast<int>(D.d * D.esize), x_perm, st),
+            "gather");
+  if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
   MOE_HIP(moe::launch_expert_ffn(fa, st, ev ? ev[4] : nullptr), "expert_ffn");
   if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
   // 5. combine (adding the two K halves of GEMM2 when it was split)

@@ -14,6 +14,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
+constexpr int kWaves = 4;          // waves of a 256-thread workgroup
 constexpr int kBlockTokens = 64;   // tokens per permutation wave (one lane per token)
 constexpr int kGroupTokens = 16;   // tokens per routing group (one histogram / probability-sum row)
 constexpr int kMaxE = 64;

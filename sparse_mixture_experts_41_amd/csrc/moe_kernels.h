@@ -24,7 +24,10 @@ struct RouterArgs {
   int32_t* hist;          // [ng,E]
   int ng;
 };
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream);
+// K slices of the bf16 router (1 = one fused kernel); zpart needs slices * T * E floats when
+// slices > 1 (unused otherwise and for float32).
+int router_slices(int T, int d, int E);
+hipError_t launch_router(const RouterArgs& a, float* zpart, hipStream_t stream);
 
 // Per-group expert histogram of top-k indices ([ng,E], 16 tokens per group).
 hipError_t launch_histogram(const int32_t* idx, int T, int E, int k, int32_t* hist, hipStream_t stream);
@@ -56,7 +59,10 @@ hipError_t launch_gather(const void* x, const int32_t* perm, const int32_t* kept
                          int E, int R, int row_bytes, void* x_perm, hipStream_t stream);
 
 struct FfnArgs {
-  const void* x_perm;     // [R,d]
+  const void* x_perm;     // [R,d] (unused when rows is set)
+  const void* x;          // [T,d] token rows, read through `rows` (bf16 MFMA path only)
+  const int32_t* rows;    // [R] or null: x row of expert-sorted row r (perm); see ffn_gathers
+  int T;
   const int32_t* kept;    // [E]
   const int32_t* offsets; // [E]
   const void* W1;         // [E,d_ffn,d]
@@ -69,6 +75,9 @@ struct FfnArgs {
   int E, d, d_ffn, R, C;
   int bf16;
 };
+// Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
+// copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
+bool ffn_gathers(const FfnArgs& a);
 // Number of K parts GEMM2 is split into (1 or 2): 2 when its tiles would fill fewer than four
 // rounds of the 256 CUs. With 2, y_perm + y_perm2 (summed in float32) is the GEMM2 result.
 int ffn_splits(const FfnArgs& a);

@@ -9,8 +9,10 @@
 //
 // Layout (bfloat16): one workgroup per 16 tokens computes their logits over all of d with
 // MFMAs, reading each x row once, adds the four wave partials in a fixed order, and runs
-// softmax and top-k with one lane per token row (the row lives in LDS). Partial statistics
-// (column sums of p, expert histograms) are written per group of 16 tokens.
+// softmax and top-k with four lanes per token row (the row lives in LDS). With fewer than 256
+// groups of 16 tokens, d is cut into K slices instead: slice partials go to a workspace and a
+// second kernel adds them in slice order before the same epilogue. Partial statistics (column
+// sums of p, expert histograms) are written per group of 16 tokens.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -135,7 +137,8 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
                                   float* __restrict__ w_out) {
   const int lane = lane_id();
   const size_t base = static_cast<size_t>(t0) * E;
-  for (int i = lane; i < nt * E; i += kWave) logits[base + i] = rows[(i / E) * ldr + i % E];
+  for (int r = 0; r < nt; ++r)               // E <= 64: one coalesced row per step
+    if (lane < E) logits[base + static_cast<size_t>(r) * E + lane] = rows[r * ldr + lane];
   const int tl = lane >> 2, q = lane & 3;
   const int EQ = (E + 3) >> 2;
   const int e0 = q * EQ, e1 = min(E, e0 + EQ);
@@ -152,7 +155,8 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
   }
   __syncthreads();
   if (scores)
-    for (int i = lane; i < nt * E; i += kWave) scores[base + i] = rows[(i / E) * ldr + i % E];
+    for (int r = 0; r < nt; ++r)
+      if (lane < E) scores[base + static_cast<size_t>(r) * E + lane] = rows[r * ldr + lane];
   __syncthreads();
   if (!valid) {
     for (int e = e0; e < e1; ++e) row[e] = 0.0f;
@@ -214,26 +218,63 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
   return q == 0 ? sel : 0ull;
 }
 
-// bf16 router: one workgroup per 16 tokens over all of d. The d/64 chunks of 64 are dealt
-// round-robin to the 4 waves; each wave issues the loads of NB chunks before their MFMAs and
-// accumulates NT tiles of v_mfma_f32_16x16x32_bf16 (x rows as A, W_g rows as B, both
-// K-contiguous). The four wave partials are added in LDS in wave order, the bias is added, and
-// wave 0 runs the epilogue.
-template <int NT, int NB>
-__global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
+// One wave per 16-token group `grp`: epilogue (four lanes per token) and the group partials.
+// `rows` holds the group's logits with b_g added; rows past nt_tok are ignored.
+__device__ void group_finish(const RouterArgs& a, float* rows, int LDE, int t0, int nt_tok, int grp) {
+  const int lane = lane_id();
+  const int E = a.E;
+  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.gumbel, a.key0, a.key1, a.logits,
+                                     a.scores, a.idx, a.w);
+  __syncthreads();
+  // group partials: column sums of p over the 16 rows (ascending), and the histogram, whose bits
+  // come from lane 4 t of each token (the popcount of the whole ballot)
+  const size_t gofs = static_cast<size_t>(grp) * E;
+  if (lane < E) {
+    float ps = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kGroupTokens; ++r) ps += rows[r * LDE + lane];
+    a.probsum_part[gofs + lane] = ps;
+  }
+  // each token's mask (held by lane 4 t) to LDS, then lane e counts expert e over the tokens
+  __shared__ uint64_t masks[kWaves][kGroupTokens];
+  uint64_t* mk = masks[threadIdx.x >> 6];
+  if ((lane & 3) == 0) mk[lane >> 2] = sel;   // zero for tokens past nt_tok
+  __syncthreads();
+  if (lane < E) {
+    int c = 0;
+#pragma unroll
+    for (int t = 0; t < kGroupTokens; ++t) c += static_cast<int>((mk[t] >> lane) & 1ull);
+    a.hist[gofs + lane] = c;
+  }
+}
+
+// bf16 router: one workgroup per MT groups of 16 tokens over all of d (or over one K slice,
+// SPLIT). The chunks of 64 along d are dealt round-robin to the 4 waves; each wave issues the
+// loads of NB chunks before their MFMAs and accumulates MT x NT tiles of
+// v_mfma_f32_16x16x32_bf16 (x rows as A, W_g rows as B, both K-contiguous). The four wave
+// partials are added in LDS in wave order, the bias is added, and wave w runs the epilogue of
+// group w. MT = 4 cuts the W_g traffic per token by four when E is large.
+template <int NT, int NB, int MT, bool SPLIT>
+__global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a, float* __restrict__ zpart) {
+  constexpr int TB = kGroupTokens * MT;
   constexpr int LDR = 16 * NT + 1, LDE = kMaxE + 1;
-  __shared__ float red[4][16 * LDR];
-  __shared__ float rows[kGroupTokens * LDE];
+  __shared__ float red[4][TB * LDR];
+  __shared__ float rows[TB * LDE];
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int t0 = blockIdx.x * kGroupTokens;
-  const int nt_tok = min(kGroupTokens, a.T - t0);
+  const int t0 = blockIdx.x * TB;
+  const int nt_tok = min(TB, a.T - t0);
   const int d = a.d, E = a.E;
-  const int nchunk = d / 64;
-  const u16* __restrict__ x = static_cast<const u16*>(a.x);
-  const u16* __restrict__ Wg = static_cast<const u16*>(a.Wg);
+  // K slice blockIdx.y of gridDim.y: chunks [cb, ce) of 64
+  const int nchunk_all = d / 64, ks = blockIdx.y, KS = gridDim.y;
+  const int cb = ks * nchunk_all / KS, ce = (ks + 1) * nchunk_all / KS;
+  const int nchunk = ce - cb;
+  const u16* __restrict__ x = static_cast<const u16*>(a.x) + static_cast<size_t>(cb) * 64;
+  const u16* __restrict__ Wg = static_cast<const u16*>(a.Wg) + static_cast<size_t>(cb) * 64;
   const int r16 = lane & 15, g = lane >> 4;
   // rows past the last token re-read the last token; they only feed rows that are not kept
-  const u16* ap = x + static_cast<size_t>(t0 + min(r16, nt_tok - 1)) * d + 16 * g;
+  const u16* ap[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) ap[m] = x + static_cast<size_t>(t0 + min(m * 16 + r16, nt_tok - 1)) * d + 16 * g;
   const u16* bp[NT];
   bool bvalid[NT];
 #pragma unroll
@@ -242,19 +283,24 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
     bvalid[n] = e < E;
     bp[n] = Wg + static_cast<size_t>(bvalid[n] ? e : 0) * d + 16 * g;
   }
-  floatx4 acc[NT];
+  floatx4 acc[MT][NT];
 #pragma unroll
-  for (int n = 0; n < NT; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int n = 0; n < NT; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
   // chunk c covers k in [64c, 64c + 64): lane group g takes k 64c + 16g + [0, 16) as two
   // 8-element pieces, and MFMA step h uses piece h of both operands (same k order on A and B)
   for (int c0 = wave; c0 < nchunk; c0 += 4 * NB) {
-    bf16x8 av[NB][2], bv[NB][NT][2];
+    bf16x8 av[NB][MT][2], bv[NB][NT][2];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       const int kc = (c0 + 4 * i) * 64;
       if (c0 + 4 * i < nchunk) {
-        av[i][0] = *reinterpret_cast<const bf16x8*>(ap + kc);
-        av[i][1] = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          av[i][m][0] = *reinterpret_cast<const bf16x8*>(ap[m] + kc);
+          av[i][m][1] = *reinterpret_cast<const bf16x8*>(ap[m] + kc + 8);
+        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
           bv[i][n][0] = bvalid[n] ? *reinterpret_cast<const bf16x8*>(bp[n] + kc) : bf16x8{};
@@ -268,41 +314,81 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int n = 0; n < NT; ++n)
-            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][h], bv[i][n][h], acc[n], 0, 0, 0);
+          for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+              acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i][m][h], bv[i][n][h], acc[m][n], 0, 0, 0);
       }
     }
   }
   // C layout of the 16x16 tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][(4 * g + i) * LDR + n * 16 + r16] = acc[n][i];
+    for (int n = 0; n < NT; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][(m * 16 + 4 * g + i) * LDR + n * 16 + r16] = acc[m][n][i];
   __syncthreads();
-  for (int o = threadIdx.x; o < kGroupTokens * E; o += 256) {
+  if (SPLIT) {   // slice partial sums to zpart[ks][t][e]; router_finish_kernel does the rest
+    for (int o = threadIdx.x; o < nt_tok * E; o += 256) {
+      const int row = o / E, col = o - row * E;
+      const int l = row * LDR + col;
+      zpart[(static_cast<size_t>(ks) * a.T + t0 + row) * E + col] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+    }
+    return;
+  }
+  for (int o = threadIdx.x; o < TB * E; o += 256) {
     const int row = o / E, col = o - row * E;
     const int l = row * LDR + col;
     rows[row * LDE + col] =
         (((red[0][l] + red[1][l]) + red[2][l]) + red[3][l]) + (a.bg != nullptr ? a.bg[col] : 0.0f);
   }
   __syncthreads();
-  if (threadIdx.x >= kWave) return;   // the remaining barriers count wave 0 only
-  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.gumbel, a.key0, a.key1, a.logits,
-                                     a.scores, a.idx, a.w);
-  __syncthreads();
-  // group partials: column sums of p over the 16 rows (ascending), and the histogram, whose bits
-  // come from lane 4 t of each token (the popcount of the whole ballot)
-  const size_t gofs = static_cast<size_t>(blockIdx.x) * E;
-  if (lane < E) {
-    float ps = 0.0f;
+  // wave w finishes group w; waves without a group leave (the remaining barriers count the rest)
+  const int nt_w = min(kGroupTokens, nt_tok - wave * kGroupTokens);
+  if (wave >= MT || nt_w <= 0) return;
+  group_finish(a, rows + wave * kGroupTokens * LDE, LDE, t0 + wave * kGroupTokens, nt_w, blockIdx.x * MT + wave);
+}
+
+// Sums the KS slice partials of one 16-token group in slice order (all 256 threads, every load
+// in flight at once), adds b_g, and runs the group epilogue on wave 0.
+constexpr int kMaxSlices = 16;
+__global__ __launch_bounds__(256) void router_finish_kernel(RouterArgs a, int KS, const float* __restrict__ zpart) {
+  constexpr int LDE = kMaxE + 1;
+  constexpr int PER = kGroupTokens * kMaxE / 256;   // <= 4 elements per thread
+  __shared__ float rows[kGroupTokens * LDE];
+  const int t0 = blockIdx.x * kGroupTokens;
+  const int nt_tok = min(kGroupTokens, a.T - t0);
+  const int E = a.E, n = nt_tok * E;
+  const size_t base = static_cast<size_t>(t0) * E, slice = static_cast<size_t>(a.T) * E;
+  // every slice's loads in flight at once (KS <= kMaxSlices), then added in slice order
+  float v[kMaxSlices][PER];
 #pragma unroll
-    for (int r = 0; r < kGroupTokens; ++r) ps += rows[r * LDE + lane];
-    a.probsum_part[gofs + lane] = ps;
+  for (int ks = 0; ks < kMaxSlices; ++ks)
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = threadIdx.x + 256 * j;
+      v[ks][j] = (ks < KS && i < n) ? zpart[ks * slice + base + i] : 0.0f;
+    }
+  float z[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    z[j] = v[0][j];
+#pragma unroll
+    for (int ks = 1; ks < kMaxSlices; ++ks)
+      if (ks < KS) z[j] += v[ks][j];
   }
-  for (int e = 0; e < E; ++e) {
-    const uint64_t b = __ballot(static_cast<int>((sel >> e) & 1ull));
-    if (lane == 0) a.hist[gofs + e] = __popcll(b);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = threadIdx.x + 256 * j;
+    if (i < n) {
+      const int e = i % E;
+      rows[(i / E) * LDE + e] = z[j] + (a.bg != nullptr ? a.bg[e] : 0.0f);
+    }
   }
+  __syncthreads();
+  if (threadIdx.x >= kWave) return;   // the remaining barriers count wave 0 only
+  group_finish(a, rows, LDE, t0, nt_tok, blockIdx.x);
 }
 
 // float32 storage: plain FMA dot products, one lane per token, 64 tokens per workgroup
@@ -357,27 +443,52 @@ __global__ __launch_bounds__(64) void histogram_kernel(const int32_t* __restrict
 
 }  // namespace
 
-template <int NT>
-static void launch_router_bf16(const RouterArgs& a, hipStream_t stream) {
-  // keep about 8 chunks' worth of operand registers per lane: 2 (x) + 2 NT (W_g) per chunk
-  constexpr int NB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
-  const dim3 grid((a.T + kGroupTokens - 1) / kGroupTokens), block(256);
-  hipLaunchKernelGGL((router_bf16_kernel<NT, NB>), grid, block, 0, stream, a);
+int router_slices(int T, int d, int E) {
+  (void)E;
+  const int ng = (T + kGroupTokens - 1) / kGroupTokens;
+  if (ng >= 256) return 1;                   // enough groups to fill the chip: one fused kernel
+  int ks = (512 + ng - 1) / ng;              // aim at >= 512 workgroups
+  const int cap = d / 64 / 4;                // >= 4 chunks (one per wave) per slice
+  ks = ks < cap ? ks : cap;
+  return ks < 1 ? 1 : (ks > kMaxSlices ? kMaxSlices : ks);
 }
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t stream) {
+template <int NT>
+static hipError_t launch_router_bf16(const RouterArgs& a, float* zpart, hipStream_t stream) {
+  // keep about 8 chunks' worth of operand registers per lane: 2 (x) + 2 NT (W_g) per chunk
+  constexpr int NB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
+  const int ng = (a.T + kGroupTokens - 1) / kGroupTokens;
+  const int KS = router_slices(a.T, a.d, a.E);
+  if (KS == 1) {
+    if constexpr (NT >= 3) {
+      if (ng >= 4 * 256) {                   // large E and enough tokens: 64 tokens per workgroup
+        hipLaunchKernelGGL((router_bf16_kernel<NT, 2, 4, false>), dim3((ng + 3) / 4), dim3(256), 0, stream, a,
+                           nullptr);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((router_bf16_kernel<NT, NB, 1, false>), dim3(ng), dim3(256), 0, stream, a, nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((router_bf16_kernel<NT, NB, 1, true>), dim3(ng, KS), dim3(256), 0, stream, a, zpart);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(router_finish_kernel, dim3(ng), dim3(256), 0, stream, a, KS, zpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const RouterArgs& a, float* zpart, hipStream_t stream) {
   if (!a.bf16) {
     const dim3 grid((a.T + kBlockTokens - 1) / kBlockTokens), block(kWave);
     hipLaunchKernelGGL(router_f32_kernel, grid, block, 0, stream, a);
     return hipGetLastError();
   }
   switch ((a.E + 15) / 16) {
-    case 1: launch_router_bf16<1>(a, stream); break;
-    case 2: launch_router_bf16<2>(a, stream); break;
-    case 3: launch_router_bf16<3>(a, stream); break;
-    default: launch_router_bf16<4>(a, stream); break;
+    case 1: return launch_router_bf16<1>(a, zpart, stream);
+    case 2: return launch_router_bf16<2>(a, zpart, stream);
+    case 3: return launch_router_bf16<3>(a, zpart, stream);
+    default: return launch_router_bf16<4>(a, zpart, stream);
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_histogram(const int32_t* idx, int T, int E, int k, int32_t* hist, hipStream_t stream) {

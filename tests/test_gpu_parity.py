@@ -36,6 +36,14 @@ SMALL = {
     # float32 with Gumbel noise and a temperature
     "f32_gumbel": (MoEShape("f32_gumbel", T=300, d=96, E=6, k=2, d_ffn=200, capacity_factor=0.9, temperature=0.5,
                             gumbel=True, dtype="f32", seed=7), 0.1),
+    # few tokens over a wide d: the router cuts d into K slices (4 here) and adds them in a
+    # second kernel; E = 24 spans two 16-expert MFMA tiles; Gumbel noise at tau = 0.8
+    "router_slices": (MoEShape("router_slices", T=300, d=1024, E=24, k=3, d_ffn=128, capacity_factor=1.0,
+                               temperature=0.8, gumbel=True, seed=3, wg_std=None), 0.2),
+    # E > 32 with more than 1024 token groups: the router takes 64 tokens per workgroup; the last
+    # workgroup holds one 16-token group
+    "router_wide_tiles": (MoEShape("router_wide_tiles", T=16400, d=128, E=40, k=2, d_ffn=64, capacity_factor=1.0,
+                                   wg_std=None), 0.1),
     # tokens spanning many 16-token routing groups and 64-token permutation waves, E not a multiple of 16
     "many_blocks": (MoEShape("many_blocks", T=3000, d=128, E=37, k=4, d_ffn=128, capacity_factor=1.1,
                              wg_std=None), 0.0),
