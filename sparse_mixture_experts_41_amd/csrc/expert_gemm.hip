@@ -213,43 +213,59 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
 
-  // Epilogue straight from the accumulators. The MFMAs take the B fragment as their first
-  // operand, so block (i, j) holds the transposed 32x32 result: lane (l32, hi) has tile row
-  // wm*128 + 32 i + l32 at columns wn*128 + 32 j + 8 q + 4 hi + (0..3), q = 0..3, i.e. four
-  // consecutive outputs of one row, stored as 8 bytes of bf16 (GeLU) or 16 bytes of float.
-  // N is a multiple of 64, so each 32-column block lies wholly inside or outside [0, N).
-  // Only the NI row blocks the wave multiplied can hold segment rows.
+  // Epilogue. The MFMAs take the B fragment as their first operand, so block (i, j) holds the
+  // transposed 32x32 result: lane (l32, hi) has tile row wm*128 + 32 i + l32 at columns
+  // wn*128 + 32 j + 8 q + 4 hi + (0..3), q = 0..3, four consecutive outputs of one row. Bias
+  // and GeLU are applied in registers; each 32x128 row block then goes through the wave's own
+  // LDS region (8-byte bf16 or 16-byte float pieces) and back out as whole rows: 16 lanes
+  // (bf16) or 32 lanes (float) store each row's 256 or 512 contiguous bytes, so every store
+  // covers whole cache lines. N is a multiple of 64, so each 16-byte piece lies wholly inside
+  // or outside [0, N). Only the NI row blocks the wave multiplied can hold segment rows.
   auto epilogue = [&](auto ni_const, auto bias_const) {
     constexpr int NI = decltype(ni_const)::value;
     constexpr bool BIAS = decltype(bias_const)::value;
-    float* fout = static_cast<float*>(kpart == 0 ? g.out : g.out2);
+    constexpr int OB = EPI == kEpiGelu ? 2 : 4;           // output bytes per element
+    constexpr int PITCH = 128 * OB + 16;                   // bytes per staged row (padded)
+    constexpr int CPRW = 128 * OB / 16;                    // 16-byte pieces per row
+    constexpr int RPW = 64 / CPRW;                         // rows per wave store
+    static_assert(4 * 32 * PITCH <= NS * STAGE, "epilogue staging fits the operand ring");
+    char* st = smem + wave * 32 * PITCH;
+    char* outb = static_cast<char*>(EPI == kEpiGelu ? g.out : (kpart == 0 ? g.out : g.out2));
+    __syncthreads();                                       // every wave is done with the ring
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int r = m0 + wm * 128 + i * 32 + l32;
-      if (r >= m_e) continue;
-      const size_t rowoff = static_cast<size_t>(row0 + r) * N;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int cj = n0 + wn * 128 + j * 32;
-        if (cj >= N) continue;
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int c = cj + 8 * q + 4 * hi;
+          const int cl = j * 32 + 8 * q + 4 * hi;            // column within the wave tile
           float o[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)   // one addition either way: GeLU then needs no canonicalisation
-            o[u] = acc[i][j][4 * q + u] + (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + c + u, true) : 0.0f);
+            o[u] = acc[i][j][4 * q + u] +
+                   (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + wn * 128 + cl + u, N - 1), true)
+                         : 0.0f);
+          char* dst = st + l32 * PITCH + cl * OB;
           if (EPI == kEpiGelu) {
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = static_cast<__bf16>(gelu_bf16_path(o[u]));
-            *reinterpret_cast<bf16x4*>(static_cast<u16*>(g.out) + rowoff + c) = pk;
+            *reinterpret_cast<bf16x4*>(dst) = pk;
           } else {
-            *reinterpret_cast<floatx4*>(fout + rowoff + c) = floatx4{o[0], o[1], o[2], o[3]};
+            *reinterpret_cast<floatx4*>(dst) = floatx4{o[0], o[1], o[2], o[3]};
           }
         }
-        __builtin_amdgcn_sched_barrier(0);   // one 32x32 block at a time: bounded register use
+      // the wave reads back only what it wrote itself: LDS keeps one wave's accesses in order
+#pragma unroll
+      for (int it = 0; it < 32 / RPW; ++it) {
+        const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
+        const int r = m0 + wm * 128 + i * 32 + rr;
+        const int c = n0 + wn * 128 + pc * (16 / OB);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * PITCH + pc * 16);
+        if (r < m_e && c < N)
+          *reinterpret_cast<u32x4*>(outb + (static_cast<size_t>(row0 + r) * N + c) * OB) = v;
       }
+      __builtin_amdgcn_sched_barrier(0);   // one row block at a time: bounded register use
     }
   };
   const bool add_bias = kpart == 0 && g.bias != nullptr;
