@@ -489,7 +489,8 @@ bool ffn_gathers(const FfnArgs& a) {
 int ffn_splits(const FfnArgs& a) {
   if (!a.bf16 || a.C <= 16) return 1;
   const int tiles2 = tile_grid(a.R, a.E, a.C, 256, a.d, 256);
-  return (tiles2 < 4 * 256 && a.d_ffn % 64 == 0 && a.d_ffn >= 1024) ? 2 : 1;
+  // weight-streaming shapes (every expert within two row tiles) gain nothing from splitting
+  return (a.C > 512 && tiles2 < 4 * 256 && a.d_ffn % 64 == 0 && a.d_ffn >= 1024) ? 2 : 1;
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {

@@ -78,7 +78,8 @@ struct FfnArgs {
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
 // copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
 bool ffn_gathers(const FfnArgs& a);
-// Number of K parts GEMM2 is split into (1 or 2): 2 when its tiles would fill fewer than four
+// Number of K parts GEMM2 is split into (1 or 2): 2 when the capacity exceeds two 256-row tiles
+// (compute-bound experts) and its tiles would fill fewer than four
 // rounds of the 256 CUs. With 2, y_perm + y_perm2 (summed in float32) is the GEMM2 result.
 int ffn_splits(const FfnArgs& a);
 // GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
