@@ -13,9 +13,8 @@ Philox-4x32-10 called as a library.
 from . import philox
 from .moe_layer import (balance_stats, brute_dense, capacity, combine, dispatch, expert,
                         expert_ffn, forward, forward_rows, gelu, logits, renormalise, route,
-                        route_from_scores,
-                        scores, softmax, topk)
+                        route_from_scores, scores, shared_expert, silu, softmax, temperature_at, topk)
 
 __all__ = ["philox", "capacity", "logits", "scores", "softmax", "topk", "renormalise", "route", "route_from_scores",
-           "dispatch", "expert", "expert_ffn", "gelu", "combine", "balance_stats", "forward",
-           "forward_rows", "brute_dense"]
+           "dispatch", "expert", "expert_ffn", "gelu", "silu", "combine", "balance_stats", "forward",
+           "forward_rows", "brute_dense", "shared_expert", "temperature_at"]

@@ -16,6 +16,13 @@ Sources (pages cited by title or address and section):
        3.1 (dense loop: every expert on every token, masked by routing).
   [L]  "Mixture of Experts (MoE) 原理与工程落地全指南" (lpnh.cn), section 2.2 (Gumbel noise
        added to the logits, divided by a temperature, then softmax).
+  [A]  "为什么92%的AI团队误用MoE？…" (aberweb.com), sections 2.3 (a shared expert that every
+       token uses, plus the routed experts), 3.2 (experts Linear -> SiLU -> Linear; the
+       temperature schedule tau = max(0.5, 1.0 - 0.0001 * step)).
+  [M]  "MoE架构揭秘：参数规模≠计算量…" (mhpn.cn): the same schedule with rate 0.001.
+Forward variants (the plain layer is the default of each): SiLU experts ([A] 3.2); Gaussian
+router noise noise_std * N(0, 1) added to the logits ([G] 3.3; generator in philox.py); a
+shared expert whose output is added to every token's routed sum ([A] 2.3).
 
 Readings taken where the pages leave a step open:
   * top-k selects on the float32 scores s (logits, plus Gumbel noise, over tau); ties go to
@@ -36,7 +43,7 @@ import math
 from fractions import Fraction
 
 import numpy as np
-from scipy.special import erf
+from scipy.special import erf, expit
 
 from . import philox
 
@@ -108,16 +115,22 @@ def route_from_scores(s: np.ndarray, k: int) -> dict:
     return {"s": s, "p": p, "idx": idx, "w": w}
 
 
-def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None):
+def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None, noise_std=0.0):
     """Router step. Returns z (float64 logits), s (float32 scores), p, idx, w.
 
-    With ``given_scores`` (float32 [T,E]) the routing is re-derived from those scores
-    instead of the oracle's own logits (z is still the oracle's float64 logit)."""
+    Noise: Gumbel when ``gumbel``, else Gaussian noise of std ``noise_std`` when it is > 0,
+    else none. With ``given_scores`` (float32 [T,E]) the routing is re-derived from those
+    scores instead of the oracle's own logits (z is still the oracle's float64 logit)."""
     z = logits(x, Wg, bg)
     if given_scores is not None:
         s = np.asarray(given_scores, np.float32)
     else:
-        g32 = philox.gumbel_f32(seed, z.shape[0], z.shape[1]) if gumbel else None
+        if gumbel:
+            g32 = philox.gumbel_f32(seed, z.shape[0], z.shape[1])
+        elif noise_std > 0.0:
+            g32 = philox.gaussian_f32(seed, z.shape[0], z.shape[1], noise_std)
+        else:
+            g32 = None
         s = scores(z.astype(np.float32), tau, g32)
     out = route_from_scores(s, k)
     out["z"] = z
@@ -154,19 +167,27 @@ def gelu(v: np.ndarray) -> np.ndarray:
     return 0.5 * v * (1.0 + erf(v * SQRT1_2))
 
 
-def expert(xr, W1e, b1e, W2e, b2e) -> np.ndarray:
-    """One expert on rows xr: Linear(d -> d_ffn) -> GeLU -> Linear(d_ffn -> d)."""
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU(v) = v * sigmoid(v) ([A] 3.2's nn.SiLU); the sigmoid is scipy's expit."""
+    return v * expit(v)
+
+
+ACTIVATIONS = {"gelu": gelu, "silu": silu}
+
+
+def expert(xr, W1e, b1e, W2e, b2e, act: str = "gelu") -> np.ndarray:
+    """One expert on rows xr: Linear(d -> d_ffn) -> activation -> Linear(d_ffn -> d)."""
     h = np.asarray(xr, np.float64) @ np.asarray(W1e, np.float64).T
     if b1e is not None:
         h = h + np.asarray(b1e, np.float64)
-    h = gelu(h)
+    h = ACTIVATIONS[act](h)
     y = h @ np.asarray(W2e, np.float64).T
     if b2e is not None:
         y = y + np.asarray(b2e, np.float64)
     return y
 
 
-def expert_ffn(x_perm, kept, offsets, W1, b1, W2, b2) -> np.ndarray:
+def expert_ffn(x_perm, kept, offsets, W1, b1, W2, b2, act: str = "gelu") -> np.ndarray:
     """Each expert e runs on its own contiguous segment of the expert-sorted rows."""
     y_perm = np.zeros((x_perm.shape[0], W2.shape[1]), dtype=np.float64)
     for e in range(len(kept)):
@@ -175,7 +196,7 @@ def expert_ffn(x_perm, kept, offsets, W1, b1, W2, b2) -> np.ndarray:
             continue
         lo = int(offsets[e])
         y_perm[lo:lo + n] = expert(x_perm[lo:lo + n], W1[e], None if b1 is None else b1[e],
-                                   W2[e], None if b2 is None else b2[e])
+                                   W2[e], None if b2 is None else b2[e], act)
     return y_perm
 
 
@@ -200,17 +221,29 @@ def balance_stats(counts: np.ndarray, p: np.ndarray, k: int) -> dict:
 
 
 # ---------------------------------------------------------------- whole layer
+def shared_expert(x, shared, act: str = "gelu"):
+    """The shared expert ([A] 2.3) on every token; ``shared`` = (W1s, b1s, W2s, b2s) or None."""
+    if shared is None:
+        return None
+    W1s, b1s, W2s, b2s = shared
+    return expert(x, W1s, b1s, W2s, b2s, act)
+
+
 def forward(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=False,
-            seed=0, given_scores=None) -> dict:
-    """The layer: route -> dispatch -> gather -> experts -> combine, plus f, P, L."""
+            seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None) -> dict:
+    """The layer: route -> dispatch -> gather -> experts -> combine (+ shared expert), plus
+    f, P, L."""
     T, d = x.shape
     E = Wg.shape[0]
-    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
     C = capacity(T, E, k, capacity_factor)
     dsp = dispatch(r["idx"], E, C)
     x_perm = np.asarray(x, np.float64)[dsp["perm"]]
-    y_perm = expert_ffn(x_perm, dsp["kept"], dsp["offsets"], W1, b1, W2, b2)
+    y_perm = expert_ffn(x_perm, dsp["kept"], dsp["offsets"], W1, b1, W2, b2, act)
     y = combine(y_perm, dsp["dest"], r["w"])
+    ys = shared_expert(x, shared, act)
+    if ys is not None:
+        y = y + ys
     st = balance_stats(dsp["counts"], r["p"], k)
     out = dict(r)
     out.update(dsp)
@@ -220,7 +253,7 @@ def forward(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=Fa
 
 
 def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0,
-                 gumbel=False, seed=0, given_scores=None) -> dict:
+                 gumbel=False, seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None) -> dict:
     """The layer's output for selected tokens only, at any size.
 
     Routing and dispatch are done for all tokens (they decide which slots survive); each
@@ -228,7 +261,7 @@ def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0
     selected token sums its slots in j order."""
     T, d = x.shape
     E = Wg.shape[0]
-    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
     C = capacity(T, E, k, capacity_factor)
     dsp = dispatch(r["idx"], E, C)
     rows = np.asarray(rows, np.int64)
@@ -239,12 +272,15 @@ def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0
         if not sel:
             continue
         xe = np.asarray(x[[rows[i] for i, _ in sel]], np.float64)
-        ye = expert(xe, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+        ye = expert(xe, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e], act)
         for n, (i, j) in enumerate(sel):
             contrib[i, j] = r["w"][rows[i], j] * ye[n]
     y = np.zeros((len(rows), W2.shape[1]), dtype=np.float64)
     for j in range(k):
         y += contrib[:, j]
+    ys = shared_expert(np.asarray(x[rows], np.float64), shared, act)
+    if ys is not None:
+        y = y + ys
     st = balance_stats(dsp["counts"], r["p"], k)
     out = dict(r)
     out.update(dsp)
@@ -255,14 +291,14 @@ def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0
 
 # ---------------------------------------------------------------- brute force (tiny sizes)
 def brute_dense(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=False,
-                seed=0, given_scores=None) -> dict:
+                seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None) -> dict:
     """Every expert on every token, masked by routing and capacity ([D] 3.1's dense loop).
 
     Capacity is applied from its definition: slot (t, j) with expert e survives iff fewer
     than C earlier tokens t' < t chose e. O(T^2 k^2); tiny inputs only."""
     T, d = x.shape
     E = Wg.shape[0]
-    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores)
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
     C = capacity(T, E, k, capacity_factor)
     idx, w = r["idx"], r["w"]
     keep = np.zeros((T, k), dtype=bool)
@@ -273,9 +309,18 @@ def brute_dense(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbe
             keep[t, j] = earlier < C
     y = np.zeros((T, W2.shape[1]), dtype=np.float64)
     for e in range(E):
-        ye = expert(x, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e])
+        ye = expert(x, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e], act)
         mask = np.zeros(T, dtype=np.float64)
         for j in range(k):
             mask += np.where((idx[:, j] == e) & keep[:, j], w[:, j], 0.0)
         y += mask[:, None] * ye
+    if shared is not None:                   # the shared expert, also on every token
+        W1s, b1s, W2s, b2s = shared
+        y += expert(x, W1s, b1s, W2s, b2s, act)
     return {"y": y, "keep": keep, "idx": idx, "w": w, "C": C}
+
+
+# ---------------------------------------------------------------- temperature schedule
+def temperature_at(step: int, tau0: float = 1.0, tau_min: float = 0.5, rate: float = 1e-4) -> float:
+    """tau_t = max(tau_min, tau0 - rate * t) ([A] 3.2: 0.5, 1.0, 1e-4; [M]: rate 1e-3)."""
+    return max(float(tau_min), float(tau0) - float(rate) * float(step))

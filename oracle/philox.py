@@ -19,6 +19,13 @@ taken here, for a token t, an expert e and a 64-bit seed:
   u = (w0 + 1/2) * 2^-32 in float64 (strictly inside (0, 1), so no clamp is needed),
   g = -log(-log(u)) in float64, rounded once to float32.
 
+Gaussian noise (the training-time router noise of the kwkr.cn page on sparse activation,
+section 3.3: a standard normal draw per (token, expert) times noise_std, added to the
+logits). Reading taken here: from the same block (counter (t, e, 0, 0)), u1 and u2 are words 0
+and 1 mapped as above, and n = sqrt(-2 ln u1) cos(2 pi u2) (the Box-Muller transform, G. E. P.
+Box and M. E. Muller, "A Note on the Generation of Random Normal Deviates", Ann. Math. Statist.
+29, 1958), in float64; the noise noise_std * n is rounded once to float32.
+
 Two implementations follow: one on Python integers, one vectorised in numpy. They are
 written separately and checked against each other (and against rocRAND's Philox, called as
 a library) by the tests.
@@ -99,3 +106,22 @@ def gumbel_scalar(seed: int, t: int, e: int) -> np.float32:
     w0 = philox4x32_10((t, e, 0, 0), seed_key(seed))[0]
     u = (w0 + 0.5) * 2.0 ** -32
     return np.float32(-math.log(-math.log(u)))
+
+
+def gaussian_f32(seed: int, T: int, E: int, noise_std: float, t0: int = 0) -> np.ndarray:
+    """float32 Gaussian noise noise_std * n[t, e] for tokens t0 .. t0+T-1, experts 0 .. E-1."""
+    k0, k1 = seed_key(seed)
+    t = np.arange(t0, t0 + T, dtype=np.uint64)[:, None]
+    e = np.arange(E, dtype=np.uint64)[None, :]
+    w0, w1, _, _ = philox4x32_10_np(t, e, 0, 0, k0, k1)
+    u1, u2 = uniform_open(w0), uniform_open(w1)
+    n = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
+    return (float(noise_std) * n).astype(np.float32)
+
+
+def gaussian_scalar(seed: int, t: int, e: int, noise_std: float) -> np.float32:
+    """The same noise through the Python-integer Philox and the math module."""
+    import math
+    w0, w1, _, _ = philox4x32_10((t, e, 0, 0), seed_key(seed))
+    u1, u2 = (w0 + 0.5) * 2.0 ** -32, (w1 + 0.5) * 2.0 ** -32
+    return np.float32(float(noise_std) * math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2))
