@@ -40,6 +40,12 @@ def _args():
     ap.add_argument("--traffic", default=None,
                     help="JSON with rocprofv3-measured HBM bytes per launch "
                          "(default: profiles/traffic_<workload>.json)")
+    ap.add_argument("--activation", choices=("gelu", "silu"), default="gelu",
+                    help="expert activation (forward variant)")
+    ap.add_argument("--noise-std", type=float, default=0.0,
+                    help="Gaussian router noise std (forward variant; needs a workload without Gumbel noise)")
+    ap.add_argument("--shared-d-ffn", type=int, default=0,
+                    help="hidden width of a shared expert every token uses (forward variant; 0 = none)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -70,8 +76,9 @@ def stored_traffic(path: str, kernel: str):
     return rec.get("bytes_per_launch", {}).get(kernel)
 
 
-def cpu_baseline(shape, arrays, n_tokens: int) -> dict:
-    """The oracle as it stands, timed on the host cores on the first n_tokens tokens."""
+def cpu_baseline(shape, arrays, n_tokens: int, variant: dict | None = None) -> dict:
+    """The oracle as it stands, timed on the host cores on the first n_tokens tokens.
+    ``variant``: activation, noise_std and shared-expert arrays of a forward variant."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -91,8 +98,13 @@ def cpu_baseline(shape, arrays, n_tokens: int) -> dict:
             val(arrays["b2"]))
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
+        vkw = {}
+        if variant:
+            shared = variant.get("shared")
+            vkw = dict(act=variant["activation"], noise_std=variant["noise_std"],
+                       shared=None if shared is None else tuple(val(shared[n]) for n in ("W1s", "b1s", "W2s", "b2s")))
         out = oracle.forward(*args, k=shape.k, capacity_factor=shape.capacity_factor, tau=shape.temperature,
-                             gumbel=shape.gumbel, seed=shape.seed)
+                             gumbel=shape.gumbel, seed=shape.seed, **vkw)
         t1 = time.perf_counter()
         blas = [f"{i.get('internal_api')} {i.get('version')}" for i in threadpool_info()]
     assert np.isfinite(out["y"]).all()
@@ -114,7 +126,7 @@ def main() -> int:
     import torch
 
     from sparse_mixture_experts_41_amd import ops
-    from workloads import CONFIGS, make_inputs
+    from workloads import CONFIGS, make_inputs, make_shared_expert
 
     torch.cuda.set_device(0)
     if args.calibrate_copy_mib > 0:
@@ -140,7 +152,18 @@ def main() -> int:
     tensors = [dev(arrays[n]) for n in ("x", "Wg", "bg", "W1", "b1", "W2", "b2")]
     cfg = ops.make_config(shape.T, shape.d, shape.E, shape.k, shape.d_ffn, shape.capacity_factor,
                           shape.temperature, shape.gumbel, shape.seed, shape.dtype)
-    plan = ops.ForwardPlan(cfg, *tensors, keep_routing=False)
+    with_variant = args.activation != "gelu" or args.noise_std > 0.0 or args.shared_d_ffn > 0
+    variant = None
+    variant_host = None
+    if with_variant:
+        shared = None
+        variant_host = {"activation": args.activation, "noise_std": args.noise_std, "shared": None}
+        if args.shared_d_ffn > 0:
+            sh = make_shared_expert(shape, args.shared_d_ffn)
+            shared = tuple(dev(sh[n]) for n in ("W1s", "b1s", "W2s", "b2s"))
+            variant_host["shared"] = sh
+        variant = ops.make_variant(cfg, args.activation, args.noise_std, shared)
+    plan = ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant)
     for _ in range(args.warmup):
         plan.run()
     torch.cuda.synchronize()
@@ -163,11 +186,14 @@ def main() -> int:
     T, d, E, k, dff = shape.T, shape.d, shape.E, shape.k, shape.d_ffn
     sx = 2 if shape.dtype == "bf16" else 4
     gemm_flops = 2.0 * d * dff * kept                       # per GEMM launch, kept rows only
+    shared_flops = 4.0 * d * args.shared_d_ffn * T          # both shared-expert GEMMs, every token
     g1, g2 = stage["expert_gemm1_gelu"], stage["expert_gemm2"]
+    # the shared expert's two GEMMs run inside the second stage
+    stage_flops = {"expert_gemm1_gelu": gemm_flops, "expert_gemm2": gemm_flops + shared_flops}
     dom_name, dom_ms = ("expert_gemm1_gelu", g1) if g1 >= g2 else ("expert_gemm2", g2)
-    achieved = gemm_flops / (dom_ms * 1e-3) / 1e12
+    achieved = stage_flops[dom_name] / (dom_ms * 1e-3) / 1e12
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{shape.name}.json")
-    traffic = stored_traffic(traffic_path, dom_name)
+    traffic = None if with_variant else stored_traffic(traffic_path, dom_name)
     ng = (T + 15) // 16
     router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + ng * E * 8
     # GEMM1 reads the token rows through the permutation (no gathered copy) on the bf16 MFMA
@@ -192,11 +218,13 @@ def main() -> int:
         "data": "synthetic (seeded; workloads.make_inputs)",
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "d_ffn": dff,
                    "capacity_factor": shape.capacity_factor, "temperature": shape.temperature,
-                   "gumbel": shape.gumbel, "parallelism": "none (one GPU)"},
+                   "gumbel": shape.gumbel, "parallelism": "none (one GPU)",
+                   **({"variant": {"activation": args.activation, "noise_std": args.noise_std,
+                                   "shared_d_ffn": args.shared_d_ffn}} if with_variant else {})},
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
-        "grouped_gemm": {"tflops": 2 * gemm_flops / ((g1 + g2) * 1e-3) / 1e12,
-                         "frac_of_peak": 2 * gemm_flops / ((g1 + g2) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "grouped_gemm": {"tflops": (2 * gemm_flops + shared_flops) / ((g1 + g2) * 1e-3) / 1e12,
+                         "frac_of_peak": (2 * gemm_flops + shared_flops) / ((g1 + g2) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                          "kept_rows": kept, "dropped_slots": int(k * T - kept)},
         "hbm_stages": {
             "router": {"GB/s": router_bytes / (stage["route"] * 1e-3) / 1e9, "bytes": router_bytes},
@@ -210,7 +238,7 @@ def main() -> int:
     }
     if args.cpu_sample_tokens != 0:
         n_cpu = T if args.cpu_sample_tokens < 0 else min(args.cpu_sample_tokens, T)
-        line["cpu_baseline"] = cpu_baseline(shape, arrays, n_cpu)
+        line["cpu_baseline"] = cpu_baseline(shape, arrays, n_cpu, variant_host)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -150,6 +150,51 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
                        const moe_forward_aux* aux, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Forward variants. A zeroed moe_variant is the plain layer above, and moe_forward_ex with
+ * variant = NULL is moe_forward. Stage calls (moe_route ... moe_combine) take no variant.
+ */
+typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SILU = 1 } moe_activation;
+
+typedef struct moe_variant {
+  int32_t activation;      /* moe_activation of every expert (routed and shared): GeLU, or
+                              SiLU(v) = v sigmoid(v) (aberweb.com page, section 3.2)         */
+  float noise_std;         /* 0: no Gaussian noise. > 0 (needs gumbel = 0): s = (z + g)/tau,
+                              g = noise_std * n with n standard normal per (token, expert)
+                              (kwkr.cn page, section 3.3): from the Philox block of the Gumbel
+                              noise (same key, counter (t, e, 0, 0)), u1 and u2 = (word 0 or
+                              word 1 + 1/2) 2^-32, n = sqrt(-2 ln u1) cos(2 pi u2) in float64,
+                              and g = noise_std * n rounded once to float32                 */
+  int64_t shared_d_ffn;    /* 0: none. Else the hidden width of one shared expert that every
+                              token uses (aberweb.com page, section 2.3):
+                              y[t] = FFN_s(x[t]) + sum_j w[t,j] FFN_e(x[t]); the float32 sum
+                              starts from FFN_s and adds the slots in j order. bf16 needs a
+                              multiple of 64.                                                 */
+  const void* W1s;         /* [shared_d_ffn, d] dtype (required when shared_d_ffn > 0)        */
+  const void* b1s;         /* [shared_d_ffn] dtype, nullable                                  */
+  const void* W2s;         /* [d, shared_d_ffn] dtype (required when shared_d_ffn > 0)        */
+  const void* b2s;         /* [d] dtype, nullable                                             */
+} moe_variant;
+
+/* Workspace bytes of moe_forward_ex for `cfg` and `variant` (nullable). Host only.
+ * MOE_EINVAL for an unknown activation, a negative or non-finite noise_std, noise_std > 0
+ * together with gumbel = 1; MOE_EUNSUPPORTED for a shared_d_ffn the dtype cannot take. */
+moe_status moe_workspace_size_ex(const moe_config* cfg, const moe_variant* variant, size_t* bytes);
+
+/* The layer with the variant's activation, router noise and shared expert; arguments as
+ * moe_forward. With a shared expert, stage 5 of aux.stage_events (expert GEMM2) also covers
+ * the shared expert's two GEMMs. */
+moe_status moe_forward_ex(const moe_config* cfg, const moe_variant* variant, const void* x,
+                          const void* Wg, const float* bg, const void* W1, const void* b1,
+                          const void* W2, const void* b2, void* y, float* f, float* P, float* L,
+                          int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws,
+                          size_t ws_bytes, moe_stream_t stream);
+
+/* Temperature schedule tau_t = max(tau_min, tau0 - rate * step) (aberweb.com page, section
+ * 3.2: tau0 = 1, tau_min = 0.5, rate = 1e-4; mhpn.cn page: rate 1e-3), computed in double and
+ * rounded once to float; the result goes to moe_config.temperature. Host only. */
+float moe_temperature_at(int64_t step, float tau0, float tau_min, float rate);
+
 /* Static text of a status code. */
 const char* moe_status_str(moe_status status);
 

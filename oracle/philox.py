@@ -24,7 +24,8 @@ section 3.3: a standard normal draw per (token, expert) times noise_std, added t
 logits). Reading taken here: from the same block (counter (t, e, 0, 0)), u1 and u2 are words 0
 and 1 mapped as above, and n = sqrt(-2 ln u1) cos(2 pi u2) (the Box-Muller transform, G. E. P.
 Box and M. E. Muller, "A Note on the Generation of Random Normal Deviates", Ann. Math. Statist.
-29, 1958), in float64; the noise noise_std * n is rounded once to float32.
+29, 1958), in float64; noise_std is a float32 parameter (its float32 value is used), and the
+noise noise_std * n is rounded once to float32.
 
 Two implementations follow: one on Python integers, one vectorised in numpy. They are
 written separately and checked against each other (and against rocRAND's Philox, called as
@@ -116,7 +117,7 @@ def gaussian_f32(seed: int, T: int, E: int, noise_std: float, t0: int = 0) -> np
     w0, w1, _, _ = philox4x32_10_np(t, e, 0, 0, k0, k1)
     u1, u2 = uniform_open(w0), uniform_open(w1)
     n = np.sqrt(-2.0 * np.log(u1)) * np.cos(2.0 * np.pi * u2)
-    return (float(noise_std) * n).astype(np.float32)
+    return (float(np.float32(noise_std)) * n).astype(np.float32)
 
 
 def gaussian_scalar(seed: int, t: int, e: int, noise_std: float) -> np.float32:
@@ -124,4 +125,5 @@ def gaussian_scalar(seed: int, t: int, e: int, noise_std: float) -> np.float32:
     import math
     w0, w1, _, _ = philox4x32_10((t, e, 0, 0), seed_key(seed))
     u1, u2 = (w0 + 0.5) * 2.0 ** -32, (w1 + 0.5) * 2.0 ** -32
-    return np.float32(float(noise_std) * math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2))
+    sd = float(np.float32(noise_std))
+    return np.float32(sd * math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2))

@@ -34,6 +34,16 @@ class MoeForwardAux(ctypes.Structure):
     ]
 
 
+MOE_ACT_GELU, MOE_ACT_SILU = 0, 1
+
+
+class MoeVariant(ctypes.Structure):
+    _fields_ = [
+        ("activation", ctypes.c_int32), ("noise_std", ctypes.c_float), ("shared_d_ffn", ctypes.c_int64),
+        ("W1s", ctypes.c_void_p), ("b1s", ctypes.c_void_p), ("W2s", ctypes.c_void_p), ("b2s", ctypes.c_void_p),
+    ]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"status {status}: {detail}")
@@ -43,6 +53,7 @@ class MoeError(RuntimeError):
 
 _P = ctypes.c_void_p
 _CFG = ctypes.POINTER(MoeConfig)
+_VAR = ctypes.POINTER(MoeVariant)
 _SIGS = {
     "moe_capacity": (ctypes.c_int64, [_CFG]),
     "moe_workspace_size": (ctypes.c_int, [_CFG, ctypes.POINTER(ctypes.c_size_t)]),
@@ -52,6 +63,10 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),
+    "moe_workspace_size_ex": (ctypes.c_int, [_CFG, _VAR, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_forward_ex": (ctypes.c_int, [_CFG, _VAR, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),
+    "moe_temperature_at": (ctypes.c_float, [ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -4,7 +4,8 @@
 // which the page's section 3.2 code computes as a weighted scatter-add of the expert outputs
 // back onto their tokens. Here each token gathers its own k rows instead, so no atomics are
 // needed and the sum order is fixed: float32 accumulation in j order, one final rounding.
-// Dropped slots (dest = -1) contribute exactly zero (the page's section 2.3 and 6.1).
+// Dropped slots (dest = -1) contribute exactly zero (the page's section 2.3 and 6.1). With a
+// shared expert (aberweb.com page, section 2.3) each token's sum starts from its output.
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -16,6 +17,7 @@ namespace {
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const float* __restrict__ y_perm2,
+                                                      const float* __restrict__ y_shared,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ w, int T, int d, int k, int R,
                                                       void* __restrict__ y) {
@@ -26,6 +28,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     const int t = static_cast<int>(it / groups);
     const int c = static_cast<int>(it - static_cast<long long>(t) * groups) * 8;
     floatx4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if (y_shared != nullptr) {
+      const floatx4* sh = reinterpret_cast<const floatx4*>(y_shared + static_cast<size_t>(t) * d + c);
+      acc0 = sh[0];
+      acc1 = sh[1];
+    }
     for (int j = 0; j < k; ++j) {
       const int r = dest[static_cast<size_t>(t) * k + j];
       if (r < 0 || r >= R) continue;   // dropped (or out-of-range) slot: contributes zero
@@ -64,18 +71,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* y_perm, const float* y_perm2, const int32_t* dest, const float* w, int T,
-                          int d, int k, int R, int bf16, void* y, hipStream_t stream) {
+hipError_t launch_combine(const float* y_perm, const float* y_perm2, const float* y_shared, const int32_t* dest,
+                          const float* w, int T, int d, int k, int R, int bf16, void* y, hipStream_t stream) {
   const long long items = static_cast<long long>(T) * (d / 8);
   long long blocks = (items + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (bf16)
     hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y_perm, y_perm2,
-                       dest, w, T, d, k, R, y);
+                       y_shared, dest, w, T, d, k, R, y);
   else
     hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y_perm, y_perm2,
-                       dest, w, T, d, k, R, y);
+                       y_shared, dest, w, T, d, k, R, y);
   return hipGetLastError();
 }
 

@@ -36,12 +36,20 @@ struct GemmArgs {
   void* out2;             // [R,N] float partial sums of the second K part (splits == 2)
   const int32_t* rows;    // [R] or null: A row of expert-sorted row r is rows[r] (fused gather)
   int a_rows;             // rows of A when `rows` is set (a_rows * K * 2 < 2^31)
+  int dense;              // 1: one expert (E = 1) over all R rows; kept and offsets are unused
 };
 
-enum { kEpiGelu = 0, kEpiLinear = 1 };
+enum { kEpiGelu = 0, kEpiLinear = 1, kEpiSilu = 2 };   // GEMM1 (activation, bf16 out) or GEMM2 (float out)
+
+// The activation of an expert's hidden layer, for results rounded to bf16.
+template <int EPI>
+__device__ __forceinline__ float activation_bf16(float v) {
+  return EPI == kEpiGelu ? gelu_bf16_path(v) : silu_bf16_path(v);
+}
 
 // Rows of expert e's segment; a segment that does not fit [0, R) or exceeds C counts as empty.
 __device__ __forceinline__ int segment_rows(const GemmArgs& g, int e) {
+  if (g.dense) return e == 0 ? g.R : 0;
   const int m = g.kept[e], o = g.offsets[e];
   return (m > 0 && m <= g.C && o >= 0 && o <= g.R - m) ? m : 0;
 }
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   int e, mt, nt;
   decode_tile(unit - kpart * n_tiles, g, BM, tiles_n, e, mt, nt);
   const int m_e = segment_rows(g, e);
-  const int row0 = g.offsets[e];
+  const int row0 = g.dense ? 0 : g.offsets[e];
   const int m0 = mt * BM, n0 = nt * BN;
   const int N = g.N, K = g.K;
   const int nk = K / BK / g.splits;          // K steps of this part
@@ -224,13 +232,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   auto epilogue = [&](auto ni_const, auto bias_const) {
     constexpr int NI = decltype(ni_const)::value;
     constexpr bool BIAS = decltype(bias_const)::value;
-    constexpr int OB = EPI == kEpiGelu ? 2 : 4;           // output bytes per element
+    constexpr int OB = EPI == kEpiLinear ? 4 : 2;         // output bytes per element
     constexpr int PITCH = 128 * OB + 16;                   // bytes per staged row (padded)
     constexpr int CPRW = 128 * OB / 16;                    // 16-byte pieces per row
     constexpr int RPW = 64 / CPRW;                         // rows per wave store
     static_assert(4 * 32 * PITCH <= NS * STAGE, "epilogue staging fits the operand ring");
     char* st = smem + wave * 32 * PITCH;
-    char* outb = static_cast<char*>(EPI == kEpiGelu ? g.out : (kpart == 0 ? g.out : g.out2));
+    char* outb = static_cast<char*>(EPI != kEpiLinear ? g.out : (kpart == 0 ? g.out : g.out2));
     __syncthreads();                                       // every wave is done with the ring
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -246,10 +254,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
                    (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + wn * 128 + cl + u, N - 1), true)
                          : 0.0f);
           char* dst = st + l32 * PITCH + cl * OB;
-          if (EPI == kEpiGelu) {
+          if (EPI != kEpiLinear) {
             bf16x4 pk;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) pk[u] = static_cast<__bf16>(gelu_bf16_path(o[u]));
+            for (int u = 0; u < 4; ++u) pk[u] = static_cast<__bf16>(activation_bf16<EPI>(o[u]));
             *reinterpret_cast<bf16x4*>(dst) = pk;
           } else {
             *reinterpret_cast<floatx4*>(dst) = floatx4{o[0], o[1], o[2], o[3]};
@@ -372,7 +380,7 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
   const int e = blockIdx.x / nblk_n, nb = blockIdx.x - e * nblk_n;
   const int m_e = segment_rows(g, e);
   if (m_e == 0) return;
-  const int row0 = g.offsets[e];
+  const int row0 = g.dense ? 0 : g.offsets[e];
   const int N = g.N, K = g.K;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
@@ -430,8 +438,8 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
       if (r < m_e) {
         const size_t o = static_cast<size_t>(row0 + r) * N + n;
         const float val = acc[t][i] + bias;
-        if (EPI == kEpiGelu)
-          static_cast<u16*>(g.out)[o] = f32_to_bf16(gelu_bf16_path(val));
+        if (EPI != kEpiLinear)
+          static_cast<u16*>(g.out)[o] = f32_to_bf16(activation_bf16<EPI>(val));
         else
           static_cast<float*>(g.out)[o] = val;
       }
@@ -451,7 +459,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
   int e, mt, nt;
   if (!decode_tile(blockIdx.x, g, FBM, tiles_n, e, mt, nt)) return;
   const int m_e = segment_rows(g, e);
-  const int row0 = g.offsets[e];
+  const int row0 = g.dense ? 0 : g.offsets[e];
   const int m0 = mt * 16, n0 = nt * 16;
   const int N = g.N, K = g.K;
   const float* __restrict__ A = static_cast<const float*>(g.A);
@@ -469,7 +477,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
   const int r = m0 + ty, c = n0 + tx;
   if (r < m_e && c < N) {
     const float val = acc + load_bias(g.bias, static_cast<size_t>(e) * N + c, false);
-    static_cast<float*>(g.out)[static_cast<size_t>(row0 + r) * N + c] = (EPI == kEpiGelu) ? gelu_erf(val) : val;
+    static_cast<float*>(g.out)[static_cast<size_t>(row0 + r) * N + c] =
+        EPI == kEpiGelu ? gelu_erf(val) : (EPI == kEpiSilu ? silu_exact(val) : val);
   }
 }
 
@@ -493,41 +502,55 @@ int ffn_splits(const FfnArgs& a) {
   return (a.C > 512 && tiles2 < 4 * 256 && a.d_ffn % 64 == 0 && a.d_ffn >= 1024) ? 2 : 1;
 }
 
-hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
-  GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr, nullptr, 0};
-  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2,
-              nullptr, 0};
+template <int ACT>
+static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, int C, int R, int E, int N1, int N2,
+                             hipStream_t stream, hipEvent_t ev_mid) {
   hipError_t err;
-  if (!a.bf16) {
-    const int grid1 = tile_grid(a.R, a.E, a.C, FBM, a.d_ffn, 16);
-    const int grid2 = tile_grid(a.R, a.E, a.C, FBM, a.d, 16);
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel<kEpiGelu>, dim3(grid1), dim3(256), 0, stream, g1);
+  if (!bf16) {
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<ACT>, dim3(tile_grid(R, E, C, FBM, N1, 16)), dim3(256), 0, stream, g1);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemm_f32_kernel<kEpiLinear>, dim3(grid2), dim3(256), 0, stream, g2);
-    return hipGetLastError();
-  }
-  if (a.C <= 16) {
-    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiGelu>, dim3(a.E * ((a.d_ffn + GV_COLS - 1) / GV_COLS)), dim3(256),
-                       0, stream, g1);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
-    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiLinear>, dim3(a.E * ((a.d + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<kEpiLinear>, dim3(tile_grid(R, E, C, FBM, N2, 16)), dim3(256), 0,
                        stream, g2);
     return hipGetLastError();
   }
-  if (a.rows != nullptr) {                   // GEMM1 reads the token rows of x directly
-    g1.A = a.x;
-    g1.rows = a.rows;
-    g1.a_rows = a.T;
+  if (C <= 16) {
+    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<ACT>, dim3(E * ((N1 + GV_COLS - 1) / GV_COLS)), dim3(256), 0, stream,
+                       g1);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
+    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<kEpiLinear>, dim3(E * ((N2 + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
+                       stream, g2);
+    return hipGetLastError();
   }
-  const int grid1 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d_ffn, 256));
-  const int grid2 = round_grid(tile_grid(a.R, a.E, a.C, 256, a.d, 256) * g2.splits);
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiGelu, 32, 4>), dim3(grid1), dim3(256), 0, stream, g1);
+  const int grid1 = round_grid(tile_grid(R, E, C, 256, N1, 256));
+  const int grid2 = round_grid(tile_grid(R, E, C, 256, N2, 256) * g2.splits);
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, 32, 4>), dim3(grid1), dim3(256), 0, stream, g1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
   return hipGetLastError();
+}
+
+hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
+  GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr, nullptr, 0, 0};
+  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2,
+              nullptr, 0, 0};
+  if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
+    g1.A = a.x;
+    g1.rows = a.rows;
+    g1.a_rows = a.T;
+  }
+  return a.act == kActSilu ? launch_ffn<kEpiSilu>(g1, g2, a.bf16, a.C, a.R, a.E, a.d_ffn, a.d, stream, ev_mid)
+                           : launch_ffn<kEpiGelu>(g1, g2, a.bf16, a.C, a.R, a.E, a.d_ffn, a.d, stream, ev_mid);
+}
+
+hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream) {
+  // one dense expert over the T token rows in order: E = 1, no split of K
+  GemmArgs g1{a.x, a.W1, a.b1, a.H, nullptr, nullptr, 1, a.d_ffn, a.d, a.T, a.T, 1, nullptr, nullptr, 0, 1};
+  GemmArgs g2{a.H, a.W2, a.b2, a.y, nullptr, nullptr, 1, a.d, a.d_ffn, a.T, a.T, 1, nullptr, nullptr, 0, 1};
+  return a.act == kActSilu ? launch_ffn<kEpiSilu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr)
+                           : launch_ffn<kEpiGelu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr);
 }
 
 namespace {

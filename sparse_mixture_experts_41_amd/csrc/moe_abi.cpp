@@ -27,13 +27,16 @@ struct Derived {
   bool bf16;
   size_t esize;
   float tau;
-  int gumbel;
+  int noise;        // moe::kNoiseNone / kNoiseGumbel / kNoiseGaussian
+  float noise_std;  // Gaussian only
+  int act;          // moe::kActGelu / kActSilu
+  int dffs;         // shared expert hidden width, 0 = none
   uint32_t key0, key1;
 };
 
 struct Layout {
   size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
-      y_perm2, total;
+      y_perm2, Hs, ys, total;
 };
 
 // C = ceil(c*k*T/E) for the exact value of the double c = m * 2^sh (m a 53-bit integer).
@@ -90,9 +93,36 @@ moe_status check_config(const moe_config* cfg, Derived* D) {
   D->bf16 = bf16;
   D->esize = bf16 ? 2 : 4;
   D->tau = cfg->temperature;
-  D->gumbel = cfg->gumbel;
+  D->noise = cfg->gumbel ? moe::kNoiseGumbel : moe::kNoiseNone;
+  D->noise_std = 0.0f;
+  D->act = moe::kActGelu;
+  D->dffs = 0;
   D->key0 = static_cast<uint32_t>(cfg->seed & 0xffffffffull);
   D->key1 = static_cast<uint32_t>(cfg->seed >> 32);
+  return MOE_OK;
+}
+
+// Forward variants on top of a checked configuration.
+moe_status check_variant(const moe_variant* v, Derived* D) {
+  if (v == nullptr) return MOE_OK;
+  if (v->activation != MOE_ACT_GELU && v->activation != MOE_ACT_SILU) return fail(MOE_EINVAL, "unknown activation");
+  if (!(v->noise_std >= 0.0f) || !std::isfinite(v->noise_std))
+    return fail(MOE_EINVAL, "noise_std must be finite and >= 0");
+  if (v->noise_std > 0.0f && D->noise == moe::kNoiseGumbel)
+    return fail(MOE_EINVAL, "Gaussian noise (noise_std > 0) needs gumbel = 0");
+  if (v->shared_d_ffn < 0) return fail(MOE_EINVAL, "shared_d_ffn must be >= 0");
+  if (v->shared_d_ffn > 65536) return fail(MOE_EUNSUPPORTED, "shared_d_ffn is limited to 65536");
+  if (v->shared_d_ffn > 0) {
+    if (D->bf16 && v->shared_d_ffn % 64 != 0) return fail(MOE_EUNSUPPORTED, "bf16 needs shared_d_ffn % 64 == 0");
+    if (!D->bf16 && (v->shared_d_ffn % 8 != 0 || v->shared_d_ffn > 16384))
+      return fail(MOE_EUNSUPPORTED, "float32 needs shared_d_ffn a multiple of 8, at most 16384");
+  }
+  D->act = v->activation == MOE_ACT_SILU ? moe::kActSilu : moe::kActGelu;
+  if (v->noise_std > 0.0f) {
+    D->noise = moe::kNoiseGaussian;
+    D->noise_std = v->noise_std;
+  }
+  D->dffs = static_cast<int>(v->shared_d_ffn);
   return MOE_OK;
 }
 
@@ -122,6 +152,8 @@ Layout layout_of(const Derived& D) {
   L.H = take(R * static_cast<size_t>(D.dff) * D.esize);
   L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
   L.y_perm2 = take(D.bf16 ? R * static_cast<size_t>(D.d) * 4 : 0);
+  L.Hs = take(D.dffs > 0 ? T * static_cast<size_t>(D.dffs) * D.esize : 0);
+  L.ys = take(D.dffs > 0 ? T * static_cast<size_t>(D.d) * 4 : 0);
   L.total = off;
   return L;
 }
@@ -176,7 +208,8 @@ moe::RouterArgs router_args(const Derived& D, const void* x, const void* Wg, con
   a.k = D.k;
   a.bf16 = D.bf16 ? 1 : 0;
   a.tau = D.tau;
-  a.gumbel = D.gumbel;
+  a.noise = D.noise;
+  a.noise_std = D.noise_std;
   a.key0 = D.key0;
   a.key1 = D.key1;
   a.logits = logits;
@@ -326,18 +359,28 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   }
   MOE_CHECK(need_ws(D, ws, ws_bytes, &Lw));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  MOE_HIP(moe::launch_combine(y_perm, nullptr, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
+  MOE_HIP(moe::launch_combine(y_perm, nullptr, nullptr, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
+          "combine");
   if (stats) MOE_HIP(moe::launch_stats(counts, prob_colsum, D.E, D.k, D.T, f, P, L, st), "stats");
   return MOE_OK;
 }
 
-moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, const float* bg, const void* W1,
-                       const void* b1, const void* W2, const void* b2, void* y, float* f, float* P, float* L,
-                       int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws, size_t ws_bytes,
-                       moe_stream_t stream) {
+namespace {
+
+moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const void* x, const void* Wg,
+                        const float* bg, const void* W1, const void* b1, const void* W2, const void* b2, void* y,
+                        float* f, float* P, float* L, int32_t* counts, int32_t* kept, const moe_forward_aux* aux,
+                        void* ws, size_t ws_bytes, moe_stream_t stream) {
   Derived D;
   Layout Lw;
   MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(check_variant(variant, &D));
+  if (D.dffs > 0) {
+    MOE_CHECK(need(variant->W1s, 16, "W1s"));
+    MOE_CHECK(need(variant->b1s, D.esize, "b1s", true));
+    MOE_CHECK(need(variant->W2s, 16, "W2s"));
+    MOE_CHECK(need(variant->b2s, D.esize, "b2s", true));
+  }
   MOE_CHECK(need(x, 16, "x"));
   MOE_CHECK(need(Wg, 16, "Wg"));
   MOE_CHECK(need(bg, 4, "bg", true));
@@ -369,7 +412,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(ax.stage_events);
   float* logits = ax.logits ? ax.logits : at<float>(ws, Lw.logits);
-  const bool has_scores = D.gumbel != 0 || D.tau != 1.0f;
+  const bool has_scores = D.noise != moe::kNoiseNone || D.tau != 1.0f;
   float* scores = ax.scores ? ax.scores : (has_scores ? at<float>(ws, Lw.scores) : nullptr);
   int32_t* idx = ax.topk_idx ? ax.topk_idx : at<int32_t>(ws, Lw.idx);
   float* w = ax.topk_w ? ax.topk_w : at<float>(ws, Lw.w);
@@ -432,6 +475,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
   fa.C = C;
   fa.bf16 = D.bf16 ? 1 : 0;
   fa.y_perm2 = at<float>(ws, Lw.y_perm2);
+  fa.act = D.act;
   if (moe::ffn_gathers(fa))
     fa.rows = perm;
   else
@@ -439,12 +483,61 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
             "gather");
   if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
   MOE_HIP(moe::launch_expert_ffn(fa, st, ev ? ev[4] : nullptr), "expert_ffn");
+  // 4b. the shared expert on every token (timed with the second expert GEMM)
+  float* y_shared = nullptr;
+  if (D.dffs > 0) {
+    moe::SharedFfnArgs sa{};
+    sa.x = x;
+    sa.W1 = variant->W1s;
+    sa.b1 = variant->b1s;
+    sa.W2 = variant->W2s;
+    sa.b2 = variant->b2s;
+    sa.H = at<void>(ws, Lw.Hs);
+    sa.y = y_shared = at<float>(ws, Lw.ys);
+    sa.T = D.T;
+    sa.d = D.d;
+    sa.d_ffn = D.dffs;
+    sa.bf16 = D.bf16 ? 1 : 0;
+    sa.act = D.act;
+    MOE_HIP(moe::launch_shared_ffn(sa, st), "shared_ffn");
+  }
   if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
-  // 5. combine (adding the two K halves of GEMM2 when it was split)
+  // 5. combine (adding the two K halves of GEMM2 when it was split, from the shared output)
   const float* y_perm2 = moe::ffn_splits(fa) == 2 ? fa.y_perm2 : nullptr;
-  MOE_HIP(moe::launch_combine(y_perm, y_perm2, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st), "combine");
+  MOE_HIP(moe::launch_combine(y_perm, y_perm2, y_shared, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
+          "combine");
   if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");
   return MOE_OK;
+}
+
+}  // namespace
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, const float* bg, const void* W1,
+                       const void* b1, const void* W2, const void* b2, void* y, float* f, float* P, float* L,
+                       int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws, size_t ws_bytes,
+                       moe_stream_t stream) {
+  return forward_impl(cfg, nullptr, x, Wg, bg, W1, b1, W2, b2, y, f, P, L, counts, kept, aux, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_ex(const moe_config* cfg, const moe_variant* variant, const void* x, const void* Wg,
+                          const float* bg, const void* W1, const void* b1, const void* W2, const void* b2, void* y,
+                          float* f, float* P, float* L, int32_t* counts, int32_t* kept, const moe_forward_aux* aux,
+                          void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return forward_impl(cfg, variant, x, Wg, bg, W1, b1, W2, b2, y, f, P, L, counts, kept, aux, ws, ws_bytes, stream);
+}
+
+moe_status moe_workspace_size_ex(const moe_config* cfg, const moe_variant* variant, size_t* bytes) {
+  Derived D;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(check_variant(variant, &D));
+  if (bytes == nullptr) return fail(MOE_EINVAL, "bytes is NULL");
+  *bytes = layout_of(D).total;
+  return MOE_OK;
+}
+
+float moe_temperature_at(int64_t step, float tau0, float tau_min, float rate) {
+  const double t = static_cast<double>(tau0) - static_cast<double>(rate) * static_cast<double>(step);
+  return static_cast<float>(t > static_cast<double>(tau_min) ? t : static_cast<double>(tau_min));
 }
 
 const char* moe_status_str(moe_status status) {

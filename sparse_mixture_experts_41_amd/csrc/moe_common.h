@@ -36,9 +36,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): word 0 of the block for counter
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): words 0 and 1 of the block for counter
 // (c0, c1, 0, 0) and key (k0, k1).
-__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+__device__ __forceinline__ void philox_words01(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1, uint32_t& w0,
+                                               uint32_t& w1) {
   uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
@@ -55,7 +56,14 @@ __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint3
     x2 = n2;
     x3 = lo0;
   }
-  return x0;
+  w0 = x0;
+  w1 = x1;
+}
+
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+  uint32_t w0, w1;
+  philox_words01(c0, c1, k0, k1, w0, w1);
+  return w0;
 }
 
 // Gumbel(0,1) noise for (token t, expert e): u = (w0 + 1/2) 2^-32 in float64, strictly inside
@@ -64,6 +72,26 @@ __device__ __forceinline__ float gumbel_noise(uint32_t t, uint32_t e, uint32_t k
   const uint32_t w0 = philox_word0(t, e, k0, k1);
   const double u = (static_cast<double>(w0) + 0.5) * 0x1p-32;
   return static_cast<float>(-log(-log(u)));
+}
+
+// Gaussian noise std * n for (token t, expert e): u1, u2 from words 0 and 1 as above,
+// n = sqrt(-2 ln u1) cos(2 pi u2) (Box-Muller) in float64, rounded once to float32.
+__device__ __forceinline__ float gaussian_noise(uint32_t t, uint32_t e, uint32_t k0, uint32_t k1, float std) {
+  uint32_t w0, w1;
+  philox_words01(t, e, k0, k1, w0, w1);
+  const double u1 = (static_cast<double>(w0) + 0.5) * 0x1p-32;
+  const double u2 = (static_cast<double>(w1) + 0.5) * 0x1p-32;
+  const double n = sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925287 * u2);
+  return static_cast<float>(static_cast<double>(std) * n);
+}
+
+// SiLU(v) = v sigmoid(v) = v / (1 + e^-v), float32 with the library exponential.
+__device__ __forceinline__ float silu_exact(float v) { return v / (1.0f + expf(-v)); }
+
+// SiLU for results rounded to bf16: v * rcp(1 + 2^(-v log2 e)) with the hardware exp2 and
+// reciprocal (a few float32 ulps). SiLU(+inf) = +inf; a -inf input gives NaN.
+__device__ __forceinline__ float silu_bf16_path(float v) {
+  return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * -1.4426950408889634f));
 }
 
 __device__ __forceinline__ float gelu_erf(float v) {

@@ -7,6 +7,9 @@
 
 namespace moe {
 
+// Router noise added to the logits before the temperature: none, Gumbel, or Gaussian.
+enum { kNoiseNone = 0, kNoiseGumbel = 1, kNoiseGaussian = 2 };
+
 struct RouterArgs {
   const void* x;          // [T,d] dtype
   const void* Wg;         // [E,d] dtype
@@ -14,7 +17,8 @@ struct RouterArgs {
   int T, d, E, k;
   int bf16;               // 1 = bfloat16 storage, 0 = float32
   float tau;
-  int gumbel;
+  int noise;              // kNoiseNone, kNoiseGumbel or kNoiseGaussian
+  float noise_std;        // Gaussian noise only
   uint32_t key0, key1;
   float* logits;          // [T,E]
   float* scores;          // [T,E] or null
@@ -58,6 +62,9 @@ hipError_t launch_permute(const int32_t* idx, const int32_t* blockbase, const in
 hipError_t launch_gather(const void* x, const int32_t* perm, const int32_t* kept, const int32_t* offsets,
                          int E, int R, int row_bytes, void* x_perm, hipStream_t stream);
 
+// Expert activation: GeLU (the default) or SiLU.
+enum { kActGelu = 0, kActSilu = 1 };
+
 struct FfnArgs {
   const void* x_perm;     // [R,d] (unused when rows is set)
   const void* x;          // [T,d] token rows, read through `rows` (bf16 MFMA path only)
@@ -74,6 +81,7 @@ struct FfnArgs {
   float* y_perm2;         // [R,d] second K half of GEMM2 when ffn_splits() == 2
   int E, d, d_ffn, R, C;
   int bf16;
+  int act;                // kActGelu or kActSilu
 };
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
 // copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
@@ -84,13 +92,29 @@ bool ffn_gathers(const FfnArgs& a);
 int ffn_splits(const FfnArgs& a);
 // GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid);
+// The shared expert: one dense FFN over the T token rows of x (no routing):
+// H = act(x W1ᵀ + b1) [T, d_ffn], y = H W2ᵀ + b2 [T, d] float.
+struct SharedFfnArgs {
+  const void* x;          // [T,d]
+  const void* W1;         // [d_ffn,d]
+  const void* b1;         // [d_ffn] or null
+  const void* W2;         // [d,d_ffn]
+  const void* b2;         // [d] or null
+  void* H;                // [T,d_ffn]
+  float* y;               // [T,d]
+  int T, d, d_ffn;
+  int bf16, act;
+};
+hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream);
+
 // y_perm[r] += y_perm2[r] for the sum(kept) valid rows (standalone expert FFN with 2 parts).
 hipError_t launch_add_partials(float* y_perm, const float* y_perm2, const int32_t* kept, const int32_t* offsets,
                                int E, int R, int d, hipStream_t stream);
 
-// y_perm2 (nullable): second GEMM2 partial, added to y_perm before weighting.
-hipError_t launch_combine(const float* y_perm, const float* y_perm2, const int32_t* dest, const float* w, int T,
-                          int d, int k, int R, int bf16, void* y, hipStream_t stream);
+// y_perm2 (nullable): second GEMM2 partial, added to y_perm before weighting. y_shared
+// (nullable, [T,d] float): the shared expert's output, where each token's sum starts.
+hipError_t launch_combine(const float* y_perm, const float* y_perm2, const float* y_shared, const int32_t* dest,
+                          const float* w, int T, int d, int k, int R, int bf16, void* y, hipStream_t stream);
 
 hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,
                         float* L, hipStream_t stream);

@@ -20,13 +20,18 @@ namespace moe {
 
 namespace {
 
+__device__ __forceinline__ float router_noise(int kind, float std, uint32_t t, uint32_t e, uint32_t k0,
+                                              uint32_t k1) {
+  return kind == kNoiseGumbel ? gumbel_noise(t, e, k0, k1) : gaussian_noise(t, e, k0, k1, std);
+}
+
 // Epilogue of up to BT tokens held by one wave (BT = 16 or 64). `rows` (LDS, BT rows of pitch
 // ldr) holds the float32 logits z (bias added) of tokens t0 .. t0+nt-1. Writes the logits and
 // scores (coalesced, from LDS), then per token (one lane each) the top-k indices and weights;
 // leaves p in `rows` (zero rows past nt) and returns this lane's bitmask of chosen experts.
 template <int BT>
-__device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int gumbel,
-                                   uint32_t key0, uint32_t key1, float* __restrict__ logits,
+__device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
+                                   float noise_std, uint32_t key0, uint32_t key1, float* __restrict__ logits,
                                    float* __restrict__ scores, int32_t* __restrict__ idx_out,
                                    float* __restrict__ w_out) {
   const int lane = lane_id();
@@ -34,11 +39,12 @@ __device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, 
   for (int i = lane; i < nt * E; i += kWave) logits[base + i] = rows[(i / E) * ldr + i % E];
   const bool valid = lane < nt;                    // nt <= BT
   float* row = rows + (lane < BT ? lane : 0) * ldr;
-  if (valid && (gumbel || tau != 1.0f)) {
+  if (valid && (noise != kNoiseNone || tau != 1.0f)) {
     const int t = t0 + lane;
     for (int e = 0; e < E; ++e) {
       float s = row[e];
-      if (gumbel) s = s + gumbel_noise(static_cast<uint32_t>(t), static_cast<uint32_t>(e), key0, key1);
+      if (noise != kNoiseNone)
+        s = s + router_noise(noise, noise_std, static_cast<uint32_t>(t), static_cast<uint32_t>(e), key0, key1);
       if (tau != 1.0f) s = s / tau;
       row[e] = s;
     }
@@ -131,8 +137,8 @@ __device__ __forceinline__ void group_partials(const float* rows, int ldr, uint6
 // Cross-lane steps are xor butterflies within each group of four lanes, so all four lanes of a
 // token hold identical values. Leaves p in `rows` (zero rows past nt); lane 4 t returns token
 // t's bitmask of chosen experts, the other lanes 0.
-__device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int gumbel,
-                                  uint32_t key0, uint32_t key1, float* __restrict__ logits,
+__device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
+                                  float noise_std, uint32_t key0, uint32_t key1, float* __restrict__ logits,
                                   float* __restrict__ scores, int32_t* __restrict__ idx_out,
                                   float* __restrict__ w_out) {
   const int lane = lane_id();
@@ -144,11 +150,12 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
   const int e0 = q * EQ, e1 = min(E, e0 + EQ);
   float* row = rows + tl * ldr;
   const bool valid = tl < nt;
-  if (valid && (gumbel || tau != 1.0f)) {
+  if (valid && (noise != kNoiseNone || tau != 1.0f)) {
     const int t = t0 + tl;
     for (int e = e0; e < e1; ++e) {
       float s = row[e];
-      if (gumbel) s = s + gumbel_noise(static_cast<uint32_t>(t), static_cast<uint32_t>(e), key0, key1);
+      if (noise != kNoiseNone)
+        s = s + router_noise(noise, noise_std, static_cast<uint32_t>(t), static_cast<uint32_t>(e), key0, key1);
       if (tau != 1.0f) s = s / tau;
       row[e] = s;
     }
@@ -223,7 +230,7 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
 __device__ void group_finish(const RouterArgs& a, float* rows, int LDE, int t0, int nt_tok, int grp) {
   const int lane = lane_id();
   const int E = a.E;
-  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.gumbel, a.key0, a.key1, a.logits,
+  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.noise, a.noise_std, a.key0, a.key1, a.logits,
                                      a.scores, a.idx, a.w);
   __syncthreads();
   // group partials: column sums of p over the 16 rows (ascending), and the histogram, whose bits
@@ -412,7 +419,7 @@ __global__ __launch_bounds__(64) void router_f32_kernel(RouterArgs a) {
     }
   }
   __syncthreads();
-  const uint64_t sel = group_epilogue<kBlockTokens>(rows, LDR, t0, nt, a.E, a.k, a.tau, a.gumbel, a.key0, a.key1,
+  const uint64_t sel = group_epilogue<kBlockTokens>(rows, LDR, t0, nt, a.E, a.k, a.tau, a.noise, a.noise_std, a.key0, a.key1,
                                                     a.logits, a.scores, a.idx, a.w);
   __syncthreads();
   group_partials<kBlockTokens>(rows, LDR, sel, blk * (kBlockTokens / kGroupTokens), a.ng, a.E, a.probsum_part,

@@ -14,7 +14,8 @@ from . import _lib
 from ._lib import MOE_FORWARD_STAGES, STAGE_NAMES, MoeConfig, MoeForwardAux, make_config
 
 __all__ = ["make_config", "capacity", "workspace_size", "workspace", "route", "dispatch", "expert_ffn", "combine",
-           "forward", "ForwardPlan", "StageEvents", "STAGE_NAMES", "MoeConfig"]
+           "forward", "ForwardPlan", "StageEvents", "STAGE_NAMES", "MoeConfig", "make_variant", "workspace_size_ex",
+           "temperature_at"]
 
 
 def _storage_dtype(cfg: MoeConfig) -> torch.dtype:
@@ -198,10 +199,44 @@ class StageEvents:
                 self.array[i] = None
 
 
-class ForwardPlan:
-    """Preallocated outputs and workspace for repeated moe_forward calls on fixed tensors."""
+def make_variant(cfg: MoeConfig, activation: str = "gelu", noise_std: float = 0.0, shared=None):
+    """A moe_variant: expert activation ("gelu" or "silu"), Gaussian router noise std, and an
+    optional shared expert ``shared = (W1s [ds,d], b1s [ds] or None, W2s [d,ds], b2s [d] or None)``.
+    Returns (variant, tensors kept alive for it)."""
+    sd = _storage_dtype(cfg)
+    v = _lib.MoeVariant()
+    v.activation = {"gelu": _lib.MOE_ACT_GELU, "silu": _lib.MOE_ACT_SILU}[activation]
+    v.noise_std = float(noise_std)
+    keep = ()
+    if shared is not None:
+        W1s, b1s, W2s, b2s = shared
+        ds = W1s.shape[0]
+        _expect(W1s, "W1s", (ds, cfg.d), sd)
+        _expect(b1s, "b1s", (ds,), sd, optional=True)
+        _expect(W2s, "W2s", (cfg.d, ds), sd)
+        _expect(b2s, "b2s", (cfg.d,), sd, optional=True)
+        v.shared_d_ffn = int(ds)
+        v.W1s, v.b1s, v.W2s, v.b2s = _ptr(W1s), _ptr(b1s), _ptr(W2s), _ptr(b2s)
+        keep = tuple(shared)
+    return v, keep
 
-    def __init__(self, cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True):
+
+def workspace_size_ex(cfg: MoeConfig, variant) -> int:
+    n = ctypes.c_size_t()
+    _lib.check(_lib.load().moe_workspace_size_ex(ctypes.byref(cfg), ctypes.byref(variant), ctypes.byref(n)))
+    return n.value
+
+
+def temperature_at(step: int, tau0: float = 1.0, tau_min: float = 0.5, rate: float = 1e-4) -> float:
+    """moe_temperature_at: max(tau_min, tau0 - rate * step), rounded to float32."""
+    return float(_lib.load().moe_temperature_at(int(step), float(tau0), float(tau_min), float(rate)))
+
+
+class ForwardPlan:
+    """Preallocated outputs and workspace for repeated moe_forward calls on fixed tensors.
+    ``variant`` (from make_variant) selects moe_forward_ex."""
+
+    def __init__(self, cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True, variant=None):
         sd = _storage_dtype(cfg)
         T, d, E, k, dff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ffn
         _expect(x, "x", (T, d), sd)
@@ -214,7 +249,11 @@ class ForwardPlan:
         dev = x.device
         self.cfg = cfg
         self.inputs = (x, Wg, bg, W1, b1, W2, b2)
-        self.ws = workspace(cfg, dev)
+        self.variant = variant
+        if variant is None:
+            self.ws = workspace(cfg, dev)
+        else:
+            self.ws = torch.empty((workspace_size_ex(cfg, variant[0]),), dtype=torch.uint8, device=dev)
         f32, i32 = torch.float32, torch.int32
         self.out = {
             "y": torch.empty((T, d), dtype=sd, device=dev),
@@ -245,13 +284,18 @@ class ForwardPlan:
         self.aux.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value if events is not None else None
         x, Wg, bg, W1, b1, W2, b2 = self.inputs
         o = self.out
-        _lib.check(_lib.load().moe_forward(
-            ctypes.byref(self.cfg), _ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
-            _ptr(o["y"]), _ptr(o["f"]), _ptr(o["P"]), _ptr(o["L"]), _ptr(o["counts"]), _ptr(o["kept"]),
-            ctypes.byref(self.aux), _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        args = (_ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                _ptr(o["y"]), _ptr(o["f"]), _ptr(o["P"]), _ptr(o["L"]), _ptr(o["counts"]), _ptr(o["kept"]),
+                ctypes.byref(self.aux), _ptr(self.ws), self.ws.numel(), _stream(stream))
+        lib = _lib.load()
+        if self.variant is None:
+            _lib.check(lib.moe_forward(ctypes.byref(self.cfg), *args))
+        else:
+            _lib.check(lib.moe_forward_ex(ctypes.byref(self.cfg), ctypes.byref(self.variant[0]), *args))
         return o
 
 
-def forward(cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True) -> dict:
-    """The whole layer (moe_forward); returns y, f, P, L, counts, kept (+ routing arrays)."""
-    return ForwardPlan(cfg, x, Wg, bg, W1, b1, W2, b2, keep_routing=keep_routing).run()
+def forward(cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True, variant=None) -> dict:
+    """The whole layer (moe_forward, or moe_forward_ex with a variant); returns y, f, P, L,
+    counts, kept (+ routing arrays)."""
+    return ForwardPlan(cfg, x, Wg, bg, W1, b1, W2, b2, keep_routing=keep_routing, variant=variant).run()

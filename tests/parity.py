@@ -21,7 +21,7 @@ import torch
 import oracle
 from oracle import philox
 from sparse_mixture_experts_41_amd import ops
-from workloads import MoEShape, bf16_bits_to_f32, make_inputs
+from workloads import MoEShape, bf16_bits_to_f32, make_inputs, make_shared_expert
 
 Z_REL = 1e-4
 BF16_MAX_RMS = 2e-2
@@ -50,15 +50,38 @@ def to_device(arr, dtype, device="cuda"):
 
 
 class Problem:
-    """Seeded inputs of one shape, on the host (exact values) and on the GPU (storage dtype)."""
+    """Seeded inputs of one shape, on the host (exact values) and on the GPU (storage dtype).
 
-    def __init__(self, shape: MoEShape, bias_std: float = 0.0, arrays: dict | None = None):
+    Forward variants: ``activation`` ("gelu"/"silu"), Gaussian router ``noise_std``, and a
+    shared expert of hidden width ``shared_d_ffn`` (seeded weights; 0 = none)."""
+
+    def __init__(self, shape: MoEShape, bias_std: float = 0.0, arrays: dict | None = None, activation: str = "gelu",
+                 noise_std: float = 0.0, shared_d_ffn: int = 0):
         self.shape = shape
         self.cfg = config_of(shape)
         self.arrays = arrays if arrays is not None else make_inputs(shape, bias_std)
         dt = shape.dtype
         self.host = {n: (a if n == "bg" else host_values(a, dt)) for n, a in self.arrays.items()}
         self.dev = {n: to_device(a, dt) for n, a in self.arrays.items()}
+        self.activation, self.noise_std, self.shared_d_ffn = activation, float(noise_std), int(shared_d_ffn)
+        self.shared_host = self.shared_dev = None
+        if self.shared_d_ffn:
+            sh = make_shared_expert(shape, self.shared_d_ffn, bias_std)
+            self.shared_host = tuple(host_values(sh[n], dt) for n in ("W1s", "b1s", "W2s", "b2s"))
+            self.shared_dev = tuple(to_device(sh[n], dt) for n in ("W1s", "b1s", "W2s", "b2s"))
+
+    @property
+    def has_variant(self) -> bool:
+        return self.activation != "gelu" or self.noise_std > 0.0 or self.shared_d_ffn > 0
+
+    def variant(self):
+        if not self.has_variant:
+            return None
+        return ops.make_variant(self.cfg, self.activation, self.noise_std, self.shared_dev)
+
+    def oracle_kw(self) -> dict:
+        """The variant's keyword arguments of oracle.forward / forward_rows / brute_dense."""
+        return dict(act=self.activation, noise_std=self.noise_std, shared=self.shared_host)
 
     def args(self):
         d = self.dev
@@ -70,7 +93,7 @@ class Problem:
 
 
 def run_forward(p: Problem) -> dict:
-    plan = ops.ForwardPlan(p.cfg, *p.args())
+    plan = ops.ForwardPlan(p.cfg, *p.args(), variant=p.variant())
     out = plan.run()
     torch.cuda.synchronize()
     res = {k: (v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()) for k, v in out.items()}
@@ -88,7 +111,12 @@ def check_logits(z_gpu, z_ref):
 def check_scores(p: Problem, z_gpu, s_gpu):
     """The GPU's scores from its own logits: s = ((z + g) / tau) in float32 with the oracle's g."""
     sh = p.shape
-    g32 = philox.gumbel_f32(sh.seed, sh.T, sh.E) if sh.gumbel else None
+    if sh.gumbel:
+        g32 = philox.gumbel_f32(sh.seed, sh.T, sh.E)
+    elif p.noise_std > 0.0:
+        g32 = philox.gaussian_f32(sh.seed, sh.T, sh.E, p.noise_std)
+    else:
+        g32 = None
     s_ref = oracle.scores(z_gpu, sh.temperature, g32)
     ulp = np.abs(s_gpu.view(np.int32).astype(np.int64) - s_ref.view(np.int32).astype(np.int64))
     same = s_gpu == s_ref
@@ -154,9 +182,10 @@ def check_forward_full(p: Problem, gpu: dict | None = None) -> dict:
     check_scores(p, gpu["logits"], gpu["scores"])
     chk = check_routing(p, gpu)
     ref = oracle.forward(*p.host_args(), k=sh.k, capacity_factor=sh.capacity_factor, tau=sh.temperature,
-                         gumbel=sh.gumbel, seed=sh.seed, given_scores=gpu["scores"])
+                         gumbel=sh.gumbel, seed=sh.seed, given_scores=gpu["scores"], **p.oracle_kw())
     dropped_all = np.all(ref["dest"] < 0, axis=1)
-    assert np.all(gpu["y"][dropped_all] == 0.0), "fully dropped tokens must give exactly 0"
+    if not p.shared_d_ffn:
+        assert np.all(gpu["y"][dropped_all] == 0.0), "fully dropped tokens must give exactly 0"
     stats = check_output(gpu["y"], ref["y"], sh.dtype, sh.name)
     stats.update(kept=int(chk["dispatch"]["kept"].sum()), drops=int(chk["dispatch"]["drops"].sum()),
                  fully_dropped=int(dropped_all.sum()))
@@ -185,9 +214,11 @@ def check_forward_sampled(p: Problem, gpu: dict | None = None) -> dict:
     chk = check_routing(p, gpu)
     rows, rand_pos = sample_rows(sh.T, chk["dispatch"]["dest"])
     ref = oracle.forward_rows(rows, *p.host_args(), k=sh.k, capacity_factor=sh.capacity_factor,
-                              tau=sh.temperature, gumbel=sh.gumbel, seed=sh.seed, given_scores=gpu["scores"])
+                              tau=sh.temperature, gumbel=sh.gumbel, seed=sh.seed, given_scores=gpu["scores"],
+                              **p.oracle_kw())
     dropped_all = np.all(ref["dest"][rows] < 0, axis=1)
-    assert np.all(gpu["y"][rows][dropped_all] == 0.0)
+    if not p.shared_d_ffn:
+        assert np.all(gpu["y"][rows][dropped_all] == 0.0)
     rms = np.sqrt(np.mean(ref["y_rows"][rand_pos] ** 2))      # rms(y_ref) over all tokens, estimated
     stats = check_output(gpu["y"][rows], ref["y_rows"], sh.dtype, sh.name, rms=rms)
     stats.update(kept=int(chk["dispatch"]["kept"].sum()), drops=int(chk["dispatch"]["drops"].sum()),

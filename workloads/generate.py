@@ -28,6 +28,7 @@ _CHUNK = 1 << 22
 # One stream id per tensor.
 STREAM_X, STREAM_WG, STREAM_BG, STREAM_W1, STREAM_B1, STREAM_W2, STREAM_B2 = 0, 1, 2, 3, 4, 5, 6
 STREAM_CENTRES, STREAM_CLUSTER, STREAM_NOISE = 7, 8, 9
+STREAM_W1S, STREAM_B1S, STREAM_W2S, STREAM_B2S = 10, 11, 12, 13
 
 N_CLUSTERS = 512
 CLUSTER_ZIPF_S = 1.2
@@ -159,3 +160,16 @@ def make_inputs(cfg: MoEShape, bias_std: float = 0.0) -> dict:
         "x": _store(x, dt), "Wg": _store(Wg, dt), "bg": bg,
         "W1": _store(W1, dt), "b1": b1, "W2": _store(W2, dt), "b2": b2,
     }
+
+
+def make_shared_expert(cfg: MoEShape, d_ffn_s: int, bias_std: float = 0.0) -> dict:
+    """Weights of one shared expert for ``cfg`` in storage form: W1s [d_ffn_s, d] ~ N(0, 1/sqrt(d)),
+    W2s [d, d_ffn_s] ~ N(0, 1/sqrt(d_ffn_s)); b1s, b2s ~ N(0, bias_std) when bias_std > 0."""
+    d, seed, dt = cfg.d, cfg.seed, cfg.dtype
+    W1s = normal_f32(seed, STREAM_W1S, (d_ffn_s, d), 1.0 / np.sqrt(d))
+    W2s = normal_f32(seed, STREAM_W2S, (d, d_ffn_s), 1.0 / np.sqrt(d_ffn_s))
+    b1s = b2s = None
+    if bias_std > 0.0:
+        b1s = _store(normal_f32(seed, STREAM_B1S, (d_ffn_s,), bias_std), dt)
+        b2s = _store(normal_f32(seed, STREAM_B2S, (d,), bias_std), dt)
+    return {"W1s": _store(W1s, dt), "b1s": b1s, "W2s": _store(W2s, dt), "b2s": b2s}
