@@ -19,7 +19,8 @@ Sources (pages cited by title or address and section):
   [A]  "为什么92%的AI团队误用MoE？…" (aberweb.com), sections 2.3 (a shared expert that every
        token uses, plus the routed experts), 3.2 (experts Linear -> SiLU -> Linear; the
        temperature schedule tau = max(0.5, 1.0 - 0.0001 * step)).
-  [M]  "MoE架构揭秘：参数规模≠计算量…" (mhpn.cn): the same schedule with rate 0.001.
+  [M]  "MoE架构揭秘：参数规模≠计算量…" (mhpn.cn): the same schedule with rate 0.001; section
+       3.1's load-variance loss.
 Forward variants (the plain layer is the default of each): SiLU experts ([A] 3.2); Gaussian
 router noise noise_std * N(0, 1) added to the logits ([G] 3.3; generator in philox.py); a
 shared expert whose output is added to every token's routed sum ([A] 2.3).
@@ -220,6 +221,136 @@ def balance_stats(counts: np.ndarray, p: np.ndarray, k: int) -> dict:
     return {"f": f, "P": P, "L": float(E * np.sum(f * P))}
 
 
+# ---------------------------------------------------------------- capacity policies ([M] 3.x)
+def dispatch_random(idx: np.ndarray, E: int, C: int, seed: int) -> dict:
+    """Random capacity dropping: expert e keeps the C slots with the smallest (priority, t),
+    priority = philox.drop_priority(seed)[t, e] (a uniformly random subset of its slots when
+    over capacity); kept rows are stored in token order. Same outputs as dispatch()."""
+    T, k = idx.shape
+    prio = philox.drop_priority(seed, T, E)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int64)
+    kept = np.minimum(counts, C)
+    offsets = np.concatenate([[0], np.cumsum(kept)[:-1]]).astype(np.int64)
+    dest = np.full((T, k), -1, dtype=np.int64)
+    perm = np.empty(int(kept.sum()), dtype=np.int64)
+    for e in range(E):
+        slots = [(t, j) for t in range(T) for j in range(k) if idx[t, j] == e]      # token order
+        chosen = sorted(slots, key=lambda tj: (int(prio[tj[0], e]), tj[0]))[:C]
+        keep = sorted(chosen)                                                        # back to token order
+        for r, (t, j) in enumerate(keep):
+            dest[t, j] = offsets[e] + r
+            perm[offsets[e] + r] = t
+    return {"counts": counts, "kept": kept, "offsets": offsets, "dest": dest, "perm": perm,
+            "drops": counts - kept, "C": C}
+
+
+def dispatch_reroute(idx: np.ndarray, idx_next: np.ndarray, E: int, C: int) -> dict:
+    """Rerouting over-capacity slots to the next-best experts: pass 1 is dispatch() (token
+    order); the slots it drops move, in j order within a token, to idx_next[t, 0], idx_next[t,
+    1], ... (the token's (k+1)-th, (k+2)-th, ... ranked experts; -1 past the last expert:
+    dropped), and pass 2 assigns those slots in slot order (t*k + j) to the capacity left after
+    pass 1. Expert e's segment holds its pass-1 rows, then its pass-2 rows. Returns dispatch()'s
+    fields (counts are pass-1 counts; kept, drops final) plus `final_idx` [T,k], the expert
+    each slot ends at (its pass-1 choice when it had no next expert)."""
+    T, k = idx.shape
+    d1 = dispatch(idx, E, C)
+    rank1 = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if d1["dest"][t, j] >= 0:
+                e = idx[t, j]
+                rank1[t, j] = d1["dest"][t, j] - d1["offsets"][e]
+    kept1 = d1["kept"]
+    room = C - kept1
+    kept2 = np.zeros(E, dtype=np.int64)
+    rank2 = np.full((T, k), -1, dtype=np.int64)
+    final_idx = idx.copy()
+    for t in range(T):
+        m = 0                                       # the token's dropped slots so far
+        for j in range(k):
+            if d1["dest"][t, j] >= 0:
+                continue
+            e2 = idx_next[t, m]
+            m += 1
+            if e2 < 0:
+                continue
+            final_idx[t, j] = e2
+            if kept2[e2] < room[e2]:
+                rank2[t, j] = kept2[e2]
+                kept2[e2] += 1
+    kept = kept1 + kept2
+    offsets = np.concatenate([[0], np.cumsum(kept)[:-1]]).astype(np.int64)
+    dest = np.full((T, k), -1, dtype=np.int64)
+    perm = np.empty(int(kept.sum()), dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if rank1[t, j] >= 0:
+                r = offsets[idx[t, j]] + rank1[t, j]
+            elif rank2[t, j] >= 0:
+                e2 = final_idx[t, j]
+                r = offsets[e2] + kept1[e2] + rank2[t, j]
+            else:
+                continue
+            dest[t, j] = r
+            perm[r] = t
+    # drops[e]: slots that chose e in pass 1 and have no row at the end
+    drops = np.bincount(idx[dest < 0].ravel(), minlength=E).astype(np.int64)
+    return {"counts": d1["counts"], "kept": kept, "offsets": offsets, "dest": dest, "perm": perm,
+            "drops": drops, "C": C, "final_idx": final_idx, "kept1": kept1, "kept2": kept2}
+
+
+def next_choices(s: np.ndarray, k: int) -> np.ndarray:
+    """[T,k]: the (k+1)-th ... (2k)-th ranked experts of each token by score (lower index first
+    on ties); -1 past the E-th."""
+    T, E = s.shape
+    out = np.full((T, k), -1, dtype=np.int64)
+    m = min(2 * k, E) - k
+    if m > 0:
+        out[:, :m] = topk(s, k + m)[:, k:]
+    return out
+
+
+def reweight(p: np.ndarray, final_idx: np.ndarray) -> np.ndarray:
+    """w[t, j] = p[t, final_idx[t, j]] / sum_j' p[t, final_idx[t, j']] (renormalise() on the
+    experts the slots end at)."""
+    return renormalise(p, final_idx)
+
+
+# ---------------------------------------------------------------- routing statistics
+def routing_stats(counts: np.ndarray, p: np.ndarray) -> dict:
+    """Load statistics of one batch, none with an outer coefficient (lambda):
+
+      usage_e    = counts_e / T (slots routed to e before capacity, over the tokens; [A] 2.4)
+      loss_sq    = sum_e usage_e^2                                   ([A] 2.4, standard form)
+      loss_quant = 0.5 Q50(usage) + 0.3 Q90(usage) + 0.2 Q99(usage)  ([A] 2.4, improved form);
+                   Qq over the E experts, linear interpolation between order statistics
+      loss_var   = sum_e (counts_e - mean_e counts)^2                ([M] 3.1)
+      usage_std  = population standard deviation of usage            ([A] 3.6)
+      entropy    = mean over tokens of -sum_e p ln p, 0 ln 0 = 0     ([A] 3.6)"""
+    counts = np.asarray(counts, np.float64)
+    p = np.asarray(p, np.float64)
+    T = p.shape[0]
+    usage = counts / T
+    srt = np.sort(usage)
+    E = len(srt)
+
+    def quantile(q):
+        h = (E - 1) * q
+        lo = int(math.floor(h))
+        hi = min(lo + 1, E - 1)
+        return srt[lo] + (h - lo) * (srt[hi] - srt[lo])
+
+    plogp = np.where(p > 0.0, p * np.log(np.where(p > 0.0, p, 1.0)), 0.0)
+    return {
+        "usage": usage,
+        "loss_sq": float(np.sum(usage ** 2)),
+        "loss_quant": float(0.5 * quantile(0.5) + 0.3 * quantile(0.9) + 0.2 * quantile(0.99)),
+        "loss_var": float(np.sum((counts - counts.mean()) ** 2)),
+        "usage_std": float(np.sqrt(np.mean((usage - usage.mean()) ** 2))),
+        "entropy": float(np.mean(-plogp.sum(axis=1))),
+    }
+
+
 # ---------------------------------------------------------------- whole layer
 def shared_expert(x, shared, act: str = "gelu"):
     """The shared expert ([A] 2.3) on every token; ``shared`` = (W1s, b1s, W2s, b2s) or None."""
@@ -229,23 +360,38 @@ def shared_expert(x, shared, act: str = "gelu"):
     return expert(x, W1s, b1s, W2s, b2s, act)
 
 
+def dispatch_policy(r: dict, E: int, C: int, k: int, policy: str, seed: int) -> tuple[dict, np.ndarray]:
+    """Dispatch under a capacity policy ("token": dispatch(); "random": dispatch_random();
+    "reroute": dispatch_reroute()); returns the dispatch and the combine weights."""
+    if policy == "token":
+        return dispatch(r["idx"], E, C), r["w"]
+    if policy == "random":
+        return dispatch_random(r["idx"], E, C, seed), r["w"]
+    if policy == "reroute":
+        dsp = dispatch_reroute(r["idx"], next_choices(r["s"], k), E, C)
+        return dsp, reweight(r["p"], dsp["final_idx"])
+    raise ValueError(policy)
+
+
 def forward(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=False,
-            seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None) -> dict:
+            seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None, policy="token") -> dict:
     """The layer: route -> dispatch -> gather -> experts -> combine (+ shared expert), plus
-    f, P, L."""
+    f, P, L and the routing statistics."""
     T, d = x.shape
     E = Wg.shape[0]
     r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
     C = capacity(T, E, k, capacity_factor)
-    dsp = dispatch(r["idx"], E, C)
+    dsp, w = dispatch_policy(r, E, C, k, policy, seed)
     x_perm = np.asarray(x, np.float64)[dsp["perm"]]
     y_perm = expert_ffn(x_perm, dsp["kept"], dsp["offsets"], W1, b1, W2, b2, act)
-    y = combine(y_perm, dsp["dest"], r["w"])
+    y = combine(y_perm, dsp["dest"], w)
     ys = shared_expert(x, shared, act)
     if ys is not None:
         y = y + ys
     st = balance_stats(dsp["counts"], r["p"], k)
     out = dict(r)
+    out["w"] = w
+    out["stats"] = routing_stats(dsp["counts"], r["p"])
     out.update(dsp)
     out.update(st)
     out.update({"x_perm": x_perm, "y_perm": y_perm, "y": y})
@@ -253,7 +399,8 @@ def forward(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=Fa
 
 
 def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0,
-                 gumbel=False, seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None) -> dict:
+                 gumbel=False, seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None,
+                 policy="token") -> dict:
     """The layer's output for selected tokens only, at any size.
 
     Routing and dispatch are done for all tokens (they decide which slots survive); each
@@ -263,18 +410,19 @@ def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0
     E = Wg.shape[0]
     r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
     C = capacity(T, E, k, capacity_factor)
-    dsp = dispatch(r["idx"], E, C)
+    dsp, w = dispatch_policy(r, E, C, k, policy, seed)
+    final_idx = dsp.get("final_idx", r["idx"])
     rows = np.asarray(rows, np.int64)
     contrib = np.zeros((len(rows), k, W2.shape[1]), dtype=np.float64)
     for e in range(E):
         sel = [(i, j) for i, t in enumerate(rows) for j in range(k)
-               if r["idx"][t, j] == e and dsp["dest"][t, j] >= 0]
+               if final_idx[t, j] == e and dsp["dest"][t, j] >= 0]
         if not sel:
             continue
         xe = np.asarray(x[[rows[i] for i, _ in sel]], np.float64)
         ye = expert(xe, W1[e], None if b1 is None else b1[e], W2[e], None if b2 is None else b2[e], act)
         for n, (i, j) in enumerate(sel):
-            contrib[i, j] = r["w"][rows[i], j] * ye[n]
+            contrib[i, j] = w[rows[i], j] * ye[n]
     y = np.zeros((len(rows), W2.shape[1]), dtype=np.float64)
     for j in range(k):
         y += contrib[:, j]
@@ -283,6 +431,7 @@ def forward_rows(rows, x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0
         y = y + ys
     st = balance_stats(dsp["counts"], r["p"], k)
     out = dict(r)
+    out["w"] = w
     out.update(dsp)
     out.update(st)
     out["y_rows"] = y

@@ -127,3 +127,13 @@ def gaussian_scalar(seed: int, t: int, e: int, noise_std: float) -> np.float32:
     u1, u2 = (w0 + 0.5) * 2.0 ** -32, (w1 + 0.5) * 2.0 ** -32
     sd = float(np.float32(noise_std))
     return np.float32(sd * math.sqrt(-2.0 * math.log(u1)) * math.cos(2.0 * math.pi * u2))
+
+
+def drop_priority(seed: int, T: int, E: int) -> np.ndarray:
+    """uint32 priority of slot (token t, expert e) for random capacity dropping: word 2 of the
+    Philox block of counter (t, e, 0, 0) (the block the router noise draws words 0 and 1 from)."""
+    k0, k1 = seed_key(seed)
+    t = np.arange(T, dtype=np.uint64)[:, None]
+    e = np.arange(E, dtype=np.uint64)[None, :]
+    _, _, w2, _ = philox4x32_10_np(t, e, 0, 0, k0, k1)
+    return w2
