@@ -156,6 +156,31 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
  */
 typedef enum { MOE_ACT_GELU = 0, MOE_ACT_SILU = 1 } moe_activation;
 
+/* What happens to the slots past an expert's capacity C (mhpn.cn page on MoE architecture,
+ * section 3.3, names dropping at random and rerouting to the next-best expert besides the
+ * first-come order of the kwkr.cn page, sections 2.3 and 3.2). */
+typedef enum {
+  MOE_DROP_TOKEN_ORDER = 0, /* keep the first C slots in token order (the plain layer)        */
+  MOE_DROP_RANDOM = 1,      /* keep the C slots with the smallest (priority, token), priority =
+                               word 2 of the Philox-4x32-10 block of counter (t, e, 0, 0) under
+                               the config's seed (words 0 and 1 feed the router noise); the
+                               kept rows of an expert stay in token order                    */
+  MOE_DROP_REROUTE = 2      /* pass 1 is token order; a token's slots dropped there take, in j
+                               order, its (k+1)-th, (k+2)-th ... ranked experts (by score,
+                               lower index on ties; none past the E-th), and pass 2 fills the
+                               capacity left after pass 1 in slot order (t k + j). An expert's
+                               rows are its pass-1 rows, then its pass-2 rows. A token with a
+                               moved slot has its weights renormalised over the experts its
+                               slots end at: w_j = p_{e_j} / sum_j' p_{e_j'}, computed as
+                               exp(s_j - m) / sum exp(s_j' - m) from the float32 scores.
+                               counts, f, P, L are those of pass 1; kept is final;
+                               aux.topk_idx holds the pass-1 choices, aux.topk_w the final
+                               weights                                                         */
+} moe_drop_policy;
+
+/* Number of floats moe_variant.route_stats receives. */
+#define MOE_ROUTE_STATS 5
+
 typedef struct moe_variant {
   int32_t activation;      /* moe_activation of every expert (routed and shared): GeLU, or
                               SiLU(v) = v sigmoid(v) (aberweb.com page, section 3.2)         */
@@ -174,11 +199,23 @@ typedef struct moe_variant {
   const void* b1s;         /* [shared_d_ffn] dtype, nullable                                  */
   const void* W2s;         /* [d, shared_d_ffn] dtype (required when shared_d_ffn > 0)        */
   const void* b2s;         /* [d] dtype, nullable                                             */
+  int32_t drop_policy;     /* moe_drop_policy                                                 */
+  int32_t reserved;        /* must be 0                                                       */
+  float* route_stats;      /* nullable; else [MOE_ROUTE_STATS] f32 on the device, written by the
+                              layer from the counts before capacity (u_e = counts_e / T) and
+                              the full softmax p, each in float64 rounded once to float32
+                              (aberweb.com page, sections 2.4 and 3.6; mhpn.cn page, 3.1):
+                              [0] sum_e u_e^2; [1] 0.5 Q50 + 0.3 Q90 + 0.2 Q99 of u, Qq by
+                              linear interpolation at position (E-1) q of the sorted u;
+                              [2] sum_e (counts_e - mean counts)^2; [3] population standard
+                              deviation of u; [4] mean over tokens of -sum_e p ln p (0 ln 0 =
+                              0; per-token terms in float32, summed in a fixed order)         */
 } moe_variant;
 
 /* Workspace bytes of moe_forward_ex for `cfg` and `variant` (nullable). Host only.
- * MOE_EINVAL for an unknown activation, a negative or non-finite noise_std, noise_std > 0
- * together with gumbel = 1; MOE_EUNSUPPORTED for a shared_d_ffn the dtype cannot take. */
+ * MOE_EINVAL for an unknown activation or drop policy, a negative or non-finite noise_std,
+ * noise_std > 0 together with gumbel = 1, a nonzero reserved field, or a misaligned
+ * route_stats; MOE_EUNSUPPORTED for a shared_d_ffn the dtype cannot take. */
 moe_status moe_workspace_size_ex(const moe_config* cfg, const moe_variant* variant, size_t* bytes);
 
 /* The layer with the variant's activation, router noise and shared expert; arguments as

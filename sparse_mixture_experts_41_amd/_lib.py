@@ -35,12 +35,15 @@ class MoeForwardAux(ctypes.Structure):
 
 
 MOE_ACT_GELU, MOE_ACT_SILU = 0, 1
+MOE_DROP_TOKEN_ORDER, MOE_DROP_RANDOM, MOE_DROP_REROUTE = 0, 1, 2
+MOE_ROUTE_STATS = 5
 
 
 class MoeVariant(ctypes.Structure):
     _fields_ = [
         ("activation", ctypes.c_int32), ("noise_std", ctypes.c_float), ("shared_d_ffn", ctypes.c_int64),
         ("W1s", ctypes.c_void_p), ("b1s", ctypes.c_void_p), ("W2s", ctypes.c_void_p), ("b2s", ctypes.c_void_p),
+        ("drop_policy", ctypes.c_int32), ("reserved", ctypes.c_int32), ("route_stats", ctypes.c_void_p),
     ]
 
 

@@ -84,6 +84,59 @@ __device__ void write_stats(const int32_t* counts, const float* colsum, int E, i
   }
 }
 
+// Load statistics of the batch from the expert counts (before capacity) and the sum of the
+// tokens' routing entropies (aberweb.com page on MoE misuse, sections 2.4 and 3.6; mhpn.cn
+// page on MoE architecture, section 3.1), in float64, rounded once to float32:
+//   out[0] = sum_e u_e^2 with u_e = counts_e / T
+//   out[1] = 0.5 Q50(u) + 0.3 Q90(u) + 0.2 Q99(u), Qq by linear interpolation between the
+//            order statistics at position (E - 1) q
+//   out[2] = sum_e (counts_e - mean counts)^2
+//   out[3] = population standard deviation of u
+//   out[4] = ent_sum / T (mean routing entropy)
+// Called by every thread of the workgroup; `srt` is LDS scratch of kMaxE doubles.
+__device__ void write_route_stats(const int* tot, int E, int T, float ent_sum, float* out, double* srt) {
+  const int e = threadIdx.x;
+  if (e < E) {                               // rank sort of the counts (ties by index)
+    const int c = tot[e];
+    int rank = 0;
+    for (int j = 0; j < E; ++j) {
+      const int cj = tot[j];
+      rank += (cj < c || (cj == c && j < e)) ? 1 : 0;
+    }
+    srt[rank] = static_cast<double>(c) / static_cast<double>(T);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double dT = static_cast<double>(T), dE = static_cast<double>(E);
+    double sq = 0.0, csum = 0.0, usum = 0.0;
+    for (int j = 0; j < E; ++j) {
+      const double u = static_cast<double>(tot[j]) / dT;
+      sq += u * u;
+      csum += static_cast<double>(tot[j]);
+      usum += u;
+    }
+    const double cmean = csum / dE, umean = usum / dE;
+    double var = 0.0, uvar = 0.0;
+    for (int j = 0; j < E; ++j) {
+      const double dc = static_cast<double>(tot[j]) - cmean;
+      const double du = static_cast<double>(tot[j]) / dT - umean;
+      var += dc * dc;
+      uvar += du * du;
+    }
+    auto quantile = [&](double q) {
+      const double h = (dE - 1.0) * q;
+      const int lo = static_cast<int>(floor(h));
+      const int hi = lo + 1 < E ? lo + 1 : E - 1;
+      return srt[lo] + (h - static_cast<double>(lo)) * (srt[hi] - srt[lo]);
+    };
+    out[0] = static_cast<float>(sq);
+    out[1] = static_cast<float>(0.5 * quantile(0.5) + 0.3 * quantile(0.9) + 0.2 * quantile(0.99));
+    out[2] = static_cast<float>(var);
+    out[3] = static_cast<float>(sqrt(uvar / dE));
+    out[4] = static_cast<float>(static_cast<double>(ent_sum) / dT);
+  }
+}
+
 // Counts, capacity truncation, expert offsets and the per-(group, expert) base ranks, plus the
 // balance statistics when the probability partials are given. One workgroup.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
@@ -139,10 +192,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     }
   }
   __syncthreads();
+  if (a.bases_only) return;                  // uniform over the workgroup
   if (threadIdx.x < kWave) {                 // wave 0: one expert per lane, exclusive scan of kept
     const int ee = threadIdx.x;
     const int c = ee < E ? tot[ee] : 0;
-    const int kp = c < a.C ? c : a.C;
+    const int base = (a.base_kept != nullptr && ee < E) ? a.base_kept[ee] : 0;
+    const int room = a.C - base;
+    const int kp = base + (c < room ? c : room);
     int incl = kp;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -150,7 +206,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       if (ee >= off) incl += n;
     }
     if (ee < E) {
-      a.counts[ee] = c;
+      if (a.counts != nullptr) a.counts[ee] = c;
       a.kept[ee] = kp;
       a.offsets[ee] = incl - kp;
     }
@@ -160,6 +216,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     if (threadIdx.x < E) a.colsum[threadIdx.x] = csum[threadIdx.x];
     write_stats(tot, csum, E, a.k, a.T, a.f, a.P, a.L, prod);
   }
+  if (a.route_stats != nullptr) {
+    __syncthreads();                         // prod is reused below
+    blocked_colsum(a.ent_part, ng, 1, csum, flds);
+    write_route_stats(tot, E, a.T, csum[0], a.route_stats, prod);
+  }
 }
 
 __global__ __launch_bounds__(64) void stats_kernel(const int32_t* __restrict__ counts, const float* __restrict__ colsum,
@@ -168,12 +229,31 @@ __global__ __launch_bounds__(64) void stats_kernel(const int32_t* __restrict__ c
   write_stats(counts, colsum, E, k, T, f, P, L, prod);
 }
 
+// Key of slot (token t, expert e) under random capacity dropping: the slot's priority in the
+// high word, the token in the low word, so keys are unique within an expert and order by
+// (priority, token).
+__device__ __forceinline__ uint64_t drop_key(int t, int e, uint32_t key0, uint32_t key1) {
+  return (static_cast<uint64_t>(drop_priority(static_cast<uint32_t>(t), static_cast<uint32_t>(e), key0, key1)) << 32) |
+         static_cast<uint32_t>(t);
+}
+
+// Whether slot (t, e) survives random dropping: thresh[e] is the largest kept key, all ones
+// when the expert is within capacity (no priority needed then).
+__device__ __forceinline__ bool kept_at_random(int t, int e, const uint64_t* __restrict__ thresh, uint32_t key0,
+                                               uint32_t key1) {
+  const uint64_t th = thresh[e];
+  return th == ~0ull || drop_key(t, e, key0, key1) <= th;
+}
+
 // One wave per 64 tokens: stable ranks by wave ballot within each 16-token group, capacity
-// test, dest and perm.
+// test, dest and perm. RANDOM: only the slots kept by random dropping take part, ranked in
+// token order among themselves (blockbase counts kept slots only).
+template <bool RANDOM>
 __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__ idx,
                                                     const int32_t* __restrict__ blockbase,
                                                     const int32_t* __restrict__ offsets, int T, int E, int k,
-                                                    int C, int32_t* __restrict__ dest,
+                                                    int C, const uint64_t* __restrict__ thresh, uint32_t key0,
+                                                    uint32_t key1, int32_t* __restrict__ dest,
                                                     int32_t* __restrict__ perm) {
   __shared__ uint64_t emask[kMaxE];
   const int lane = lane_id();
@@ -184,10 +264,13 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
   uint64_t sel = 0ull;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
-    ch[j] = 0;
+    ch[j] = -1;
     if (valid && j < k) {
-      ch[j] = idx[static_cast<size_t>(t) * k + j];
-      if (ch[j] >= 0 && ch[j] < E) sel |= 1ull << ch[j];   // out-of-range choices are dropped
+      const int e = idx[static_cast<size_t>(t) * k + j];
+      if (e >= 0 && e < E && (!RANDOM || kept_at_random(t, e, thresh, key0, key1))) {
+        ch[j] = e;                                           // out-of-range or dropped: -1
+        sel |= 1ull << e;
+      }
     }
   }
   for (int e = 0; e < E; ++e) {
@@ -203,7 +286,7 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
       const int e = ch[j];
-      if (e < 0 || e >= E) {
+      if (e < 0) {
         dest[static_cast<size_t>(t) * k + j] = -1;
         continue;
       }
@@ -216,6 +299,273 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
       dest[static_cast<size_t>(t) * k + j] = dst;
     }
   }
+}
+
+// Random dropping, selection: one workgroup per expert finds the C-th smallest key among the
+// expert's slots by radix selection over the 64-bit key, eight bits per pass, most significant
+// first (a pass histograms the next digit of the slots that match the digits fixed so far, then
+// fixes the digit whose bin holds the wanted rank). When the wanted bin holds a single slot, one
+// more pass reads that slot's key. Experts within capacity keep everything: all ones.
+__global__ __launch_bounds__(kScanThreads) void select_random_kernel(const int32_t* __restrict__ idx,
+                                                                     const int32_t* __restrict__ counts, int T,
+                                                                     int k, int C, uint32_t key0, uint32_t key1,
+                                                                     uint64_t* __restrict__ thresh) {
+  __shared__ int bins[256];
+  __shared__ int pick_digit, pick_need, pick_count;
+  __shared__ uint64_t found;
+  const int e = blockIdx.x;
+  if (counts[e] <= C) {
+    if (threadIdx.x == 0) thresh[e] = ~0ull;
+    return;
+  }
+  uint64_t prefix = 0ull;                    // the digits fixed so far, in place
+  int need = C;                              // wanted rank (1-based) among the matching slots
+  int shift = 64;
+  bool unique = false;
+  while (shift > 0) {
+    shift -= 8;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) bins[i] = 0;
+    __syncthreads();
+    const int hs = shift + 8;                // bits at and above hs are fixed (none when 64)
+    for (int t = threadIdx.x; t < T; t += blockDim.x) {
+      bool mine = false;
+      for (int j = 0; j < k; ++j) mine |= idx[static_cast<size_t>(t) * k + j] == e;
+      if (!mine) continue;
+      const uint64_t key = drop_key(t, e, key0, key1);
+      if (hs < 64 && (key >> hs) != (prefix >> hs)) continue;
+      atomicAdd(&bins[(key >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) {               // wave 0: four bins per lane, prefix over lanes
+      const int l = threadIdx.x;
+      int b4[4], loc = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        b4[u] = bins[4 * l + u];
+        loc += b4[u];
+      }
+      int incl = loc;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int n = __shfl_up(incl, off);
+        if (l >= off) incl += n;
+      }
+      int run = incl - loc;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (run < need && run + b4[u] >= need) {
+          pick_digit = 4 * l + u;
+          pick_need = need - run;
+          pick_count = b4[u];
+        }
+        run += b4[u];
+      }
+    }
+    __syncthreads();
+    prefix |= static_cast<uint64_t>(pick_digit) << shift;
+    need = pick_need;
+    const int cnt = pick_count;
+    __syncthreads();                         // pick_* and bins are rewritten by the next pass
+    if (cnt == 1 && shift > 0) {
+      unique = true;
+      break;
+    }
+  }
+  if (unique) {                              // the one slot that matches the fixed digits
+    for (int t = threadIdx.x; t < T; t += blockDim.x) {
+      bool mine = false;
+      for (int j = 0; j < k; ++j) mine |= idx[static_cast<size_t>(t) * k + j] == e;
+      if (!mine) continue;
+      const uint64_t key = drop_key(t, e, key0, key1);
+      if ((key >> shift) == (prefix >> shift)) found = key;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) thresh[e] = found;
+  } else if (threadIdx.x == 0) {
+    thresh[e] = prefix;
+  }
+}
+
+// Random dropping: per-group histogram of the surviving slots. One wave per 64 tokens.
+__global__ __launch_bounds__(64) void kept_histogram_kernel(const int32_t* __restrict__ idx,
+                                                            const uint64_t* __restrict__ thresh, int T, int E, int k,
+                                                            uint32_t key0, uint32_t key1,
+                                                            int32_t* __restrict__ hist) {
+  constexpr int NG = kBlockTokens / kGroupTokens;
+  const int lane = lane_id();
+  const int t = blockIdx.x * kBlockTokens + lane;
+  const int ng = (T + kGroupTokens - 1) / kGroupTokens;
+  const int grp0 = blockIdx.x * NG;
+  uint64_t sel = 0ull;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[static_cast<size_t>(t) * k + j];
+      if (e >= 0 && e < E && kept_at_random(t, e, thresh, key0, key1)) sel |= 1ull << e;
+    }
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(static_cast<int>((sel >> e) & 1ull));
+    if (lane < NG && grp0 + lane < ng)
+      hist[static_cast<size_t>(grp0 + lane) * E + e] = __popcll((b >> (kGroupTokens * lane)) & 0xFFFFull);
+  }
+}
+
+// Rerouting, first half. One wave per 64 tokens. Pass-1 rank of each slot as in the token-order
+// dispatch; a token's slots past capacity take, in j order, its next-ranked experts
+// idx_next[t, 0], idx_next[t, 1], ...: cand[t, j] = that expert, or -1 (kept in pass 1, or no
+// next expert). A token's candidates go to distinct experts, so per-group ballots rank them in
+// slot order; hist2 is their per-group histogram.
+__global__ __launch_bounds__(64) void reroute_rank_kernel(const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ idx_next,
+                                                          const int32_t* __restrict__ blockbase1, int T, int E,
+                                                          int k, int C, int32_t* __restrict__ cand,
+                                                          int32_t* __restrict__ hist2) {
+  constexpr int NG = kBlockTokens / kGroupTokens;
+  __shared__ uint64_t emask[kMaxE];
+  const int lane = lane_id();
+  const int t = blockIdx.x * kBlockTokens + lane;
+  const bool valid = t < T;
+  const int ng = (T + kGroupTokens - 1) / kGroupTokens;
+  const int grp0 = blockIdx.x * NG;
+  int ch[kMaxK];
+  uint64_t sel = 0ull;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    ch[j] = -1;
+    if (valid && j < k) {
+      const int e = idx[static_cast<size_t>(t) * k + j];
+      if (e >= 0 && e < E) {
+        ch[j] = e;
+        sel |= 1ull << e;
+      }
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(static_cast<int>((sel >> e) & 1ull));
+    if (lane == 0) emask[e] = b;
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t gmask = 0xFFFFull << (lane & ~(kGroupTokens - 1));
+  const int grp = t / kGroupTokens;
+  uint64_t csel = 0ull;
+  int m = 0;                                 // the token's dropped slots so far
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (valid && j < k) {
+      const int e = ch[j];
+      int c = -1;
+      if (e >= 0) {
+        const int r = blockbase1[static_cast<size_t>(grp) * E + e] + __popcll(emask[e] & below & gmask);
+        if (r >= C) {
+          const int e2 = idx_next[static_cast<size_t>(t) * k + m];
+          ++m;
+          if (e2 >= 0 && e2 < E) {
+            c = e2;
+            csel |= 1ull << e2;
+          }
+        }
+      }
+      cand[static_cast<size_t>(t) * k + j] = c;
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(static_cast<int>((csel >> e) & 1ull));
+    if (lane < NG && grp0 + lane < ng)
+      hist2[static_cast<size_t>(grp0 + lane) * E + e] = __popcll((b >> (kGroupTokens * lane)) & 0xFFFFull);
+  }
+}
+
+// Rerouting, second half. One wave per 64 tokens. Slots kept in pass 1 take row offsets[e] +
+// rank1 (the first kept1[e] rows of the segment); candidates take offsets[e2] + kept1[e2] +
+// rank2 while rank2 < C - kept1[e2], else are dropped. A token with a candidate gets its weights
+// renormalised over the experts its slots end at, from the float32 scores s:
+// w_j = exp(s_j - m) / sum_j' exp(s_j' - m), m the largest of those scores (equal to the ratio of
+// the softmax probabilities, whose common denominator cancels).
+__global__ __launch_bounds__(64) void permute_reroute_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ cand, const int32_t* __restrict__ blockbase1,
+    const int32_t* __restrict__ blockbase2, const int32_t* __restrict__ kept1, const int32_t* __restrict__ offsets,
+    const float* __restrict__ s, int T, int E, int k, int C, int32_t* __restrict__ dest, int32_t* __restrict__ perm,
+    float* __restrict__ w) {
+  __shared__ uint64_t emask[kMaxE], emask2[kMaxE];
+  const int lane = lane_id();
+  const int t = blockIdx.x * kBlockTokens + lane;
+  const bool valid = t < T;
+  int ch[kMaxK], cd[kMaxK];
+  uint64_t sel = 0ull, csel = 0ull;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    ch[j] = -1;
+    cd[j] = -1;
+    if (valid && j < k) {
+      const int e = idx[static_cast<size_t>(t) * k + j];
+      if (e >= 0 && e < E) {
+        ch[j] = e;
+        sel |= 1ull << e;
+      }
+      const int c = cand[static_cast<size_t>(t) * k + j];
+      if (c >= 0 && c < E) {
+        cd[j] = c;
+        csel |= 1ull << c;
+      }
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    const uint64_t b = __ballot(static_cast<int>((sel >> e) & 1ull));
+    const uint64_t b2 = __ballot(static_cast<int>((csel >> e) & 1ull));
+    if (lane == 0) {
+      emask[e] = b;
+      emask2[e] = b2;
+    }
+  }
+  __syncthreads();
+  if (!valid) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const uint64_t gmask = 0xFFFFull << (lane & ~(kGroupTokens - 1));
+  const int grp = t / kGroupTokens;
+  bool moved = false;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      int dst = -1;
+      if (cd[j] >= 0) {
+        const int e2 = cd[j];
+        moved = true;
+        const int r2 = blockbase2[static_cast<size_t>(grp) * E + e2] + __popcll(emask2[e2] & below & gmask);
+        const int k1 = kept1[e2];
+        if (r2 < C - k1) dst = offsets[e2] + k1 + r2;
+      } else if (ch[j] >= 0) {
+        const int e = ch[j];
+        const int r = blockbase1[static_cast<size_t>(grp) * E + e] + __popcll(emask[e] & below & gmask);
+        if (r < C) dst = offsets[e] + r;
+      }
+      if (dst >= 0) perm[dst] = t;
+      dest[static_cast<size_t>(t) * k + j] = dst;
+    }
+  }
+  if (!moved) return;
+  const float* srow = s + static_cast<size_t>(t) * E;
+  float sv[kMaxK];
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    sv[j] = 0.0f;
+    if (j < k) {
+      const int e = cd[j] >= 0 ? cd[j] : ch[j];
+      sv[j] = e >= 0 ? srow[e] : -INFINITY;
+      m = fmaxf(m, sv[j]);
+    }
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j < k) {
+      sv[j] = expf(sv[j] - m);
+      sum += sv[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) w[static_cast<size_t>(t) * k + j] = sv[j] / sum;
 }
 
 // x_perm[r] = x[perm[r]] for r < sum(kept), 16-byte vectors; one row per workgroup iteration.
@@ -254,8 +604,49 @@ hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k
 hipError_t launch_permute(const int32_t* idx, const int32_t* blockbase, const int32_t* offsets, int T, int E,
                           int k, int C, int32_t* dest, int32_t* perm, hipStream_t stream) {
   const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
-  hipLaunchKernelGGL(permute_kernel, dim3(nblk), dim3(64), 0, stream, idx, blockbase, offsets, T, E, k, C, dest,
-                     perm);
+  hipLaunchKernelGGL(permute_kernel<false>, dim3(nblk), dim3(64), 0, stream, idx, blockbase, offsets, T, E, k, C,
+                     nullptr, 0u, 0u, dest, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_random(const int32_t* idx, const int32_t* counts, int T, int E, int k, int C, uint32_t key0,
+                                uint32_t key1, uint64_t* thresh, hipStream_t stream) {
+  hipLaunchKernelGGL(select_random_kernel, dim3(E), dim3(kScanThreads), 0, stream, idx, counts, T, k, C, key0, key1,
+                     thresh);
+  return hipGetLastError();
+}
+
+hipError_t launch_histogram_kept(const int32_t* idx, const uint64_t* thresh, int T, int E, int k, uint32_t key0,
+                                 uint32_t key1, int32_t* hist, hipStream_t stream) {
+  const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
+  hipLaunchKernelGGL(kept_histogram_kernel, dim3(nblk), dim3(64), 0, stream, idx, thresh, T, E, k, key0, key1, hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_kept(const int32_t* idx, const uint64_t* thresh, const int32_t* blockbase,
+                               const int32_t* offsets, int T, int E, int k, uint32_t key0, uint32_t key1,
+                               int32_t* dest, int32_t* perm, hipStream_t stream) {
+  const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
+  hipLaunchKernelGGL(permute_kernel<true>, dim3(nblk), dim3(64), 0, stream, idx, blockbase, offsets, T, E, k, T,
+                     thresh, key0, key1, dest, perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_reroute_rank(const int32_t* idx, const int32_t* idx_next, const int32_t* blockbase1, int T, int E,
+                               int k, int C, int32_t* cand, int32_t* hist2, hipStream_t stream) {
+  const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
+  hipLaunchKernelGGL(reroute_rank_kernel, dim3(nblk), dim3(64), 0, stream, idx, idx_next, blockbase1, T, E, k, C,
+                     cand, hist2);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_reroute(const int32_t* idx, const int32_t* cand, const int32_t* blockbase1,
+                                  const int32_t* blockbase2, const int32_t* kept1, const int32_t* offsets,
+                                  const float* s, int T, int E, int k, int C, int32_t* dest, int32_t* perm, float* w,
+                                  hipStream_t stream) {
+  const int nblk = (T + kBlockTokens - 1) / kBlockTokens;
+  hipLaunchKernelGGL(permute_reroute_kernel, dim3(nblk), dim3(64), 0, stream, idx, cand, blockbase1, blockbase2,
+                     kept1, offsets, s, T, E, k, C, dest, perm, w);
   return hipGetLastError();
 }
 

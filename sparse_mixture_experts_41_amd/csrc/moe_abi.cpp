@@ -31,12 +31,14 @@ struct Derived {
   float noise_std;  // Gaussian only
   int act;          // moe::kActGelu / kActSilu
   int dffs;         // shared expert hidden width, 0 = none
+  int policy;       // MOE_DROP_*
+  bool stats;       // routing statistics requested
   uint32_t key0, key1;
 };
 
 struct Layout {
   size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
-      y_perm2, Hs, ys, total;
+      y_perm2, Hs, ys, ent, idx_next, cand, hist2, blockbase2, kept1, thresh, total;
 };
 
 // C = ceil(c*k*T/E) for the exact value of the double c = m * 2^sh (m a 53-bit integer).
@@ -97,6 +99,8 @@ moe_status check_config(const moe_config* cfg, Derived* D) {
   D->noise_std = 0.0f;
   D->act = moe::kActGelu;
   D->dffs = 0;
+  D->policy = MOE_DROP_TOKEN_ORDER;
+  D->stats = false;
   D->key0 = static_cast<uint32_t>(cfg->seed & 0xffffffffull);
   D->key1 = static_cast<uint32_t>(cfg->seed >> 32);
   return MOE_OK;
@@ -123,6 +127,13 @@ moe_status check_variant(const moe_variant* v, Derived* D) {
     D->noise_std = v->noise_std;
   }
   D->dffs = static_cast<int>(v->shared_d_ffn);
+  if (v->drop_policy != MOE_DROP_TOKEN_ORDER && v->drop_policy != MOE_DROP_RANDOM && v->drop_policy != MOE_DROP_REROUTE)
+    return fail(MOE_EINVAL, "unknown drop_policy");
+  if (v->reserved != 0) return fail(MOE_EINVAL, "variant reserved must be 0");
+  if (v->route_stats != nullptr && (reinterpret_cast<uintptr_t>(v->route_stats) & 3u) != 0)
+    return fail(MOE_EINVAL, "route_stats is not 4-byte aligned");
+  D->policy = v->drop_policy;
+  D->stats = v->route_stats != nullptr;
   return MOE_OK;
 }
 
@@ -154,6 +165,14 @@ Layout layout_of(const Derived& D) {
   L.y_perm2 = take(D.bf16 ? R * static_cast<size_t>(D.d) * 4 : 0);
   L.Hs = take(D.dffs > 0 ? T * static_cast<size_t>(D.dffs) * D.esize : 0);
   L.ys = take(D.dffs > 0 ? T * static_cast<size_t>(D.d) * 4 : 0);
+  const bool random = D.policy == MOE_DROP_RANDOM, reroute = D.policy == MOE_DROP_REROUTE;
+  L.ent = take(D.stats ? ng * 4 : 0);
+  L.idx_next = take(reroute ? T * k * 4 : 0);
+  L.cand = take(reroute ? T * k * 4 : 0);
+  L.hist2 = take(random || reroute ? ng * E * 4 : 0);
+  L.blockbase2 = take(random || reroute ? ng * E * 4 : 0);
+  L.kept1 = take(reroute ? E * 4 : 0);
+  L.thresh = take(random ? E * 8 : 0);
   L.total = off;
   return L;
 }
@@ -428,8 +447,15 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   const int C = static_cast<int>(D.C < D.T ? D.C : D.T);
 
   if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
-  // 1-2. router: logits, scores, softmax, top-k, weights, block partials
-  const moe::RouterArgs ra = router_args(D, x, Wg, bg, logits, scores, idx, w, probsum, hist);
+  const bool reroute = D.policy == MOE_DROP_REROUTE;
+  float* ent = D.stats ? at<float>(ws, Lw.ent) : nullptr;
+  int32_t* idx_next = reroute ? at<int32_t>(ws, Lw.idx_next) : nullptr;
+  int32_t* kept1 = reroute ? at<int32_t>(ws, Lw.kept1) : kept;
+  // 1-2. router: logits, scores, softmax, top-k, weights, block partials (and the next-ranked
+  // experts for rerouting, the entropy partials for the statistics)
+  moe::RouterArgs ra = router_args(D, x, Wg, bg, logits, scores, idx, w, probsum, hist);
+  ra.ent_part = ent;
+  ra.idx_next = idx_next;
   MOE_HIP(moe::launch_router(ra, at<float>(ws, Lw.zpart), st), "router");
   if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
   // 3a. counts, capacity, offsets, block bases; f, P, L
@@ -441,7 +467,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   s.T = D.T;
   s.C = C;
   s.counts = counts;
-  s.kept = kept;
+  s.kept = kept1;
   s.offsets = offsets;
   s.blockbase = blockbase;
   s.probsum_part = probsum;
@@ -449,15 +475,52 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   s.f = f;
   s.P = P;
   s.L = L;
+  s.ent_part = ent;
+  s.route_stats = D.stats ? variant->route_stats : nullptr;
   MOE_HIP(moe::launch_scan(s, st), "scan");
   if (ev) MOE_HIP(hipEventRecord(ev[2], st), "event");
+  // 3a'. capacity policies: the rows the surviving slots take (second scan over them)
+  int32_t* hist2 = at<int32_t>(ws, Lw.hist2);
+  int32_t* blockbase2 = at<int32_t>(ws, Lw.blockbase2);
+  moe::ScanArgs s2{};
+  s2.hist = hist2;
+  s2.ng = D.ng;
+  s2.E = D.E;
+  s2.k = D.k;
+  s2.T = D.T;
+  s2.C = C;
+  s2.blockbase = blockbase2;
+  if (D.policy == MOE_DROP_RANDOM) {
+    uint64_t* thresh = at<uint64_t>(ws, Lw.thresh);
+    MOE_HIP(moe::launch_select_random(idx, counts, D.T, D.E, D.k, C, D.key0, D.key1, thresh, st), "select_random");
+    MOE_HIP(moe::launch_histogram_kept(idx, thresh, D.T, D.E, D.k, D.key0, D.key1, hist2, st), "histogram_kept");
+    s2.bases_only = 1;
+    MOE_HIP(moe::launch_scan(s2, st), "scan_kept");
+  } else if (reroute) {
+    int32_t* cand = at<int32_t>(ws, Lw.cand);
+    MOE_HIP(moe::launch_reroute_rank(idx, idx_next, blockbase, D.T, D.E, D.k, C, cand, hist2, st), "reroute_rank");
+    s2.base_kept = kept1;
+    s2.kept = kept;
+    s2.offsets = offsets;
+    MOE_HIP(moe::launch_scan(s2, st), "scan_reroute");
+  }
   // 3b. stable permutation with the drop mask, then the row gather (unless GEMM1 reads the
   // token rows through the permutation itself)
   moe::FfnArgs fa{};
   fa.x = x;
   fa.T = D.T;
   fa.rows = nullptr;
-  MOE_HIP(moe::launch_permute(idx, blockbase, offsets, D.T, D.E, D.k, C, dest, perm, st), "permute");
+  if (D.policy == MOE_DROP_RANDOM) {
+    MOE_HIP(moe::launch_permute_kept(idx, at<uint64_t>(ws, Lw.thresh), blockbase2, offsets, D.T, D.E, D.k, D.key0,
+                                     D.key1, dest, perm, st),
+            "permute_kept");
+  } else if (reroute) {
+    MOE_HIP(moe::launch_permute_reroute(idx, at<int32_t>(ws, Lw.cand), blockbase, blockbase2, kept1, offsets,
+                                        scores != nullptr ? scores : logits, D.T, D.E, D.k, C, dest, perm, w, st),
+            "permute_reroute");
+  } else {
+    MOE_HIP(moe::launch_permute(idx, blockbase, offsets, D.T, D.E, D.k, C, dest, perm, st), "permute");
+  }
   // 4. experts
   fa.x_perm = x_perm;
   fa.kept = kept;

@@ -36,10 +36,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
-// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): words 0 and 1 of the block for counter
+// Philox-4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): words 0-2 of the block for counter
 // (c0, c1, 0, 0) and key (k0, k1).
-__device__ __forceinline__ void philox_words01(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1, uint32_t& w0,
-                                               uint32_t& w1) {
+__device__ __forceinline__ void philox_words012(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1, uint32_t& w0,
+                                                uint32_t& w1, uint32_t& w2) {
   uint32_t x0 = c0, x1 = c1, x2 = 0u, x3 = 0u;
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
@@ -58,12 +58,26 @@ __device__ __forceinline__ void philox_words01(uint32_t c0, uint32_t c1, uint32_
   }
   w0 = x0;
   w1 = x1;
+  w2 = x2;
+}
+
+__device__ __forceinline__ void philox_words01(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1, uint32_t& w0,
+                                               uint32_t& w1) {
+  uint32_t w2;
+  philox_words012(c0, c1, k0, k1, w0, w1, w2);
 }
 
 __device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
   uint32_t w0, w1;
   philox_words01(c0, c1, k0, k1, w0, w1);
   return w0;
+}
+
+// Priority of slot (token t, expert e) for random capacity dropping: word 2 of the block above.
+__device__ __forceinline__ uint32_t drop_priority(uint32_t t, uint32_t e, uint32_t k0, uint32_t k1) {
+  uint32_t w0, w1, w2;
+  philox_words012(t, e, k0, k1, w0, w1, w2);
+  return w2;
 }
 
 // Gumbel(0,1) noise for (token t, expert e): u = (w0 + 1/2) 2^-32 in float64, strictly inside

@@ -27,6 +27,8 @@ struct RouterArgs {
   float* probsum_part;    // [ng,E], ng = ceil(T/16) token groups
   int32_t* hist;          // [ng,E]
   int ng;
+  float* ent_part;        // [ng] or null: per-group sums of the token entropies -sum_e p ln p
+  int32_t* idx_next;      // [T,k] or null: the (k+1)-th ... (2k)-th ranked experts (-1 past E)
 };
 // K slices of the bf16 router (1 = one fused kernel); zpart needs slices * T * E floats when
 // slices > 1 (unused otherwise and for float32).
@@ -53,8 +55,38 @@ struct ScanArgs {
   float* f;               // [E]
   float* P;               // [E]
   float* L;               // [1]
+  // second pass of a capacity policy: base_kept [E] slots already kept per expert, so the
+  // capacity left is C - base_kept; kept = base_kept + min(new, C - base_kept); counts may be null
+  const int32_t* base_kept;
+  int bases_only;         // 1: write blockbase only (counts, kept, offsets, statistics untouched)
+  // routing statistics (both null or both set): ent_part [ng] -> route_stats [MOE_ROUTE_STATS]
+  const float* ent_part;
+  float* route_stats;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+
+// Random capacity dropping: thresh[e] = the largest kept key (priority << 32 | token) of expert
+// e (all ones when within capacity); a slot is kept iff its key <= thresh[its expert].
+hipError_t launch_select_random(const int32_t* idx, const int32_t* counts, int T, int E, int k, int C, uint32_t key0,
+                                uint32_t key1, uint64_t* thresh, hipStream_t stream);
+// Per-group histogram of the kept slots (keys <= thresh).
+hipError_t launch_histogram_kept(const int32_t* idx, const uint64_t* thresh, int T, int E, int k, uint32_t key0,
+                                 uint32_t key1, int32_t* hist, hipStream_t stream);
+// permute for random dropping: only kept slots get rows, ranked by token order among them.
+hipError_t launch_permute_kept(const int32_t* idx, const uint64_t* thresh, const int32_t* blockbase,
+                               const int32_t* offsets, int T, int E, int k, uint32_t key0, uint32_t key1,
+                               int32_t* dest, int32_t* perm, hipStream_t stream);
+// Rerouting, first half: pass-1 ranks from blockbase1; the token's dropped slots take its next
+// experts idx_next [T,k] in j order -> cand [T,k] (-1 = none) and their group histogram hist2.
+hipError_t launch_reroute_rank(const int32_t* idx, const int32_t* idx_next, const int32_t* blockbase1, int T, int E,
+                               int k, int C, int32_t* cand, int32_t* hist2, hipStream_t stream);
+// Rerouting, second half: final dest and perm (pass-1 rows, then pass-2 rows of each expert),
+// and the weights of tokens with a moved slot renormalised over their final experts from the
+// scores s [T,E].
+hipError_t launch_permute_reroute(const int32_t* idx, const int32_t* cand, const int32_t* blockbase1,
+                                  const int32_t* blockbase2, const int32_t* kept1, const int32_t* offsets,
+                                  const float* s, int T, int E, int k, int C, int32_t* dest, int32_t* perm, float* w,
+                                  hipStream_t stream);
 
 hipError_t launch_permute(const int32_t* idx, const int32_t* blockbase, const int32_t* offsets,
                           int T, int E, int k, int C, int32_t* dest, int32_t* perm, hipStream_t stream);

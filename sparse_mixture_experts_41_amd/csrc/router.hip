@@ -33,11 +33,12 @@ template <int BT>
 __device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
                                    float noise_std, uint32_t key0, uint32_t key1, float* __restrict__ logits,
                                    float* __restrict__ scores, int32_t* __restrict__ idx_out,
-                                   float* __restrict__ w_out) {
+                                   float* __restrict__ w_out, int32_t* __restrict__ next_out, float& entropy) {
   const int lane = lane_id();
   const size_t base = static_cast<size_t>(t0) * E;
   for (int i = lane; i < nt * E; i += kWave) logits[base + i] = rows[(i / E) * ldr + i % E];
   const bool valid = lane < nt;                    // nt <= BT
+  entropy = 0.0f;
   float* row = rows + (lane < BT ? lane : 0) * ldr;
   if (valid && (noise != kNoiseNone || tau != 1.0f)) {
     const int t = t0 + lane;
@@ -59,24 +60,27 @@ __device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, 
     return 0ull;
   }
   // top-k on the scores: strict '>' keeps the lowest index among equal values (and -0 == +0);
-  // branch-free scans so the LDS reads of a row pipeline
-  uint64_t sel = 0ull;
-  int idx[kMaxK];
+  // branch-free scans so the LDS reads of a row pipeline. With next_out, up to k more
+  // selections give the next-ranked experts (for rerouting).
+  const int jmax = next_out != nullptr ? min(2 * k, E) : k;
+  uint64_t sel = 0ull, used = 0ull;
+  int idx[2 * kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    idx[j] = 0;
-    if (j < k) {
+  for (int j = 0; j < 2 * kMaxK; ++j) {
+    idx[j] = -1;
+    if (j < jmax) {
       int best = -1;
       float bv = 0.0f;
 #pragma unroll 8
       for (int e = 0; e < E; ++e) {
         const float v = row[e];
-        const bool take = !((sel >> e) & 1ull) && (best < 0 || v > bv);
+        const bool take = !((used >> e) & 1ull) && (best < 0 || v > bv);
         best = take ? e : best;
         bv = take ? v : bv;
       }
       idx[j] = best;
-      sel |= 1ull << best;
+      used |= 1ull << best;
+      if (j < k) sel |= 1ull << best;
     }
   }
   // softmax of the scores (float32; the max is the first chosen score)
@@ -88,8 +92,14 @@ __device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, 
     row[e] = ex;
     sum += ex;
   }
+  float h = 0.0f;
 #pragma unroll 8
-  for (int e = 0; e < E; ++e) row[e] = row[e] / sum;
+  for (int e = 0; e < E; ++e) {
+    const float pe = row[e] / sum;
+    row[e] = pe;
+    h -= pe > 0.0f ? pe * logf(pe) : 0.0f;
+  }
+  entropy = h;
   float psel = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
@@ -100,6 +110,7 @@ __device__ uint64_t group_epilogue(float* rows, int ldr, int t0, int nt, int E, 
     if (j < k) {
       idx_out[koff + j] = idx[j];
       w_out[koff + j] = row[idx[j]] / psel;
+      if (next_out != nullptr) next_out[koff + j] = idx[k + j];
     }
   }
   return sel;
@@ -140,7 +151,7 @@ __device__ __forceinline__ void group_partials(const float* rows, int ldr, uint6
 __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
                                   float noise_std, uint32_t key0, uint32_t key1, float* __restrict__ logits,
                                   float* __restrict__ scores, int32_t* __restrict__ idx_out,
-                                  float* __restrict__ w_out) {
+                                  float* __restrict__ w_out, int32_t* __restrict__ next_out, float& entropy) {
   const int lane = lane_id();
   const size_t base = static_cast<size_t>(t0) * E;
   for (int r = 0; r < nt; ++r)               // E <= 64: one coalesced row per step
@@ -165,21 +176,25 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
     for (int r = 0; r < nt; ++r)
       if (lane < E) scores[base + static_cast<size_t>(r) * E + lane] = rows[r * ldr + lane];
   __syncthreads();
+  entropy = 0.0f;
   if (!valid) {
     for (int e = e0; e < e1; ++e) row[e] = 0.0f;
     return 0ull;
   }
-  uint64_t sel = 0ull;
-  int idx[kMaxK];
+  // selections in score order: the first k are the choices; with next_out, up to k more (the
+  // next-ranked experts, for rerouting)
+  const int jmax = next_out != nullptr ? min(2 * k, E) : k;
+  uint64_t sel = 0ull, used = 0ull;
+  int idx[2 * kMaxK];
 #pragma unroll
-  for (int j = 0; j < kMaxK; ++j) {
-    idx[j] = 0;
-    if (j < k) {
+  for (int j = 0; j < 2 * kMaxK; ++j) {
+    idx[j] = -1;
+    if (j < jmax) {
       int best = -1;
       float bv = 0.0f;
       for (int e = e0; e < e1; ++e) {
         const float v = row[e];
-        const bool take = !((sel >> e) & 1ull) && (best < 0 || v > bv);
+        const bool take = !((used >> e) & 1ull) && (best < 0 || v > bv);
         best = take ? e : best;
         bv = take ? v : bv;
       }
@@ -193,7 +208,8 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
         bv = take ? ov : bv;
       }
       idx[j] = best;
-      sel |= 1ull << best;
+      used |= 1ull << best;
+      if (j < k) sel |= 1ull << best;
     }
   }
   const float mx = row[idx[0]];
@@ -206,7 +222,15 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
   sum += __shfl_xor(sum, 1);
   sum += __shfl_xor(sum, 2);
   const float inv = 1.0f / sum;
-  for (int e = e0; e < e1; ++e) row[e] = row[e] * inv;
+  float h = 0.0f;                            // -sum p ln p over this lane's experts (0 ln 0 = 0)
+  for (int e = e0; e < e1; ++e) {
+    const float pe = row[e] * inv;
+    row[e] = pe;
+    h -= pe > 0.0f ? pe * __logf(pe) : 0.0f;
+  }
+  h += __shfl_xor(h, 1);
+  h += __shfl_xor(h, 2);
+  entropy = h;
   __syncthreads();
   float psel = 0.0f;
 #pragma unroll
@@ -219,6 +243,7 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
       if (j < k) {
         idx_out[koff + j] = idx[j];
         w_out[koff + j] = row[idx[j]] / psel;
+        if (next_out != nullptr) next_out[koff + j] = idx[k + j];
       }
     }
   }
@@ -230,9 +255,22 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
 __device__ void group_finish(const RouterArgs& a, float* rows, int LDE, int t0, int nt_tok, int grp) {
   const int lane = lane_id();
   const int E = a.E;
-  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.noise, a.noise_std, a.key0, a.key1, a.logits,
-                                     a.scores, a.idx, a.w);
+  float ent;
+  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.noise, a.noise_std, a.key0, a.key1,
+                                     a.logits, a.scores, a.idx, a.w, a.idx_next, ent);
   __syncthreads();
+  if (a.ent_part != nullptr) {               // the group's entropy sum, tokens in order
+    __shared__ float ents[kWaves][kGroupTokens];
+    float* en = ents[threadIdx.x >> 6];
+    if ((lane & 3) == 0) en[lane >> 2] = ent;   // zero for tokens past nt_tok
+    __syncthreads();
+    if (lane == 0) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int t = 0; t < kGroupTokens; ++t) sum += en[t];
+      a.ent_part[grp] = sum;
+    }
+  }
   // group partials: column sums of p over the 16 rows (ascending), and the histogram, whose bits
   // come from lane 4 t of each token (the popcount of the whole ballot)
   const size_t gofs = static_cast<size_t>(grp) * E;
@@ -419,11 +457,22 @@ __global__ __launch_bounds__(64) void router_f32_kernel(RouterArgs a) {
     }
   }
   __syncthreads();
-  const uint64_t sel = group_epilogue<kBlockTokens>(rows, LDR, t0, nt, a.E, a.k, a.tau, a.noise, a.noise_std, a.key0, a.key1,
-                                                    a.logits, a.scores, a.idx, a.w);
+  float ent;
+  const uint64_t sel = group_epilogue<kBlockTokens>(rows, LDR, t0, nt, a.E, a.k, a.tau, a.noise, a.noise_std, a.key0,
+                                                    a.key1, a.logits, a.scores, a.idx, a.w, a.idx_next, ent);
   __syncthreads();
-  group_partials<kBlockTokens>(rows, LDR, sel, blk * (kBlockTokens / kGroupTokens), a.ng, a.E, a.probsum_part,
-                               a.hist);
+  const int grp0 = blk * (kBlockTokens / kGroupTokens);
+  group_partials<kBlockTokens>(rows, LDR, sel, grp0, a.ng, a.E, a.probsum_part, a.hist);
+  if (a.ent_part != nullptr) {               // per-group entropy sums, tokens in order
+    __shared__ float ents[kBlockTokens];
+    ents[lane] = ent;                         // zero past nt
+    __syncthreads();
+    if (lane < kBlockTokens / kGroupTokens && grp0 + lane < a.ng) {
+      float sum = 0.0f;
+      for (int t = 0; t < kGroupTokens; ++t) sum += ents[lane * kGroupTokens + t];
+      a.ent_part[grp0 + lane] = sum;
+    }
+  }
 }
 
 // Per-group expert histogram of given top-k indices: one wave per 64 tokens, four groups.

@@ -15,7 +15,7 @@ from ._lib import MOE_FORWARD_STAGES, STAGE_NAMES, MoeConfig, MoeForwardAux, mak
 
 __all__ = ["make_config", "capacity", "workspace_size", "workspace", "route", "dispatch", "expert_ffn", "combine",
            "forward", "ForwardPlan", "StageEvents", "STAGE_NAMES", "MoeConfig", "make_variant", "workspace_size_ex",
-           "temperature_at"]
+           "temperature_at", "DROP_POLICIES", "ROUTE_STAT_NAMES"]
 
 
 def _storage_dtype(cfg: MoeConfig) -> torch.dtype:
@@ -199,15 +199,23 @@ class StageEvents:
                 self.array[i] = None
 
 
-def make_variant(cfg: MoeConfig, activation: str = "gelu", noise_std: float = 0.0, shared=None):
-    """A moe_variant: expert activation ("gelu" or "silu"), Gaussian router noise std, and an
-    optional shared expert ``shared = (W1s [ds,d], b1s [ds] or None, W2s [d,ds], b2s [d] or None)``.
+DROP_POLICIES = {"token": _lib.MOE_DROP_TOKEN_ORDER, "random": _lib.MOE_DROP_RANDOM, "reroute": _lib.MOE_DROP_REROUTE}
+ROUTE_STAT_NAMES = ("loss_sq", "loss_quant", "loss_var", "usage_std", "entropy")
+
+
+def make_variant(cfg: MoeConfig, activation: str = "gelu", noise_std: float = 0.0, shared=None,
+                 drop_policy: str = "token", route_stats=None):
+    """A moe_variant: expert activation ("gelu" or "silu"), Gaussian router noise std, an
+    optional shared expert ``shared = (W1s [ds,d], b1s [ds] or None, W2s [d,ds], b2s [d] or
+    None)``, the capacity policy ("token", "random", "reroute") and an optional float32 device
+    tensor of MOE_ROUTE_STATS elements for the routing statistics (ROUTE_STAT_NAMES order).
     Returns (variant, tensors kept alive for it)."""
     sd = _storage_dtype(cfg)
     v = _lib.MoeVariant()
     v.activation = {"gelu": _lib.MOE_ACT_GELU, "silu": _lib.MOE_ACT_SILU}[activation]
     v.noise_std = float(noise_std)
-    keep = ()
+    v.drop_policy = DROP_POLICIES[drop_policy]
+    keep = {}
     if shared is not None:
         W1s, b1s, W2s, b2s = shared
         ds = W1s.shape[0]
@@ -217,7 +225,11 @@ def make_variant(cfg: MoeConfig, activation: str = "gelu", noise_std: float = 0.
         _expect(b2s, "b2s", (cfg.d,), sd, optional=True)
         v.shared_d_ffn = int(ds)
         v.W1s, v.b1s, v.W2s, v.b2s = _ptr(W1s), _ptr(b1s), _ptr(W2s), _ptr(b2s)
-        keep = tuple(shared)
+        keep["shared"] = tuple(shared)
+    if route_stats is not None:
+        _expect(route_stats, "route_stats", (_lib.MOE_ROUTE_STATS,), torch.float32)
+        v.route_stats = _ptr(route_stats)
+        keep["route_stats"] = route_stats
     return v, keep
 
 
@@ -263,6 +275,8 @@ class ForwardPlan:
             "counts": torch.empty((E,), dtype=i32, device=dev),
             "kept": torch.empty((E,), dtype=i32, device=dev),
         }
+        if variant is not None and "route_stats" in variant[1]:
+            self.out["route_stats"] = variant[1]["route_stats"]
         self.aux = MoeForwardAux()
         if keep_routing:
             R = rows_max(cfg)

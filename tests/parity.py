@@ -11,7 +11,10 @@ Tolerances (one place, used by every GPU test):
     its own reaches 2^-9 |y| and exceeds 2e-2 rms for outputs above about 10 rms (workloads
     with many dropped tokens have a small rms);
   * float32 outputs: max|y - y_ref| <= 1e-5 * max|y_ref|;
-  * weights w, P, L: relative 1e-5 (float32 softmax against the float64 one); f: relative 1e-6.
+  * weights w, P, L: relative 1e-5 (float32 softmax against the float64 one); f: relative 1e-6;
+  * routing statistics: loss_sq, loss_quant, loss_var, usage_std (float64 functions of the
+    exact counts, rounded once) relative 1e-6; entropy (float32 per-token terms) relative 1e-5
+    plus 1e-6 ln E.
 """
 from __future__ import annotations
 
@@ -56,7 +59,7 @@ class Problem:
     shared expert of hidden width ``shared_d_ffn`` (seeded weights; 0 = none)."""
 
     def __init__(self, shape: MoEShape, bias_std: float = 0.0, arrays: dict | None = None, activation: str = "gelu",
-                 noise_std: float = 0.0, shared_d_ffn: int = 0):
+                 noise_std: float = 0.0, shared_d_ffn: int = 0, drop_policy: str = "token", route_stats: bool = False):
         self.shape = shape
         self.cfg = config_of(shape)
         self.arrays = arrays if arrays is not None else make_inputs(shape, bias_std)
@@ -64,6 +67,7 @@ class Problem:
         self.host = {n: (a if n == "bg" else host_values(a, dt)) for n, a in self.arrays.items()}
         self.dev = {n: to_device(a, dt) for n, a in self.arrays.items()}
         self.activation, self.noise_std, self.shared_d_ffn = activation, float(noise_std), int(shared_d_ffn)
+        self.drop_policy, self.route_stats = drop_policy, bool(route_stats)
         self.shared_host = self.shared_dev = None
         if self.shared_d_ffn:
             sh = make_shared_expert(shape, self.shared_d_ffn, bias_std)
@@ -72,16 +76,18 @@ class Problem:
 
     @property
     def has_variant(self) -> bool:
-        return self.activation != "gelu" or self.noise_std > 0.0 or self.shared_d_ffn > 0
+        return (self.activation != "gelu" or self.noise_std > 0.0 or self.shared_d_ffn > 0
+                or self.drop_policy != "token" or self.route_stats)
 
     def variant(self):
         if not self.has_variant:
             return None
-        return ops.make_variant(self.cfg, self.activation, self.noise_std, self.shared_dev)
+        stats = torch.full((len(ops.ROUTE_STAT_NAMES),), float("nan"), device="cuda") if self.route_stats else None
+        return ops.make_variant(self.cfg, self.activation, self.noise_std, self.shared_dev, self.drop_policy, stats)
 
     def oracle_kw(self) -> dict:
-        """The variant's keyword arguments of oracle.forward / forward_rows / brute_dense."""
-        return dict(act=self.activation, noise_std=self.noise_std, shared=self.shared_host)
+        """The variant's keyword arguments of oracle.forward / forward_rows."""
+        return dict(act=self.activation, noise_std=self.noise_std, shared=self.shared_host, policy=self.drop_policy)
 
     def args(self):
         d = self.dev
@@ -130,10 +136,10 @@ def check_routing(p: Problem, gpu: dict) -> dict:
     s_gpu = gpu["scores"]
     r = oracle.route_from_scores(s_gpu, sh.k)
     np.testing.assert_array_equal(gpu["topk_idx"], r["idx"], err_msg="top-k indices")
-    np.testing.assert_allclose(gpu["topk_w"], r["w"], rtol=W_REL, atol=1e-7, err_msg="top-k weights")
-    np.testing.assert_allclose(gpu["topk_w"].astype(np.float64).sum(1), 1.0, rtol=0, atol=sh.k * 2.0 ** -23)
     C = oracle.capacity(sh.T, sh.E, sh.k, sh.capacity_factor)
-    dsp = oracle.dispatch(r["idx"], sh.E, C)
+    dsp, w = oracle.dispatch_policy(r, sh.E, C, sh.k, p.drop_policy, sh.seed)
+    np.testing.assert_allclose(gpu["topk_w"], w, rtol=W_REL, atol=1e-7, err_msg="top-k weights")
+    np.testing.assert_allclose(gpu["topk_w"].astype(np.float64).sum(1), 1.0, rtol=0, atol=sh.k * 2.0 ** -23)
     for key in ("counts", "kept", "offsets", "dest"):
         np.testing.assert_array_equal(gpu[key], dsp[key], err_msg=key)
     n = int(dsp["kept"].sum())
@@ -143,7 +149,18 @@ def check_routing(p: Problem, gpu: dict) -> dict:
     np.testing.assert_allclose(gpu["P"], st["P"], rtol=W_REL, atol=1e-9, err_msg="P")
     np.testing.assert_allclose(gpu["L"][0], st["L"], rtol=W_REL, err_msg="L")
     np.testing.assert_allclose(gpu["prob_colsum"], r["p"].sum(0), rtol=W_REL, atol=1e-6, err_msg="prob_colsum")
+    if "route_stats" in gpu:
+        check_route_stats(gpu["route_stats"], oracle.routing_stats(dsp["counts"], r["p"]), sh.E)
     return {"route": r, "dispatch": dsp, "stats": st, "C": C}
+
+
+def check_route_stats(got, ref: dict, E: int):
+    got = np.asarray(got, np.float64)
+    for i, name in enumerate(ops.ROUTE_STAT_NAMES):
+        if name == "entropy":
+            np.testing.assert_allclose(got[i], ref[name], rtol=1e-5, atol=1e-6 * np.log(E), err_msg=name)
+        else:
+            np.testing.assert_allclose(got[i], ref[name], rtol=1e-6, atol=1e-12, err_msg=name)
 
 
 def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
