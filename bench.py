@@ -46,6 +46,12 @@ def _args():
                     help="Gaussian router noise std (forward variant; needs a workload without Gumbel noise)")
     ap.add_argument("--shared-d-ffn", type=int, default=0,
                     help="hidden width of a shared expert every token uses (forward variant; 0 = none)")
+    ap.add_argument("--drop-policy", choices=("token", "random", "reroute"), default="token",
+                    help="what happens to slots past capacity (variant; token = the first C in token order)")
+    ap.add_argument("--route-stats", action="store_true",
+                    help="also compute the five routing statistics in the timed steps and report them")
+    ap.add_argument("--capacity-factor", type=float, default=None,
+                    help="override the workload's capacity factor (reported in config)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -101,7 +107,7 @@ def cpu_baseline(shape, arrays, n_tokens: int, variant: dict | None = None) -> d
         vkw = {}
         if variant:
             shared = variant.get("shared")
-            vkw = dict(act=variant["activation"], noise_std=variant["noise_std"],
+            vkw = dict(act=variant["activation"], noise_std=variant["noise_std"], policy=variant["drop_policy"],
                        shared=None if shared is None else tuple(val(shared[n]) for n in ("W1s", "b1s", "W2s", "b2s")))
         out = oracle.forward(*args, k=shape.k, capacity_factor=shape.capacity_factor, tau=shape.temperature,
                              gumbel=shape.gumbel, seed=shape.seed, **vkw)
@@ -140,6 +146,8 @@ def main() -> int:
         print(json.dumps({"calibration_copy_bytes": n, "copies": 3}), flush=True)
         return 0
     shape = CONFIGS[args.workload]
+    if args.capacity_factor is not None:
+        shape = shape.with_(capacity_factor=args.capacity_factor)
     arrays = make_inputs(shape)
 
     def dev(a):
@@ -152,17 +160,22 @@ def main() -> int:
     tensors = [dev(arrays[n]) for n in ("x", "Wg", "bg", "W1", "b1", "W2", "b2")]
     cfg = ops.make_config(shape.T, shape.d, shape.E, shape.k, shape.d_ffn, shape.capacity_factor,
                           shape.temperature, shape.gumbel, shape.seed, shape.dtype)
-    with_variant = args.activation != "gelu" or args.noise_std > 0.0 or args.shared_d_ffn > 0
+    with_variant = (args.activation != "gelu" or args.noise_std > 0.0 or args.shared_d_ffn > 0
+                    or args.drop_policy != "token" or args.route_stats)
     variant = None
     variant_host = None
+    route_stats = None
     if with_variant:
         shared = None
-        variant_host = {"activation": args.activation, "noise_std": args.noise_std, "shared": None}
+        variant_host = {"activation": args.activation, "noise_std": args.noise_std, "shared": None,
+                        "drop_policy": args.drop_policy}
+        if args.route_stats:
+            route_stats = torch.zeros((len(ops.ROUTE_STAT_NAMES),), dtype=torch.float32, device="cuda")
         if args.shared_d_ffn > 0:
             sh = make_shared_expert(shape, args.shared_d_ffn)
             shared = tuple(dev(sh[n]) for n in ("W1s", "b1s", "W2s", "b2s"))
             variant_host["shared"] = sh
-        variant = ops.make_variant(cfg, args.activation, args.noise_std, shared)
+        variant = ops.make_variant(cfg, args.activation, args.noise_std, shared, args.drop_policy, route_stats)
     plan = ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant)
     for _ in range(args.warmup):
         plan.run()
@@ -193,7 +206,7 @@ def main() -> int:
     dom_name, dom_ms = ("expert_gemm1_gelu", g1) if g1 >= g2 else ("expert_gemm2", g2)
     achieved = stage_flops[dom_name] / (dom_ms * 1e-3) / 1e12
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{shape.name}.json")
-    traffic = None if with_variant else stored_traffic(traffic_path, dom_name)
+    traffic = None if (with_variant or args.capacity_factor is not None) else stored_traffic(traffic_path, dom_name)
     ng = (T + 15) // 16
     router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + ng * E * 8
     # GEMM1 reads the token rows through the permutation (no gathered copy) on the bf16 MFMA
@@ -220,7 +233,8 @@ def main() -> int:
                    "capacity_factor": shape.capacity_factor, "temperature": shape.temperature,
                    "gumbel": shape.gumbel, "parallelism": "none (one GPU)",
                    **({"variant": {"activation": args.activation, "noise_std": args.noise_std,
-                                   "shared_d_ffn": args.shared_d_ffn}} if with_variant else {})},
+                                   "shared_d_ffn": args.shared_d_ffn, "drop_policy": args.drop_policy,
+                                   "route_stats": args.route_stats}} if with_variant else {})},
         "roofline": {"bound": "mfma", "kernel": dom_name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic},
         "grouped_gemm": {"tflops": (2 * gemm_flops + shared_flops) / ((g1 + g2) * 1e-3) / 1e12,
@@ -236,6 +250,8 @@ def main() -> int:
         "stage_ms": stage,
         "counts_minmax": [int(counts.min()), int(counts.max())],
     }
+    if route_stats is not None:
+        line["route_stats"] = dict(zip(ops.ROUTE_STAT_NAMES, route_stats.cpu().tolist()))
     if args.cpu_sample_tokens != 0:
         n_cpu = T if args.cpu_sample_tokens < 0 else min(args.cpu_sample_tokens, T)
         line["cpu_baseline"] = cpu_baseline(shape, arrays, n_cpu, variant_host)
