@@ -107,22 +107,26 @@ def renormalise(p: np.ndarray, idx: np.ndarray) -> np.ndarray:
     return sel / sel.sum(axis=1, keepdims=True)
 
 
-def route_from_scores(s: np.ndarray, k: int) -> dict:
-    """Softmax, top-k and renormalised weights from float32 scores s [T,E]."""
-    s = np.asarray(s, np.float32)
+def route_from_scores(s: np.ndarray, k: int, exact: bool = False) -> dict:
+    """Softmax, top-k and renormalised weights from float32 scores s [T,E] (float64 scores,
+    unrounded, when ``exact``)."""
+    s = np.asarray(s, np.float64 if exact else np.float32)
     p = softmax(s)
     idx = topk(s, k)
     w = renormalise(p, idx)
     return {"s": s, "p": p, "idx": idx, "w": w}
 
 
-def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None, noise_std=0.0):
+def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None, noise_std=0.0, exact_scores=False):
     """Router step. Returns z (float64 logits), s (float32 scores), p, idx, w.
 
     Noise: Gumbel when ``gumbel``, else Gaussian noise of std ``noise_std`` when it is > 0,
     else none. With ``given_scores`` (float32 [T,E]) the routing is re-derived from those
-    scores instead of the oracle's own logits (z is still the oracle's float64 logit)."""
+    scores instead of the oracle's own logits (z is still the oracle's float64 logit). With
+    ``exact_scores`` the scores are (z + g) / tau in float64, never rounded to float32 (the
+    method's definition without the device's float32 scores; smooth in the inputs)."""
     z = logits(x, Wg, bg)
+    exact = exact_scores and given_scores is None
     if given_scores is not None:
         s = np.asarray(given_scores, np.float32)
     else:
@@ -132,8 +136,11 @@ def route(x, Wg, bg, k, tau=1.0, gumbel=False, seed=0, given_scores=None, noise_
             g32 = philox.gaussian_f32(seed, z.shape[0], z.shape[1], noise_std)
         else:
             g32 = None
-        s = scores(z.astype(np.float32), tau, g32)
-    out = route_from_scores(s, k)
+        if exact:
+            s = (z + (0.0 if g32 is None else np.asarray(g32, np.float64))) / float(tau)
+        else:
+            s = scores(z.astype(np.float32), tau, g32)
+    out = route_from_scores(s, k, exact=exact)
     out["z"] = z
     return out
 
@@ -374,12 +381,13 @@ def dispatch_policy(r: dict, E: int, C: int, k: int, policy: str, seed: int) -> 
 
 
 def forward(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbel=False,
-            seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None, policy="token") -> dict:
+            seed=0, given_scores=None, act="gelu", noise_std=0.0, shared=None, policy="token",
+            exact_scores=False) -> dict:
     """The layer: route -> dispatch -> gather -> experts -> combine (+ shared expert), plus
     f, P, L and the routing statistics."""
     T, d = x.shape
     E = Wg.shape[0]
-    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std, exact_scores)
     C = capacity(T, E, k, capacity_factor)
     dsp, w = dispatch_policy(r, E, C, k, policy, seed)
     x_perm = np.asarray(x, np.float64)[dsp["perm"]]
@@ -473,3 +481,93 @@ def brute_dense(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbe
 def temperature_at(step: int, tau0: float = 1.0, tau_min: float = 0.5, rate: float = 1e-4) -> float:
     """tau_t = max(tau_min, tau0 - rate * t) ([A] 3.2: 0.5, 1.0, 1e-4; [M]: rate 1e-3)."""
     return max(float(tau_min), float(tau0) - float(rate) * float(step))
+
+
+# ---------------------------------------------------------------- backward ([G] 2.2, 2.3, 3.3)
+def gelu_grad(v: np.ndarray) -> np.ndarray:
+    """d/dv of the exact GeLU 0.5 v (1 + erf(v / sqrt 2)): Phi(v) + v phi(v)."""
+    return 0.5 * (1.0 + erf(v * SQRT1_2)) + v * np.exp(-0.5 * v * v) / math.sqrt(2.0 * math.pi)
+
+
+def silu_grad(v: np.ndarray) -> np.ndarray:
+    """d/dv of v sigmoid(v): sigmoid(v) (1 + v (1 - sigmoid(v)))."""
+    sg = expit(v)
+    return sg * (1.0 + v * (1.0 - sg))
+
+
+ACTIVATION_GRADS = {"gelu": gelu_grad, "silu": silu_grad}
+
+
+def backward(x, Wg, bg, W1, b1, W2, b2, dy, *, k, capacity_factor, lam=0.0, tau=1.0, gumbel=False, seed=0,
+             given_scores=None, act="gelu", noise_std=0.0, policy="token", exact_scores=False) -> dict:
+    """Gradients of J = sum(dy * y) + lam * L with respect to x, W_g, b_g, W1, b1, W2, b2.
+
+    What carries gradient ([G] 2.2, 2.3, 3.3): the routing decisions (top-k, capacity, the
+    policy) and f are discrete and held fixed; the weights w and the balance term's P are
+    continuous. A dropped slot gets no expert-path gradient (its output is masked to zero),
+    but its probability still sits in the denominator of the token's weights. Steps:
+      o_r = FFN_e(x_t) for each kept slot at row r of expert e; y_t = sum_j w_tj o_r
+      dO_r = w_tj dy_t;  dw_tj = <dy_t, o_r> (0 for a dropped slot)
+      dW2_e = sum_r dO_r^T h_r; db2_e = sum_r dO_r; da_r = (dO_r W2_e) * act'(a_r)
+      dW1_e = sum_r da_r^T x_t; db1_e = sum_r da_r; dx_t += da_r W1_e
+      w_tj = p_t,e_j / S_t (S_t = sum over the token's k final experts) =>
+      dp_t,e_m += (dw_tm - sum_j dw_tj w_tj) / S_t
+      dp_t,e += lam * E f_e / T (L = E sum_e f_e P_e, P_e = mean_t p_t,e)
+      ds_t = p_t * (dp_t - <p_t, dp_t>) (softmax); dz = ds / tau (the noise is a constant)
+      dW_g = dz^T x; db_g = sum_t dz_t; dx_t += dz_t W_g
+    Returns the gradients (float64) and the intermediates dz, dw."""
+    x64 = np.asarray(x, np.float64)
+    dy64 = np.asarray(dy, np.float64)
+    T, d = x64.shape
+    E = Wg.shape[0]
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std, exact_scores)
+    C = capacity(T, E, k, capacity_factor)
+    dsp, w = dispatch_policy(r, E, C, k, policy, seed)
+    final_idx = dsp.get("final_idx", r["idx"])
+    dest = dsp["dest"]
+    grad = ACTIVATION_GRADS[act]
+    fwd = ACTIVATIONS[act]
+    dx = np.zeros((T, d))
+    dW1 = np.zeros(W1.shape)
+    db1 = np.zeros(W1.shape[:2])
+    dW2 = np.zeros(W2.shape)
+    db2 = np.zeros(W2.shape[:2])
+    dw = np.zeros((T, k))
+    for e in range(E):
+        slots = sorted((int(dest[t, j]), t, j) for t in range(T) for j in range(k)
+                       if final_idx[t, j] == e and dest[t, j] >= 0)           # row order of the segment
+        if not slots:
+            continue
+        ts = np.array([t for _, t, _ in slots])
+        js = np.array([j for _, _, j in slots])
+        W1e, W2e = np.asarray(W1[e], np.float64), np.asarray(W2[e], np.float64)
+        a = x64[ts] @ W1e.T
+        if b1 is not None:
+            a = a + np.asarray(b1[e], np.float64)
+        h = fwd(a)
+        o = h @ W2e.T
+        if b2 is not None:
+            o = o + np.asarray(b2[e], np.float64)
+        dw[ts, js] = np.sum(dy64[ts] * o, axis=1)
+        dO = w[ts, js][:, None] * dy64[ts]
+        dW2[e] = dO.T @ h
+        db2[e] = dO.sum(axis=0)
+        da = (dO @ W2e) * grad(a)
+        dW1[e] = da.T @ x64[ts]
+        db1[e] = da.sum(axis=0)
+        np.add.at(dx, ts, da @ W1e)
+    p = r["p"]
+    S = np.take_along_axis(p, final_idx, axis=1).sum(axis=1)
+    corr = np.sum(dw * w, axis=1)
+    dp = np.zeros((T, E))
+    for j in range(k):
+        np.add.at(dp, (np.arange(T), final_idx[:, j]), (dw[:, j] - corr) / S)
+    f = dsp["counts"] / (k * T)
+    dp = dp + lam * E * f[None, :] / T
+    ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))
+    dz = ds / float(tau)
+    dWg = dz.T @ x64
+    dbg = dz.sum(axis=0)
+    dx = dx + dz @ np.asarray(Wg, np.float64)
+    return {"dx": dx, "dWg": dWg, "dbg": dbg, "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "dz": dz, "dw": dw,
+            "w": w, "dest": dest, "final_idx": final_idx, "route": r, "dispatch": dsp}
