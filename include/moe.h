@@ -227,6 +227,53 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_variant* variant, con
                           int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws,
                           size_t ws_bytes, moe_stream_t stream);
 
+/* ---------------------------------------------------------------------------------------
+ * Backward pass (kwkr.cn page on sparse activation, sections 2.2, 2.3 and 3.3): the gradients
+ * of J = sum(dy * y) + lam * L. The routing decisions (top-k, capacity, the drop policy) and
+ * f are discrete and carry no gradient; the combine weights w and the balance term's P do. A
+ * dropped slot contributes nothing to y, but its probability stays in its token's
+ * renormalisation, so it still reaches the router:
+ *   dw_tj = <dy_t, FFN_e(x_t)> (kept slots), w_tj = p_t,e_j / sum_j' p_t,e_j' over the token's
+ *   k final experts, dP_e = lam E f_e / T per token, softmax and 1/tau back to the logits;
+ *   expert e: dW2 = sum (w dy)^T h, dW1 = sum dA^T x with dA = (w dy W2_e) * act'(a); dx gets
+ *   dA W1_e per kept slot and dz W_g; the noise is a constant.
+ * Precision: bf16 storage keeps the pre-activations a and the products dA and w dy in bf16
+ * (MFMA operands) with float32 accumulation; float32 storage computes in float32. A shared
+ * expert is not covered (MOE_EUNSUPPORTED). */
+
+/* Stages of moe_backward (router backward, weight transposes, dA product, dx product, row
+ * transposes, dW2 product, dW1 product, bias / router / input gradients). */
+#define MOE_BACKWARD_STAGES 8
+
+typedef struct moe_backward_aux {
+  float* dz;                 /* NULL, or [T,E] f32: receives the logit gradient                */
+  moe_event_t* stage_events; /* NULL, or MOE_BACKWARD_STAGES+1 created events                  */
+} moe_backward_aux;
+
+/* Workspace bytes of moe_forward_train + moe_backward for cfg and variant (nullable). This
+ * includes the saved state (pre-activations [R, d_ffn], routing, expert outputs) and the
+ * backward's scratch (the transposed weights: 2 E d d_ffn elements). Host only. */
+moe_status moe_workspace_size_train(const moe_config* cfg, const moe_variant* variant, size_t* bytes);
+
+/* moe_forward_ex that also keeps in ws everything moe_backward needs. The routing arrays stay
+ * in ws; aux pointers, when given, receive copies. Same arguments and outputs. */
+moe_status moe_forward_train(const moe_config* cfg, const moe_variant* variant, const void* x,
+                             const void* Wg, const float* bg, const void* W1, const void* b1,
+                             const void* W2, const void* b2, void* y, float* f, float* P, float* L,
+                             int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws,
+                             size_t ws_bytes, moe_stream_t stream);
+
+/* Gradients after moe_forward_train with the same cfg, variant, inputs and ws (unchanged in
+ * between). dy [T,d] dtype; lam: the weight of L in J.
+ *   dx [T,d] dtype; dWg [E,d] f32; dbg [E] f32 (nullable); dW1 [E,d_ffn,d] f32; db1 [E,d_ffn]
+ *   f32 (nullable); dW2 [E,d,d_ffn] f32; db2 [E,d] f32 (nullable). Experts without kept rows
+ *   get zero weight gradients. Every sum has a fixed order (bitwise reproducible). */
+moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const void* x,
+                        const void* Wg, const void* W1, const void* W2, const void* dy, float lam,
+                        void* dx, float* dWg, float* dbg, float* dW1, float* db1, float* dW2,
+                        float* db2, const moe_backward_aux* aux, void* ws, size_t ws_bytes,
+                        moe_stream_t stream);
+
 /* Temperature schedule tau_t = max(tau_min, tau0 - rate * step) (aberweb.com page, section
  * 3.2: tau0 = 1, tau_min = 0.5, rate = 1e-4; mhpn.cn page: rate 1e-3), computed in double and
  * rounded once to float; the result goes to moe_config.temperature. Host only. */

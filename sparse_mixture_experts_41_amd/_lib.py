@@ -15,6 +15,9 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = 0, 1, 2, 3, 4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_FORWARD_STAGES = 6
 STAGE_NAMES = ("route", "scan", "permute_gather", "expert_gemm1_gelu", "expert_gemm2", "combine")
+MOE_BACKWARD_STAGES = 8
+BWD_STAGE_NAMES = ("bwd_router", "transpose_weights", "dact_gemm", "dx_gemm", "rows_to_cols", "wgrad_W2",
+                   "wgrad_W1", "bias_router_dx")
 
 
 class MoeConfig(ctypes.Structure):
@@ -47,6 +50,10 @@ class MoeVariant(ctypes.Structure):
     ]
 
 
+class MoeBackwardAux(ctypes.Structure):
+    _fields_ = [("dz", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"status {status}: {detail}")
@@ -69,6 +76,11 @@ _SIGS = {
     "moe_workspace_size_ex": (ctypes.c_int, [_CFG, _VAR, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_forward_ex": (ctypes.c_int, [_CFG, _VAR, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),
+    "moe_workspace_size_train": (ctypes.c_int, [_CFG, _VAR, ctypes.POINTER(ctypes.c_size_t)]),
+    "moe_forward_train": (ctypes.c_int, [_CFG, _VAR, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),
+    "moe_backward": (ctypes.c_int, [_CFG, _VAR, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.POINTER(MoeBackwardAux), _P, ctypes.c_size_t, _P]),
     "moe_temperature_at": (ctypes.c_float, [ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),

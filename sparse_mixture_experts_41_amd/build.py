@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
-SOURCES = ["router.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "moe_abi.cpp"]
+SOURCES = ["router.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "backward.hip", "moe_abi.cpp"]
 
 
 def hipcc() -> str:

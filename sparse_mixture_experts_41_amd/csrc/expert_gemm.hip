@@ -37,9 +37,24 @@ struct GemmArgs {
   const int32_t* rows;    // [R] or null: A row of expert-sorted row r is rows[r] (fused gather)
   int a_rows;             // rows of A when `rows` is set (a_rows * K * 2 < 2^31)
   int dense;              // 1: one expert (E = 1) over all R rows; kept and offsets are unused
+  // -- training --
+  void* pre;              // [R,N] or null: an activation epilogue also stores its input (dtype)
+  const float* row_scale; // [R]: activation-gradient epilogues multiply row r by row_scale[r]
+  const void* act_in;     // [R,N] dtype: the activation's input at the output positions
+  int lda, ldb;           // row pitches of A and B in elements (0: K)
+  // wgrad = 1: group e is a dense product over K = kept[e] rounded up to kWgradK, starting at
+  // column koff[e] of A [M, lda] and B [N, ldb] (columns past kept[e] hold zeros); its
+  // output is the e-th [M, N] block of out. Groups with kept[e] = 0 write nothing.
+  int wgrad;
+  int M;
+  const int32_t* koff;    // [E]
 };
 
-enum { kEpiGelu = 0, kEpiLinear = 1, kEpiSilu = 2 };   // GEMM1 (activation, bf16 out) or GEMM2 (float out)
+// GEMM1 (activation, bf16 or dtype out), GEMM2 (float out), and the backward's
+// activation-gradient epilogue: out = acc * row_scale[r] * act'(act_in[r, n]) (dtype out).
+enum { kEpiGelu = 0, kEpiLinear = 1, kEpiSilu = 2, kEpiGeluGrad = 3, kEpiSiluGrad = 4 };
+
+constexpr bool is_grad_epi(int epi) { return epi == kEpiGeluGrad || epi == kEpiSiluGrad; }
 
 // The activation of an expert's hidden layer, for results rounded to bf16.
 template <int EPI>
@@ -47,8 +62,15 @@ __device__ __forceinline__ float activation_bf16(float v) {
   return EPI == kEpiGelu ? gelu_bf16_path(v) : silu_bf16_path(v);
 }
 
+template <int EPI>
+__device__ __forceinline__ float activation_grad(float v) {
+  return EPI == kEpiGeluGrad ? gelu_grad_exact(v) : silu_grad_exact(v);
+}
+
 // Rows of expert e's segment; a segment that does not fit [0, R) or exceeds C counts as empty.
+// In wgrad mode every group with kept rows has M output rows.
 __device__ __forceinline__ int segment_rows(const GemmArgs& g, int e) {
+  if (g.wgrad) return (g.kept[e] > 0 && g.kept[e] <= g.C) ? g.M : 0;
   if (g.dense) return e == 0 ? g.R : 0;
   const int m = g.kept[e], o = g.offsets[e];
   return (m > 0 && m <= g.C && o >= 0 && o <= g.R - m) ? m : 0;
@@ -166,17 +188,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   int e, mt, nt;
   decode_tile(unit - kpart * n_tiles, g, BM, tiles_n, e, mt, nt);
   const int m_e = segment_rows(g, e);
-  const int row0 = g.dense ? 0 : g.offsets[e];
+  const int row0 = (g.dense || g.wgrad) ? 0 : g.offsets[e];
   const int m0 = mt * BM, n0 = nt * BN;
-  const int N = g.N, K = g.K;
+  const int N = g.N;
+  const int lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
+  const int K = g.wgrad ? (g.kept[e] + kWgradK - 1) / kWgradK * kWgradK : g.K;
+  const size_t kofs = g.wgrad ? static_cast<size_t>(g.koff[e]) : 0;
   const int nk = K / BK / g.splits;          // K steps of this part
   const bool gathered = g.rows != nullptr;
-  const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) +
-                                                 (gathered ? 0 : static_cast<size_t>(row0 + m0) * K)) +
+  const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + kofs +
+                                                 (gathered ? 0 : static_cast<size_t>(row0 + m0) * lda)) +
                    static_cast<size_t>(kpart) * nk * ROWB;
-  const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
-                                                 (static_cast<size_t>(e) * N + n0) * K) +
+  const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
+                                                 (g.wgrad ? static_cast<size_t>(n0) * ldb
+                                                          : (static_cast<size_t>(e) * N + n0) * ldb)) +
                    static_cast<size_t>(kpart) * nk * ROWB;
+  const size_t out_base = g.wgrad ? static_cast<size_t>(e) * g.M * N : 0;   // elements
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
 
@@ -190,12 +217,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     const int c = lslot ^ ((r / RPS) % CPR);
     const int ra = r < a_last ? r : a_last;
     const uint32_t arow = gathered ? static_cast<uint32_t>(g.rows[row0 + m0 + ra]) : static_cast<uint32_t>(ra);
-    aoff[i] = static_cast<uint32_t>((arow * K + c * 8) * 2);
-    boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * K + c * 8) * 2);
+    aoff[i] = static_cast<uint32_t>((arow * lda + c * 8) * 2);
+    boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * ldb + c * 8) * 2);
   }
-  // the clamped offsets stay below 256 rows of K elements past the B resource base and below
+  // the clamped offsets stay below 256 rows of the pitch past the B resource base and below
   // the tile's (or, gathered, all of A's) rows past the A base; anything beyond reads as zero
-  const int span = BM * K * 2, span_a = gathered ? g.a_rows * K * 2 : span;
+  const int span = BM * ldb * 2, span_a = gathered ? g.a_rows * lda * 2 : BM * lda * 2;
   auto issue = [&](int st) {   // loads of K step min(st, nk-1) into buffer st % NS
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
     const uint32_t kb = static_cast<uint32_t>(st < nk ? st : nk - 1) * ROWB;
@@ -229,19 +256,49 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   // (bf16) or 32 lanes (float) store each row's 256 or 512 contiguous bytes, so every store
   // covers whole cache lines. N is a multiple of 64, so each 16-byte piece lies wholly inside
   // or outside [0, N). Only the NI row blocks the wave multiplied can hold segment rows.
-  auto epilogue = [&](auto ni_const, auto bias_const) {
+  auto epilogue = [&](auto ni_const, auto bias_const, auto pre_const) {
     constexpr int NI = decltype(ni_const)::value;
     constexpr bool BIAS = decltype(bias_const)::value;
+    constexpr bool PRE = decltype(pre_const)::value;       // also store the activation's input
+    constexpr bool GRAD = is_grad_epi(EPI);
     constexpr int OB = EPI == kEpiLinear ? 4 : 2;         // output bytes per element
     constexpr int PITCH = 128 * OB + 16;                   // bytes per staged row (padded)
     constexpr int CPRW = 128 * OB / 16;                    // 16-byte pieces per row
     constexpr int RPW = 64 / CPRW;                         // rows per wave store
-    static_assert(4 * 32 * PITCH <= NS * STAGE, "epilogue staging fits the operand ring");
+    static_assert((EPI == kEpiLinear ? 4 : 8) * 32 * PITCH <= NS * STAGE, "epilogue staging fits the operand ring");
     char* st = smem + wave * 32 * PITCH;
+    char* st2 = smem + (4 + wave) * 32 * PITCH;            // staged inputs of the activation
     char* outb = static_cast<char*>(EPI != kEpiLinear ? g.out : (kpart == 0 ? g.out : g.out2));
     __syncthreads();                                       // every wave is done with the ring
+    // whole-row pieces of the wave's row block: LDS <-> global, 16 bytes per lane
+    auto rows_out = [&](const char* stage, char* base, int i) {
+#pragma unroll
+      for (int it = 0; it < 32 / RPW; ++it) {
+        const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
+        const int r = m0 + wm * 128 + i * 32 + rr;
+        const int c = n0 + wn * 128 + pc * (16 / OB);
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * PITCH + pc * 16);
+        if (r < m_e && c < N)
+          *reinterpret_cast<u32x4*>(base + (out_base + static_cast<size_t>(row0 + r) * N + c) * OB) = v;
+      }
+    };
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
+      float scale = 0.0f;
+      if constexpr (GRAD) {
+        // stage the activation inputs of this row block (same whole-row pattern as the stores)
+#pragma unroll
+        for (int it = 0; it < 32 / RPW; ++it) {
+          const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
+          const int r = m0 + wm * 128 + i * 32 + rr;
+          const int c = n0 + wn * 128 + pc * 8;
+          if (r < m_e && c < N)
+            *reinterpret_cast<u32x4*>(st2 + rr * PITCH + pc * 16) = *reinterpret_cast<const u32x4*>(
+                static_cast<const char*>(g.act_in) + (static_cast<size_t>(row0 + r) * N + c) * 2);
+        }
+        const int r = min(m0 + wm * 128 + i * 32 + l32, m_e - 1);
+        scale = g.row_scale[row0 + r];
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -254,25 +311,31 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
                    (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + wn * 128 + cl + u, N - 1), true)
                          : 0.0f);
           char* dst = st + l32 * PITCH + cl * OB;
-          if (EPI != kEpiLinear) {
+          if constexpr (GRAD) {
+            const bf16x4 a = *reinterpret_cast<const bf16x4*>(st2 + l32 * PITCH + cl * 2);
+            bf16x4 pk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              pk[u] = static_cast<__bf16>(o[u] * scale * activation_grad<EPI>(static_cast<float>(a[u])));
+            *reinterpret_cast<bf16x4*>(dst) = pk;
+          } else if constexpr (EPI != kEpiLinear) {
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = static_cast<__bf16>(activation_bf16<EPI>(o[u]));
             *reinterpret_cast<bf16x4*>(dst) = pk;
+            if constexpr (PRE) {
+              bf16x4 pv;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) pv[u] = static_cast<__bf16>(o[u]);
+              *reinterpret_cast<bf16x4*>(st2 + l32 * PITCH + cl * OB) = pv;
+            }
           } else {
             *reinterpret_cast<floatx4*>(dst) = floatx4{o[0], o[1], o[2], o[3]};
           }
         }
       // the wave reads back only what it wrote itself: LDS keeps one wave's accesses in order
-#pragma unroll
-      for (int it = 0; it < 32 / RPW; ++it) {
-        const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
-        const int r = m0 + wm * 128 + i * 32 + rr;
-        const int c = n0 + wn * 128 + pc * (16 / OB);
-        const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * PITCH + pc * 16);
-        if (r < m_e && c < N)
-          *reinterpret_cast<u32x4*>(outb + (static_cast<size_t>(row0 + r) * N + c) * OB) = v;
-      }
+      rows_out(st, outb, i);
+      if constexpr (PRE && EPI != kEpiLinear && !GRAD) rows_out(st2, static_cast<char*>(g.pre), i);
       __builtin_amdgcn_sched_barrier(0);   // one row block at a time: bounded register use
     }
   };
@@ -349,10 +412,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       schedule(true);
     }
     wait_vmcnt<0>();     // the trailing re-loads must land before the workgroup's LDS is released
+    if constexpr (EPI == kEpiGelu || EPI == kEpiSilu) {
+      if (g.pre != nullptr) {
+        if (add_bias)
+          epilogue(ni_const, std::true_type{}, std::true_type{});
+        else
+          epilogue(ni_const, std::false_type{}, std::true_type{});
+        return;
+      }
+    }
     if (add_bias)
-      epilogue(ni_const, std::true_type{});
+      epilogue(ni_const, std::true_type{}, std::false_type{});
     else
-      epilogue(ni_const, std::false_type{});
+      epilogue(ni_const, std::false_type{}, std::false_type{});
   };
   const int valid = m_e - m0 - wm * 128;     // segment rows in this wave's 128 rows
   if (valid > 64)
@@ -385,8 +457,9 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
   const int nbase = nb * GV_COLS + wave * 32;
-  const u16* __restrict__ ap =
-      static_cast<const u16*>(g.A) + static_cast<size_t>(row0 + (r16 < m_e ? r16 : m_e - 1)) * K + 16 * grp;
+  const int ar = row0 + (r16 < m_e ? r16 : m_e - 1);
+  const u16* __restrict__ ap = static_cast<const u16*>(g.A) +
+                               static_cast<size_t>(g.rows != nullptr ? g.rows[ar] : ar) * K + 16 * grp;
   const u16* bp[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -438,10 +511,15 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
       if (r < m_e) {
         const size_t o = static_cast<size_t>(row0 + r) * N + n;
         const float val = acc[t][i] + bias;
-        if (EPI != kEpiLinear)
+        if constexpr (is_grad_epi(EPI)) {
+          const float a = bf16_to_f32(static_cast<const u16*>(g.act_in)[o]);
+          static_cast<u16*>(g.out)[o] = f32_to_bf16(val * g.row_scale[row0 + r] * activation_grad<EPI>(a));
+        } else if constexpr (EPI != kEpiLinear) {
           static_cast<u16*>(g.out)[o] = f32_to_bf16(activation_bf16<EPI>(val));
-        else
+          if (g.pre != nullptr) static_cast<u16*>(g.pre)[o] = f32_to_bf16(val);
+        } else {
           static_cast<float*>(g.out)[o] = val;
+        }
       }
     }
   }
@@ -459,16 +537,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
   int e, mt, nt;
   if (!decode_tile(blockIdx.x, g, FBM, tiles_n, e, mt, nt)) return;
   const int m_e = segment_rows(g, e);
-  const int row0 = g.dense ? 0 : g.offsets[e];
+  const int row0 = (g.dense || g.wgrad) ? 0 : g.offsets[e];
   const int m0 = mt * 16, n0 = nt * 16;
-  const int N = g.N, K = g.K;
-  const float* __restrict__ A = static_cast<const float*>(g.A);
-  const float* __restrict__ B = static_cast<const float*>(g.B) + static_cast<size_t>(e) * N * K;
+  const int N = g.N;
+  const int lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
+  const int K = g.wgrad ? (g.kept[e] + kWgradK - 1) / kWgradK * kWgradK : g.K;
+  const size_t kofs = g.wgrad ? static_cast<size_t>(g.koff[e]) : 0;
+  const float* __restrict__ A = static_cast<const float*>(g.A) + kofs;
+  const float* __restrict__ B =
+      static_cast<const float*>(g.B) + kofs + (g.wgrad ? 0 : static_cast<size_t>(e) * N * ldb);
+  const int32_t* rows = g.rows;
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int ar = m0 + ty < m_e ? (rows != nullptr ? rows[row0 + m0 + ty] : row0 + m0 + ty) : 0;
   float acc = 0.0f;
   for (int k0 = 0; k0 < K; k0 += 16) {
-    As[ty][tx] = (m0 + ty < m_e && k0 + tx < K) ? A[static_cast<size_t>(row0 + m0 + ty) * K + k0 + tx] : 0.0f;
-    Bs[ty][tx] = (n0 + ty < N && k0 + tx < K) ? B[static_cast<size_t>(n0 + ty) * K + k0 + tx] : 0.0f;
+    As[ty][tx] = (m0 + ty < m_e && k0 + tx < K) ? A[static_cast<size_t>(ar) * lda + k0 + tx] : 0.0f;
+    Bs[ty][tx] = (n0 + ty < N && k0 + tx < K) ? B[static_cast<size_t>(n0 + ty) * ldb + k0 + tx] : 0.0f;
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) acc = fmaf(As[ty][kk], Bs[tx][kk], acc);
@@ -476,9 +560,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
   }
   const int r = m0 + ty, c = n0 + tx;
   if (r < m_e && c < N) {
+    const size_t o = (g.wgrad ? static_cast<size_t>(e) * g.M * N : 0) + static_cast<size_t>(row0 + r) * N + c;
     const float val = acc + load_bias(g.bias, static_cast<size_t>(e) * N + c, false);
-    static_cast<float*>(g.out)[static_cast<size_t>(row0 + r) * N + c] =
-        EPI == kEpiGelu ? gelu_erf(val) : (EPI == kEpiSilu ? silu_exact(val) : val);
+    float* out = static_cast<float*>(g.out);
+    if constexpr (is_grad_epi(EPI)) {
+      out[o] = val * g.row_scale[row0 + r] * activation_grad<EPI>(static_cast<const float*>(g.act_in)[o]);
+    } else {
+      out[o] = EPI == kEpiGelu ? gelu_erf(val) : (EPI == kEpiSilu ? silu_exact(val) : val);
+      if (EPI != kEpiLinear && g.pre != nullptr) static_cast<float*>(g.pre)[o] = val;
+    }
   }
 }
 
@@ -534,6 +624,7 @@ static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, 
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
   GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr, nullptr, 0, 0};
+  g1.pre = a.pre;
   GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2,
               nullptr, 0, 0};
   if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
@@ -551,6 +642,94 @@ hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream) {
   GemmArgs g2{a.H, a.W2, a.b2, a.y, nullptr, nullptr, 1, a.d, a.d_ffn, a.T, a.T, 1, nullptr, nullptr, 0, 1};
   return a.act == kActSilu ? launch_ffn<kEpiSilu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr)
                            : launch_ffn<kEpiGelu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr);
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward products (the weights already transposed, so every operand is K-contiguous).
+template <int EPI>
+static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStream_t stream) {
+  if (!bf16) {
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI>, dim3(tile_grid(g.R, g.E, C, FBM, g.N, 16)), dim3(256), 0,
+                       stream, g);
+  } else if (C <= 16) {
+    hipLaunchKernelGGL(grouped_gemv_bf16_kernel<EPI>, dim3(g.E * ((g.N + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
+                       stream, g);
+  } else {
+    const int grid = round_grid(tile_grid(g.R, g.E, C, 256, g.N, 256) * g.splits);
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream) {
+  GemmArgs g{};
+  g.A = a.A;
+  g.rows = a.rows;
+  g.a_rows = a.a_rows;
+  g.B = a.W2T;
+  g.out = a.dA;
+  g.kept = a.kept;
+  g.offsets = a.offsets;
+  g.E = a.E;
+  g.N = a.d_ffn;
+  g.K = a.d;
+  g.R = a.R;
+  g.C = a.C;
+  g.splits = 1;
+  g.row_scale = a.wrow;
+  g.act_in = a.pre;
+  return a.act == kActSilu ? launch_rows_gemm<kEpiSiluGrad>(g, a.bf16, a.C, stream)
+                           : launch_rows_gemm<kEpiGeluGrad>(g, a.bf16, a.C, stream);
+}
+
+int bwd_dx_splits(int R, int E, int C, int d, int d_ffn, int bf16) {
+  if (!bf16 || C <= 16) return 1;
+  const int tiles = tile_grid(R, E, C, 256, d, 256);
+  return (C > 512 && tiles < 4 * 256 && d_ffn % 64 == 0 && d_ffn >= 1024) ? 2 : 1;
+}
+
+hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream) {
+  GemmArgs g{};
+  g.A = a.dA;
+  g.B = a.W1T;
+  g.out = a.dXp;
+  g.out2 = a.dXp2;
+  g.kept = a.kept;
+  g.offsets = a.offsets;
+  g.E = a.E;
+  g.N = a.d;
+  g.K = a.d_ffn;
+  g.R = a.R;
+  g.C = a.C;
+  g.splits = bwd_dx_splits(a.R, a.E, a.C, a.d, a.d_ffn, a.bf16);
+  return launch_rows_gemm<kEpiLinear>(g, a.bf16, a.C, stream);
+}
+
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {
+  GemmArgs g{};
+  g.A = a.A;
+  g.B = a.B;
+  g.out = a.out;
+  g.kept = a.kept;
+  g.koff = a.koff;
+  g.E = a.E;
+  g.M = a.M;
+  g.N = a.N;
+  g.K = kWgradK;
+  g.lda = a.ld;
+  g.ldb = a.ld;
+  g.R = a.M;
+  g.C = a.C;
+  g.splits = 1;
+  g.wgrad = 1;
+  if (!a.bf16) {
+    const int grid = a.E * ((a.M + 15) / 16) * ((a.N + 15) / 16);
+    hipLaunchKernelGGL(grouped_gemm_f32_kernel<kEpiLinear>, dim3(grid), dim3(256), 0, stream, g);
+  } else {
+    const int grid = round_grid(a.E * ((a.M + 255) / 256) * ((a.N + 255) / 256));
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
+  }
+  return hipGetLastError();
 }
 
 namespace {

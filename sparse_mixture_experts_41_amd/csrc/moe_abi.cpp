@@ -33,12 +33,16 @@ struct Derived {
   int dffs;         // shared expert hidden width, 0 = none
   int policy;       // MOE_DROP_*
   bool stats;       // routing statistics requested
+  bool train;       // the workspace also holds what moe_backward needs, and its scratch
   uint32_t key0, key1;
 };
 
 struct Layout {
   size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
-      y_perm2, Hs, ys, ent, idx_next, cand, hist2, blockbase2, kept1, thresh, total;
+      y_perm2, Hs, ys, ent, idx_next, cand, hist2, blockbase2, kept1, thresh,
+      // training: saved by moe_forward_train, then moe_backward's scratch
+      pre, kept_s, f_s, koff, wrow, dz, dA, dXp, dXp2, W2T, W1T, dOT, HT, dAT, XT, dwg, dyp, total;
+  int ld;   // row pitch of the transposed, padded activations
 };
 
 // C = ceil(c*k*T/E) for the exact value of the double c = m * 2^sh (m a 53-bit integer).
@@ -101,6 +105,7 @@ moe_status check_config(const moe_config* cfg, Derived* D) {
   D->dffs = 0;
   D->policy = MOE_DROP_TOKEN_ORDER;
   D->stats = false;
+  D->train = false;
   D->key0 = static_cast<uint32_t>(cfg->seed & 0xffffffffull);
   D->key1 = static_cast<uint32_t>(cfg->seed >> 32);
   return MOE_OK;
@@ -135,6 +140,14 @@ moe_status check_variant(const moe_variant* v, Derived* D) {
   D->policy = v->drop_policy;
   D->stats = v->route_stats != nullptr;
   return MOE_OK;
+}
+
+int clamp_c(const Derived& D) { return static_cast<int>(D.C < D.T ? D.C : D.T); }
+
+// Whether the backward's first product reads dy through the permutation (every path but the
+// bf16 MFMA path with dy beyond 32-bit buffer offsets, which gathers dy into a copy first).
+bool bwd_gathers(const Derived& D) {
+  return !D.bf16 || clamp_c(D) <= 16 || static_cast<long long>(D.T) * D.d * 2 < (1ll << 31);
 }
 
 Layout layout_of(const Derived& D) {
@@ -173,6 +186,30 @@ Layout layout_of(const Derived& D) {
   L.blockbase2 = take(random || reroute ? ng * E * 4 : 0);
   L.kept1 = take(reroute ? E * 4 : 0);
   L.thresh = take(random ? E * 8 : 0);
+  const size_t d = D.d, dff = D.dff, es = D.esize;
+  const bool tr = D.train;
+  const int64_t ld = (static_cast<int64_t>(R) + static_cast<int64_t>(moe::kWgradK - 1) * D.E + moe::kWgradK - 1) /
+                     moe::kWgradK * moe::kWgradK;
+  L.ld = tr ? static_cast<int>(ld) : 0;
+  const size_t ldz = tr ? static_cast<size_t>(ld) : 0;
+  const bool dx_split = moe::bwd_dx_splits(D.R, D.E, clamp_c(D), D.d, D.dff, D.bf16 ? 1 : 0) == 2;
+  L.pre = take(tr ? R * dff * es : 0);
+  L.kept_s = take(tr ? E * 4 : 0);
+  L.f_s = take(tr ? E * 4 : 0);
+  L.koff = take(tr ? (E + 1) * 4 : 0);
+  L.wrow = take(tr ? R * 4 : 0);
+  L.dz = take(tr ? T * E * 4 : 0);
+  L.dA = take(tr ? R * dff * es : 0);
+  L.dXp = take(tr ? R * d * 4 : 0);
+  L.dXp2 = take(tr && dx_split ? R * d * 4 : 0);
+  L.W2T = take(tr ? E * d * dff * es : 0);
+  L.W1T = take(tr ? E * d * dff * es : 0);
+  L.dOT = take(d * ldz * es);
+  L.HT = take(dff * ldz * es);
+  L.dAT = take(dff * ldz * es);
+  L.XT = take(d * ldz * es);
+  L.dwg = take(tr ? static_cast<size_t>(moe::dwg_slices(D.T, D.d)) * E * d * 4 : 0);
+  L.dyp = take(tr && !bwd_gathers(D) ? R * d * es : 0);
   L.total = off;
   return L;
 }
@@ -389,11 +426,13 @@ namespace {
 moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const void* x, const void* Wg,
                         const float* bg, const void* W1, const void* b1, const void* W2, const void* b2, void* y,
                         float* f, float* P, float* L, int32_t* counts, int32_t* kept, const moe_forward_aux* aux,
-                        void* ws, size_t ws_bytes, moe_stream_t stream) {
+                        void* ws, size_t ws_bytes, moe_stream_t stream, bool train = false) {
   Derived D;
   Layout Lw;
   MOE_CHECK(check_config(cfg, &D));
   MOE_CHECK(check_variant(variant, &D));
+  D.train = train;
+  if (train && D.dffs > 0) return fail(MOE_EUNSUPPORTED, "the backward pass does not cover a shared expert");
   if (D.dffs > 0) {
     MOE_CHECK(need(variant->W1s, 16, "W1s"));
     MOE_CHECK(need(variant->b1s, D.esize, "b1s", true));
@@ -430,14 +469,22 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(ax.stage_events);
-  float* logits = ax.logits ? ax.logits : at<float>(ws, Lw.logits);
+  // training keeps the routing in the workspace for the backward (aux gets copies at the end)
+  const bool own = !train;
+  float* logits = (own && ax.logits) ? ax.logits : at<float>(ws, Lw.logits);
   const bool has_scores = D.noise != moe::kNoiseNone || D.tau != 1.0f;
-  float* scores = ax.scores ? ax.scores : (has_scores ? at<float>(ws, Lw.scores) : nullptr);
-  int32_t* idx = ax.topk_idx ? ax.topk_idx : at<int32_t>(ws, Lw.idx);
-  float* w = ax.topk_w ? ax.topk_w : at<float>(ws, Lw.w);
-  int32_t* offsets = ax.offsets ? ax.offsets : at<int32_t>(ws, Lw.offsets);
-  int32_t* dest = ax.dest ? ax.dest : at<int32_t>(ws, Lw.dest);
-  int32_t* perm = ax.perm ? ax.perm : at<int32_t>(ws, Lw.perm);
+  float* scores = (own && ax.scores) ? ax.scores : (has_scores ? at<float>(ws, Lw.scores) : nullptr);
+  int32_t* idx = (own && ax.topk_idx) ? ax.topk_idx : at<int32_t>(ws, Lw.idx);
+  float* w = (own && ax.topk_w) ? ax.topk_w : at<float>(ws, Lw.w);
+  int32_t* offsets = (own && ax.offsets) ? ax.offsets : at<int32_t>(ws, Lw.offsets);
+  int32_t* dest = (own && ax.dest) ? ax.dest : at<int32_t>(ws, Lw.dest);
+  int32_t* perm = (own && ax.perm) ? ax.perm : at<int32_t>(ws, Lw.perm);
+  int32_t* const kept_user = kept;
+  float* const f_user = f;
+  if (train) {                               // the backward reads kept and f from the workspace
+    kept = at<int32_t>(ws, Lw.kept_s);
+    f = at<float>(ws, Lw.f_s);
+  }
   float* colsum = ax.prob_colsum ? ax.prob_colsum : at<float>(ws, Lw.colsum);
   float* probsum = at<float>(ws, Lw.probsum);
   int32_t* hist = at<int32_t>(ws, Lw.hist);
@@ -539,6 +586,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   fa.bf16 = D.bf16 ? 1 : 0;
   fa.y_perm2 = at<float>(ws, Lw.y_perm2);
   fa.act = D.act;
+  fa.pre = train ? at<void>(ws, Lw.pre) : nullptr;
   if (moe::ffn_gathers(fa))
     fa.rows = perm;
   else
@@ -570,6 +618,21 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   MOE_HIP(moe::launch_combine(y_perm, y_perm2, y_shared, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
           "combine");
   if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");
+  if (train) {
+    const size_t T = D.T, E = D.E, k = D.k;
+    auto copy = [&](void* dst, const void* src, size_t bytes) {
+      return dst != nullptr ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
+    };
+    MOE_HIP(copy(kept_user, kept, E * 4), "copy");
+    MOE_HIP(copy(f_user, f, E * 4), "copy");
+    MOE_HIP(copy(ax.logits, logits, T * E * 4), "copy");
+    MOE_HIP(copy(ax.scores, scores != nullptr ? scores : logits, T * E * 4), "copy");
+    MOE_HIP(copy(ax.topk_idx, idx, T * k * 4), "copy");
+    MOE_HIP(copy(ax.topk_w, w, T * k * 4), "copy");
+    MOE_HIP(copy(ax.offsets, offsets, E * 4), "copy");
+    MOE_HIP(copy(ax.dest, dest, T * k * 4), "copy");
+    MOE_HIP(copy(ax.perm, perm, static_cast<size_t>(D.R) * 4), "copy");
+  }
   return MOE_OK;
 }
 
@@ -595,6 +658,181 @@ moe_status moe_workspace_size_ex(const moe_config* cfg, const moe_variant* varia
   MOE_CHECK(check_variant(variant, &D));
   if (bytes == nullptr) return fail(MOE_EINVAL, "bytes is NULL");
   *bytes = layout_of(D).total;
+  return MOE_OK;
+}
+
+moe_status moe_workspace_size_train(const moe_config* cfg, const moe_variant* variant, size_t* bytes) {
+  Derived D;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(check_variant(variant, &D));
+  if (D.dffs > 0) return fail(MOE_EUNSUPPORTED, "the backward pass does not cover a shared expert");
+  if (bytes == nullptr) return fail(MOE_EINVAL, "bytes is NULL");
+  D.train = true;
+  *bytes = layout_of(D).total;
+  return MOE_OK;
+}
+
+moe_status moe_forward_train(const moe_config* cfg, const moe_variant* variant, const void* x, const void* Wg,
+                             const float* bg, const void* W1, const void* b1, const void* W2, const void* b2, void* y,
+                             float* f, float* P, float* L, int32_t* counts, int32_t* kept,
+                             const moe_forward_aux* aux, void* ws, size_t ws_bytes, moe_stream_t stream) {
+  return forward_impl(cfg, variant, x, Wg, bg, W1, b1, W2, b2, y, f, P, L, counts, kept, aux, ws, ws_bytes, stream,
+                      true);
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const void* x, const void* Wg,
+                        const void* W1, const void* W2, const void* dy, float lam, void* dx, float* dWg, float* dbg,
+                        float* dW1, float* db1, float* dW2, float* db2, const moe_backward_aux* aux, void* ws,
+                        size_t ws_bytes, moe_stream_t stream) {
+  Derived D;
+  Layout Lw;
+  MOE_CHECK(check_config(cfg, &D));
+  MOE_CHECK(check_variant(variant, &D));
+  if (D.dffs > 0) return fail(MOE_EUNSUPPORTED, "the backward pass does not cover a shared expert");
+  if (!std::isfinite(lam)) return fail(MOE_EINVAL, "lam must be finite");
+  D.train = true;
+  MOE_CHECK(need(x, 16, "x"));
+  MOE_CHECK(need(Wg, 16, "Wg"));
+  MOE_CHECK(need(W1, 16, "W1"));
+  MOE_CHECK(need(W2, 16, "W2"));
+  MOE_CHECK(need(dy, 16, "dy"));
+  MOE_CHECK(need(dx, 16, "dx"));
+  MOE_CHECK(need(dWg, 4, "dWg"));
+  MOE_CHECK(need(dbg, 4, "dbg", true));
+  MOE_CHECK(need(dW1, 4, "dW1"));
+  MOE_CHECK(need(db1, 4, "db1", true));
+  MOE_CHECK(need(dW2, 4, "dW2"));
+  MOE_CHECK(need(db2, 4, "db2", true));
+  moe_backward_aux none{};
+  const moe_backward_aux& ax = aux != nullptr ? *aux : none;
+  if (ax.stage_events != nullptr)
+    for (int i = 0; i <= MOE_BACKWARD_STAGES; ++i)
+      if (ax.stage_events[i] == nullptr) return fail(MOE_EINVAL, "aux.stage_events has a NULL event");
+  MOE_CHECK(need(ax.dz, 4, "aux.dz", true));
+  MOE_CHECK(need_ws(D, ws, ws_bytes, &Lw));
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipEvent_t* ev = reinterpret_cast<hipEvent_t*>(ax.stage_events);
+  const int bf = D.bf16 ? 1 : 0;
+  const int C = clamp_c(D);
+  const int E = D.E, T = D.T, d = D.d, dff = D.dff, R = D.R;
+  const bool has_scores = D.noise != moe::kNoiseNone || D.tau != 1.0f;
+  const int32_t* kept = at<int32_t>(ws, Lw.kept_s);
+  const int32_t* offsets = at<int32_t>(ws, Lw.offsets);
+  const int32_t* perm = at<int32_t>(ws, Lw.perm);
+  const int32_t* dest = at<int32_t>(ws, Lw.dest);
+  int32_t* koff = at<int32_t>(ws, Lw.koff);
+  float* wrow = at<float>(ws, Lw.wrow);
+  float* dz = ax.dz != nullptr ? ax.dz : at<float>(ws, Lw.dz);
+  void* dA = at<void>(ws, Lw.dA);
+  moe::FfnArgs fa{};                         // the forward's GEMM2 split decides whether y_perm2 holds a part
+  fa.E = E;
+  fa.d = d;
+  fa.d_ffn = dff;
+  fa.R = R;
+  fa.C = C;
+  fa.bf16 = bf;
+  const bool fwd_split = moe::ffn_splits(fa) == 2;
+  const bool dx_split = moe::bwd_dx_splits(R, E, C, d, dff, bf) == 2;
+  float* dXp = at<float>(ws, Lw.dXp);
+  float* dXp2 = dx_split ? at<float>(ws, Lw.dXp2) : nullptr;
+
+  if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
+  // 1. router backward: dw, the softmax backward and the balance term -> dz; row weights
+  moe::BwdRouterArgs ra{};
+  ra.dy = dy;
+  ra.y_perm = at<float>(ws, Lw.y_perm);
+  ra.y_perm2 = fwd_split ? at<float>(ws, Lw.y_perm2) : nullptr;
+  ra.dest = dest;
+  ra.idx = at<int32_t>(ws, Lw.idx);
+  ra.cand = D.policy == MOE_DROP_REROUTE ? at<int32_t>(ws, Lw.cand) : nullptr;
+  ra.w = at<float>(ws, Lw.w);
+  ra.s = has_scores ? at<float>(ws, Lw.scores) : at<float>(ws, Lw.logits);
+  ra.f = at<float>(ws, Lw.f_s);
+  ra.lam_E_over_T = static_cast<float>(static_cast<double>(lam) * E / T);
+  ra.tau = D.tau;
+  ra.T = T;
+  ra.d = d;
+  ra.E = E;
+  ra.k = D.k;
+  ra.wrow = wrow;
+  ra.dz = dz;
+  MOE_HIP(moe::launch_bwd_router(ra, bf, st), "bwd_router");
+  MOE_HIP(moe::launch_wgrad_offsets(kept, E, koff, st), "wgrad_offsets");
+  if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
+  // 2. the weights transposed: W2 [E,d,dff] -> W2T [E,dff,d]; W1 [E,dff,d] -> W1T [E,d,dff]
+  void* W2T = at<void>(ws, Lw.W2T);
+  void* W1T = at<void>(ws, Lw.W1T);
+  MOE_HIP(moe::launch_transpose(W2, W2T, E, d, dff, bf, st), "transpose W2");
+  MOE_HIP(moe::launch_transpose(W1, W1T, E, dff, d, bf, st), "transpose W1");
+  if (ev) MOE_HIP(hipEventRecord(ev[2], st), "event");
+  // 3. dA = (w dy W2) * act'(a); dXp = dA W1
+  moe::BwdDactArgs da{};
+  const bool gathers = bwd_gathers(D);
+  if (gathers) {
+    da.A = dy;
+    da.rows = perm;
+    da.a_rows = T;
+  } else {
+    void* dyp = at<void>(ws, Lw.dyp);
+    MOE_HIP(moe::launch_gather(dy, perm, kept, offsets, E, R, static_cast<int>(d * D.esize), dyp, st), "gather dy");
+    da.A = dyp;
+  }
+  da.W2T = W2T;
+  da.wrow = wrow;
+  da.pre = at<void>(ws, Lw.pre);
+  da.dA = dA;
+  da.kept = kept;
+  da.offsets = offsets;
+  da.E = E;
+  da.d = d;
+  da.d_ffn = dff;
+  da.R = R;
+  da.C = C;
+  da.bf16 = bf;
+  da.act = D.act;
+  MOE_HIP(moe::launch_bwd_dact(da, st), "bwd_dact");
+  if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
+  moe::BwdDxArgs dxa{dA, W1T, dXp, dXp2, kept, offsets, E, d, dff, R, C, bf};
+  MOE_HIP(moe::launch_bwd_dx(dxa, st), "bwd_dx");
+  if (ev) MOE_HIP(hipEventRecord(ev[4], st), "event");
+  // 4. weight gradients: each expert's rows as zero-padded columns, then per-expert products
+  const int ld = Lw.ld;
+  void* dOT = at<void>(ws, Lw.dOT);
+  void* HT = at<void>(ws, Lw.HT);
+  void* dAT = at<void>(ws, Lw.dAT);
+  void* XT = at<void>(ws, Lw.XT);
+  moe::RowsToColsArgs rc{};
+  rc.kept = kept;
+  rc.offsets = offsets;
+  rc.koff = koff;
+  rc.E = E;
+  rc.ld = ld;
+  rc.src = dy, rc.rows = perm, rc.scale = wrow, rc.ncol = d, rc.dst = dOT;
+  MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols dO");
+  rc.src = at<void>(ws, Lw.H), rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = HT;
+  MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols H");
+  rc.src = dA, rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = dAT;
+  MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols dA");
+  rc.src = x, rc.rows = perm, rc.scale = nullptr, rc.ncol = d, rc.dst = XT;
+  MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols X");
+  if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
+  moe::WgradArgs wa{dOT, HT, dW2, kept, koff, E, d, dff, ld, C, bf};
+  MOE_HIP(moe::launch_wgrad(wa, st), "wgrad W2");
+  MOE_HIP(moe::launch_zero_empty(dW2, kept, E, static_cast<size_t>(d) * dff, st), "zero W2");
+  if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");
+  moe::WgradArgs wb{dAT, XT, dW1, kept, koff, E, dff, d, ld, C, bf};
+  MOE_HIP(moe::launch_wgrad(wb, st), "wgrad W1");
+  MOE_HIP(moe::launch_zero_empty(dW1, kept, E, static_cast<size_t>(d) * dff, st), "zero W1");
+  if (ev) MOE_HIP(hipEventRecord(ev[7], st), "event");
+  if (db2 != nullptr) MOE_HIP(moe::launch_segment_rowsum(dOT, kept, koff, E, d, ld, bf, db2, st), "db2");
+  if (db1 != nullptr) MOE_HIP(moe::launch_segment_rowsum(dAT, kept, koff, E, dff, ld, bf, db1, st), "db1");
+  // 5. router weights and the input gradient
+  MOE_HIP(moe::launch_dwg(x, dz, T, d, E, bf, at<float>(ws, Lw.dwg), dWg, st), "dWg");
+  if (dbg != nullptr) MOE_HIP(moe::launch_colsum(dz, T, E, dbg, st), "dbg");
+  moe::DxArgs xa{dXp, dXp2, dest, dz, Wg, T, d, E, D.k, dx};
+  MOE_HIP(moe::launch_dx(xa, bf, st), "dx");
+  if (ev) MOE_HIP(hipEventRecord(ev[8], st), "event");
   return MOE_OK;
 }
 

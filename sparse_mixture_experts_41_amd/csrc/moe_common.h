@@ -129,6 +129,18 @@ __device__ __forceinline__ float gelu_bf16_path(float v) {
   return fmaf(-fminf(a, 3.4028235e38f), h, fmaxf(v, 0.0f));
 }
 
+// Derivatives for the backward pass, float32 with the library erf and exponential:
+// GeLU'(v) = Phi(v) + v phi(v), phi(v) = e^(-v^2 / 2) / sqrt(2 pi); SiLU'(v) = s (1 + v (1 - s)),
+// s = sigmoid(v).
+__device__ __forceinline__ float gelu_grad_exact(float v) {
+  return 0.5f * (1.0f + erff(v * 0.70710678118654752440f)) + v * 0.39894228040143267794f * expf(-0.5f * v * v);
+}
+
+__device__ __forceinline__ float silu_grad_exact(float v) {
+  const float s = 1.0f / (1.0f + expf(-v));
+  return s * (1.0f + v * (1.0f - s));
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 }  // namespace moe

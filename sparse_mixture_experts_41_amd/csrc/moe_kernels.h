@@ -114,6 +114,7 @@ struct FfnArgs {
   int E, d, d_ffn, R, C;
   int bf16;
   int act;                // kActGelu or kActSilu
+  void* pre;              // [R,d_ffn] or null: GEMM1 also stores its pre-activation (training)
 };
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
 // copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
@@ -150,5 +151,118 @@ hipError_t launch_combine(const float* y_perm, const float* y_perm2, const float
 
 hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,
                         float* L, hipStream_t stream);
+
+// ---------------------------------------------------------------------------------------
+// Backward pass.
+constexpr int kWgradK = 32;   // rows of a weight-gradient product are padded to this granule
+
+// dA[r] = (A_row(r) W2_e) * wrow[r] * act'(pre[r]) over each expert's segment rows, where
+// A_row(r) = A[rows[r]] (rows set: the bf16 MFMA path reads dy through the permutation) or A[r]
+// (an expert-sorted copy); W2T [E, d_ffn, d] is W2 transposed. dA and pre: [R, d_ffn] dtype.
+struct BwdDactArgs {
+  const void* A;
+  const int32_t* rows;
+  int a_rows;
+  const void* W2T;
+  const float* wrow;
+  const void* pre;
+  void* dA;
+  const int32_t* kept;
+  const int32_t* offsets;
+  int E, d, d_ffn, R, C, bf16, act;
+};
+hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream);
+
+// dXp[r] = dA[r] W1_e (float, [R, d]); W1T [E, d, d_ffn] is W1 transposed. With
+// bwd_dx_splits() == 2 the result is dXp + dXp2.
+struct BwdDxArgs {
+  const void* dA;
+  const void* W1T;
+  float* dXp;
+  float* dXp2;
+  const int32_t* kept;
+  const int32_t* offsets;
+  int E, d, d_ffn, R, C, bf16;
+};
+int bwd_dx_splits(int R, int E, int C, int d, int d_ffn, int bf16);
+hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream);
+
+// out[e] = A[:, koff[e] : +K_e] B[:, koff[e] : +K_e]^T (float [E, M, N]) with K_e = kept[e]
+// rounded up to kWgradK; A [M, ld] and B [N, ld] dtype hold each expert's rows as columns, zero
+// past kept[e]. Experts with kept[e] = 0 are not written.
+struct WgradArgs {
+  const void* A;
+  const void* B;
+  float* out;
+  const int32_t* kept;
+  const int32_t* koff;
+  int E, M, N, ld, C, bf16;
+};
+hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream);
+
+// koff[e] = sum over e' < e of kept[e'] rounded up to kWgradK; koff[E] = the total.
+hipError_t launch_wgrad_offsets(const int32_t* kept, int E, int32_t* koff, hipStream_t stream);
+
+// Router backward, one wave per token: wrow[r] = w of the slot at row r; dz [T,E] = the
+// gradient of sum(dy * y) + lam * L with respect to the logits.
+struct BwdRouterArgs {
+  const void* dy;         // [T,d] dtype
+  const float* y_perm;    // [R,d] expert outputs (GEMM2 result)
+  const float* y_perm2;   // [R,d] or null: GEMM2's second K part
+  const int32_t* dest;    // [T,k]
+  const int32_t* idx;     // [T,k] the router's choices
+  const int32_t* cand;    // [T,k] or null: rerouted experts (-1: the slot stays at idx)
+  const float* w;         // [T,k] combine weights
+  const float* s;         // [T,E] scores (or logits when they are the scores)
+  const float* f;         // [E]
+  float lam_E_over_T;     // lam * E / T
+  float tau;
+  int T, d, E, k;
+  float* wrow;            // [R]
+  float* dz;              // [T,E]
+};
+hipError_t launch_bwd_router(const BwdRouterArgs& a, int bf16, hipStream_t stream);
+
+// dst[b] = src[b] transposed, [B][Rn][Cn] -> [B][Cn][Rn] (Rn, Cn multiples of 4).
+hipError_t launch_transpose(const void* src, void* dst, int B, int Rn, int Cn, int bf16, hipStream_t stream);
+
+// Expert-sorted rows to zero-padded columns (see WgradArgs): dst [ncol, ld] with
+// dst[n][koff[e] + i] = scale[r] * src[rows ? rows[r] : r][n], r = offsets[e] + i, i < kept[e];
+// zero for kept[e] <= i < K_e. ld is a multiple of kWgradK at least sum_e K_e.
+struct RowsToColsArgs {
+  const void* src;
+  const int32_t* rows;    // or null
+  const float* scale;     // [R] or null
+  const int32_t* kept;
+  const int32_t* offsets;
+  const int32_t* koff;
+  int E, ncol, ld;
+  void* dst;
+};
+hipError_t launch_rows_to_cols(const RowsToColsArgs& a, int bf16, hipStream_t stream);
+
+// db[e][m] = sum_i src[m][koff[e] + i] over expert e's padded columns (float [E, M]).
+hipError_t launch_segment_rowsum(const void* src, const int32_t* kept, const int32_t* koff, int E, int M, int ld,
+                                 int bf16, float* db, hipStream_t stream);
+
+// out[e] = 0 (per_expert floats) for every expert e with kept[e] = 0.
+hipError_t launch_zero_empty(float* out, const int32_t* kept, int E, size_t per_expert, hipStream_t stream);
+
+// dWg = dz^T x (float [E,d]) through part [dwg_slices(T,d), E, d] partial sums.
+int dwg_slices(int T, int d);
+hipError_t launch_dwg(const void* x, const float* dz, int T, int d, int E, int bf16, float* part, float* dWg,
+                      hipStream_t stream);
+
+// dx[t] = sum_j (dXp + dXp2)[dest_tj] + dz_t W_g (dtype [T,d]).
+struct DxArgs {
+  const float* dXp;
+  const float* dXp2;      // or null
+  const int32_t* dest;
+  const float* dz;
+  const void* Wg;
+  int T, d, E, k;
+  void* dx;
+};
+hipError_t launch_dx(const DxArgs& a, int bf16, hipStream_t stream);
 
 }  // namespace moe

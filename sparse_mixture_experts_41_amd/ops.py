@@ -11,11 +11,13 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import MOE_FORWARD_STAGES, STAGE_NAMES, MoeConfig, MoeForwardAux, make_config
+from ._lib import (BWD_STAGE_NAMES, MOE_BACKWARD_STAGES, MOE_FORWARD_STAGES, STAGE_NAMES, MoeBackwardAux, MoeConfig,
+                   MoeForwardAux, make_config)
 
 __all__ = ["make_config", "capacity", "workspace_size", "workspace", "route", "dispatch", "expert_ffn", "combine",
            "forward", "ForwardPlan", "StageEvents", "STAGE_NAMES", "MoeConfig", "make_variant", "workspace_size_ex",
-           "temperature_at", "DROP_POLICIES", "ROUTE_STAT_NAMES"]
+           "temperature_at", "DROP_POLICIES", "ROUTE_STAT_NAMES", "TrainPlan", "BWD_STAGE_NAMES",
+           "MOE_BACKWARD_STAGES", "workspace_size_train"]
 
 
 def _storage_dtype(cfg: MoeConfig) -> torch.dtype:
@@ -157,29 +159,30 @@ def combine(cfg: MoeConfig, y_perm, dest, topk_w, counts=None, prob_colsum=None,
 
 
 class StageEvents:
-    """MOE_FORWARD_STAGES + 1 HIP events for moe_forward's per-stage timing."""
+    """n_stages + 1 HIP events for per-stage timing (moe_forward's MOE_FORWARD_STAGES by default)."""
 
-    def __init__(self):
+    def __init__(self, n_stages: int = MOE_FORWARD_STAGES):
+        self.n = n_stages
         self._hip = ctypes.CDLL("libamdhip64.so")
         self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        self.array = (ctypes.c_void_p * (MOE_FORWARD_STAGES + 1))()
-        for i in range(MOE_FORWARD_STAGES + 1):
+        self.array = (ctypes.c_void_p * (self.n + 1))()
+        for i in range(self.n + 1):
             ev = ctypes.c_void_p()
             if self._hip.hipEventCreate(ctypes.byref(ev)) != 0:
                 raise RuntimeError("hipEventCreate failed")
             self.array[i] = ev
-        self.totals = [0.0] * MOE_FORWARD_STAGES
+        self.totals = [0.0] * self.n
         self.samples = 0
 
     def accumulate(self) -> list[float]:
         """Per-stage milliseconds of the last recorded forward (synchronises on the last event)."""
-        if self._hip.hipEventSynchronize(self.array[MOE_FORWARD_STAGES]) != 0:
+        if self._hip.hipEventSynchronize(self.array[self.n]) != 0:
             raise RuntimeError("hipEventSynchronize failed")
         ms = []
-        for i in range(MOE_FORWARD_STAGES):
+        for i in range(self.n):
             t = ctypes.c_float()
             if self._hip.hipEventElapsedTime(ctypes.byref(t), self.array[i], self.array[i + 1]) != 0:
                 raise RuntimeError("hipEventElapsedTime failed")
@@ -193,7 +196,7 @@ class StageEvents:
         return {name: self.totals[i] / n for i, name in enumerate(STAGE_NAMES)}
 
     def close(self):
-        for i in range(MOE_FORWARD_STAGES + 1):
+        for i in range(self.n + 1):
             if self.array[i]:
                 self._hip.hipEventDestroy(self.array[i])
                 self.array[i] = None
@@ -248,7 +251,8 @@ class ForwardPlan:
     """Preallocated outputs and workspace for repeated moe_forward calls on fixed tensors.
     ``variant`` (from make_variant) selects moe_forward_ex."""
 
-    def __init__(self, cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True, variant=None):
+    def __init__(self, cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True, variant=None,
+                 workspace_bytes: int | None = None):
         sd = _storage_dtype(cfg)
         T, d, E, k, dff = cfg.T, cfg.d, cfg.E, cfg.k, cfg.d_ffn
         _expect(x, "x", (T, d), sd)
@@ -262,7 +266,9 @@ class ForwardPlan:
         self.cfg = cfg
         self.inputs = (x, Wg, bg, W1, b1, W2, b2)
         self.variant = variant
-        if variant is None:
+        if workspace_bytes is not None:
+            self.ws = torch.empty((workspace_bytes,), dtype=torch.uint8, device=dev)
+        elif variant is None:
             self.ws = workspace(cfg, dev)
         else:
             self.ws = torch.empty((workspace_size_ex(cfg, variant[0]),), dtype=torch.uint8, device=dev)
@@ -301,15 +307,67 @@ class ForwardPlan:
         args = (_ptr(x), _ptr(Wg), _ptr(bg), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
                 _ptr(o["y"]), _ptr(o["f"]), _ptr(o["P"]), _ptr(o["L"]), _ptr(o["counts"]), _ptr(o["kept"]),
                 ctypes.byref(self.aux), _ptr(self.ws), self.ws.numel(), _stream(stream))
-        lib = _lib.load()
-        if self.variant is None:
-            _lib.check(lib.moe_forward(ctypes.byref(self.cfg), *args))
-        else:
-            _lib.check(lib.moe_forward_ex(ctypes.byref(self.cfg), ctypes.byref(self.variant[0]), *args))
+        self._call(_lib.load(), ctypes.byref(self.cfg), args)
         return o
+
+    def _call(self, lib, cfg, args):
+        if self.variant is None:
+            _lib.check(lib.moe_forward(cfg, *args))
+        else:
+            _lib.check(lib.moe_forward_ex(cfg, ctypes.byref(self.variant[0]), *args))
 
 
 def forward(cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True, variant=None) -> dict:
     """The whole layer (moe_forward, or moe_forward_ex with a variant); returns y, f, P, L,
     counts, kept (+ routing arrays)."""
     return ForwardPlan(cfg, x, Wg, bg, W1, b1, W2, b2, keep_routing=keep_routing, variant=variant).run()
+
+
+def workspace_size_train(cfg: MoeConfig, variant=None) -> int:
+    n = ctypes.c_size_t()
+    v = ctypes.byref(variant[0]) if variant is not None else None
+    _lib.check(_lib.load().moe_workspace_size_train(ctypes.byref(cfg), v, ctypes.byref(n)))
+    return n.value
+
+
+class TrainPlan(ForwardPlan):
+    """moe_forward_train then moe_backward on fixed tensors: ``run()`` is the training forward
+    (outputs as ForwardPlan), ``backward(dy, lam)`` the gradients (float32 weight gradients,
+    dx in the storage dtype). The workspace holds the forward's saved state in between."""
+
+    def __init__(self, cfg: MoeConfig, x, Wg, bg, W1, b1, W2, b2, keep_routing: bool = True, variant=None,
+                 bias_grads: bool = True):
+        super().__init__(cfg, x, Wg, bg, W1, b1, W2, b2, keep_routing=keep_routing, variant=variant,
+                         workspace_bytes=workspace_size_train(cfg, variant))
+        T, d, E, dff = cfg.T, cfg.d, cfg.E, cfg.d_ffn
+        dev = x.device
+        f32 = torch.float32
+        self.grads = {
+            "dx": torch.empty((T, d), dtype=_storage_dtype(cfg), device=dev),
+            "dWg": torch.empty((E, d), dtype=f32, device=dev),
+            "dW1": torch.empty((E, dff, d), dtype=f32, device=dev),
+            "dW2": torch.empty((E, d, dff), dtype=f32, device=dev),
+            "dz": torch.empty((T, E), dtype=f32, device=dev),
+        }
+        if bias_grads:
+            self.grads.update(dbg=torch.empty((E,), dtype=f32, device=dev),
+                              db1=torch.empty((E, dff), dtype=f32, device=dev),
+                              db2=torch.empty((E, d), dtype=f32, device=dev))
+        self.baux = MoeBackwardAux()
+        self.baux.dz = self.grads["dz"].data_ptr()
+
+    def _call(self, lib, cfg, args):
+        v = ctypes.byref(self.variant[0]) if self.variant is not None else None
+        _lib.check(lib.moe_forward_train(cfg, v, *args))
+
+    def backward(self, dy, lam: float = 0.0, events: StageEvents | None = None, stream=None) -> dict:
+        _expect(dy, "dy", (self.cfg.T, self.cfg.d), _storage_dtype(self.cfg))
+        x, Wg, bg, W1, b1, W2, b2 = self.inputs
+        g = self.grads
+        self.baux.stage_events = ctypes.cast(events.array, ctypes.c_void_p).value if events is not None else None
+        v = ctypes.byref(self.variant[0]) if self.variant is not None else None
+        _lib.check(_lib.load().moe_backward(
+            ctypes.byref(self.cfg), v, _ptr(x), _ptr(Wg), _ptr(W1), _ptr(W2), _ptr(dy), float(lam),
+            _ptr(g["dx"]), _ptr(g["dWg"]), _ptr(g.get("dbg")), _ptr(g["dW1"]), _ptr(g.get("db1")), _ptr(g["dW2"]),
+            _ptr(g.get("db2")), ctypes.byref(self.baux), _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        return g

@@ -241,3 +241,32 @@ def check_forward_sampled(p: Problem, gpu: dict | None = None) -> dict:
     stats.update(kept=int(chk["dispatch"]["kept"].sum()), drops=int(chk["dispatch"]["drops"].sum()),
                  rows=len(rows))
     return stats
+
+
+# ---------------------------------------------------------------- backward
+def run_train(p: Problem, dy_arr, lam: float) -> dict:
+    """moe_forward_train then moe_backward; forward outputs and gradients on the host."""
+    variant = p.variant()
+    plan = ops.TrainPlan(p.cfg, *p.args(), variant=variant)
+    fwd = plan.run()
+    dy = to_device(dy_arr, p.shape.dtype)
+    g = plan.backward(dy, lam)
+    torch.cuda.synchronize()
+    host = lambda v: v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()
+    out = {k: host(v) for k, v in fwd.items()}
+    out.update({k: host(v) for k, v in g.items()})
+    return out
+
+
+def backward_errors(gpu: dict, ref: dict) -> dict:
+    """Per gradient: relative Frobenius error and max error over max |ref|."""
+    res = {}
+    for key in ("dx", "dWg", "dbg", "dW1", "db1", "dW2", "db2", "dz"):
+        if key not in gpu:
+            continue
+        g = np.asarray(gpu[key], np.float64)
+        r = np.asarray(ref[key], np.float64)
+        nr = np.linalg.norm(r)
+        res[key] = (float(np.linalg.norm(g - r) / max(nr, 1e-300)),
+                    float(np.max(np.abs(g - r)) / max(np.max(np.abs(r)), 1e-300)))
+    return res

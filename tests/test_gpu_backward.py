@@ -1,0 +1,103 @@
+"""GPU parity of the backward pass (moe_forward_train + moe_backward) against oracle.backward.
+
+The oracle re-derives the routing from the GPU's own float32 scores, so both sides take the
+same discrete decisions; every gradient is then compared as a whole tensor. Cases cover the
+float32 path (plain FMA products), the bf16 MFMA path (gathered dy, activation-gradient
+epilogue, weight-gradient mode), the bf16 GEMV path (at most 16 rows per expert), a split
+dx product together with a split forward GEMM2, experts without rows, every capacity policy,
+both activations, Gumbel and Gaussian noise, temperature and the balance term.
+
+Tolerances (relative Frobenius error of each gradient tensor, and max error over max |ref|):
+  float32 storage: 3e-6 and 6e-6 (float32 sums of at most a few thousand terms: about
+  sqrt(n) 2^-24 relative; measured 2e-7 to 5e-7).
+  bf16 storage: 1.5e-2 and 3e-2. The bf16 path rounds the pre-activations, the hidden layer H,
+  dA and w * dy to bf16 (8 significant bits, relative error up to 2^-9 each) before they enter
+  float32-accumulated products; the roundings are independent across terms, so a long sum
+  keeps a relative error near 2^-9 = 2e-3 (measured 1.3e-3 to 2.4e-3). db_g is the exception:
+  each token's dz sums to zero over the experts, so the sum over tokens cancels and its
+  relative error is larger (measured up to 6e-3); the bounds leave a factor of 2.5 over that.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import MoEShape, make_upstream_grad
+
+from .parity import Problem, backward_errors, host_values, run_train
+
+pytestmark = pytest.mark.gpu
+
+S = MoEShape
+TOL = {"f32": (3e-6, 6e-6), "bf16": (1.5e-2, 3e-2)}
+
+CASES = {
+    # name: (shape, bias_std, activation, noise_std, policy, lam)
+    "f32_gelu": (S("f32_gelu", T=200, d=64, E=4, k=2, d_ffn=96, capacity_factor=0.8, temperature=0.9,
+                   dtype="f32"), 0.1, "gelu", 0.0, "token", 0.3),
+    "f32_silu_reroute_gumbel": (S("f32_silu_reroute_gumbel", T=150, d=64, E=5, k=2, d_ffn=64, capacity_factor=0.7,
+                                  gumbel=True, temperature=0.8, dtype="f32", seed=3), 0.1, "silu", 0.0, "reroute",
+                                0.1),
+    "f32_random_gaussian_ragged": (S("f32_random_gaussian_ragged", T=163, d=96, E=6, k=2, d_ffn=72,
+                                     capacity_factor=0.6, dtype="f32", seed=5), 0.05, "gelu", 0.3, "random", 0.5),
+    "bf16_gemm_gelu": (S("bf16_gemm_gelu", T=1000, d=256, E=8, k=2, d_ffn=384, capacity_factor=0.9), 0.05, "gelu",
+                       0.0, "token", 0.05),
+    "bf16_gemm_silu_reroute": (S("bf16_gemm_silu_reroute", T=700, d=128, E=6, k=2, d_ffn=192, capacity_factor=0.7,
+                                 temperature=0.9, seed=2, wg_std=None), 0.05, "silu", 0.0, "reroute", 0.2),
+    "bf16_gemv": (S("bf16_gemv", T=50, d=128, E=16, k=2, d_ffn=128, capacity_factor=1.0, wg_std=None), 0.05,
+                  "gelu", 0.0, "token", 0.1),
+    "bf16_empty_experts": (S("bf16_empty_experts", T=300, d=128, E=64, k=1, d_ffn=64, capacity_factor=1.0,
+                             recipe="zipf_bias", wg_std=None, seed=4), 0.0, "gelu", 0.0, "random", 1.0),
+    "bf16_split_dx": (S("bf16_split_dx", T=2048, d=256, E=4, k=2, d_ffn=1024, capacity_factor=1.0, seed=6), 0.0,
+                      "gelu", 0.1, "token", 0.01),
+}
+
+
+def _oracle(p: Problem, gpu: dict, dy_host, lam):
+    sh = p.shape
+    return oracle.backward(*p.host_args(), dy_host, k=sh.k, capacity_factor=sh.capacity_factor, lam=lam,
+                           tau=sh.temperature, gumbel=sh.gumbel, seed=sh.seed, given_scores=gpu["scores"],
+                           act=p.activation, noise_std=p.noise_std, policy=p.drop_policy)
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward(name):
+    shape, bias, act, noise, policy, lam = CASES[name]
+    print(f"[gpu] backward {name} {shape} act={act} noise={noise} policy={policy} lam={lam}", flush=True)
+    p = Problem(shape, bias_std=bias, activation=act, noise_std=noise, drop_policy=policy)
+    dy_arr = make_upstream_grad(shape)
+    gpu = run_train(p, dy_arr, lam)
+    ref = _oracle(p, gpu, host_values(dy_arr, shape.dtype), lam)
+    # the forward of the training call routes exactly like the oracle
+    np.testing.assert_array_equal(gpu["dest"], ref["dest"], err_msg="dest")
+    errs = backward_errors(gpu, ref)
+    print(f"[gpu]   {name}: " + ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in errs.items()), flush=True)
+    fro, mx = TOL[shape.dtype]
+    for key, (e_fro, e_max) in errs.items():
+        assert e_fro <= fro and e_max <= mx, f"{key}: relative Frobenius {e_fro:.3e}, max {e_max:.3e}"
+    if name == "bf16_empty_experts":
+        empty = np.flatnonzero(gpu["kept"] == 0)
+        assert len(empty) > 0
+        assert np.all(gpu["dW1"][empty] == 0.0) and np.all(gpu["dW2"][empty] == 0.0)
+        assert np.all(gpu["db1"][empty] == 0.0) and np.all(gpu["db2"][empty] == 0.0)
+
+
+def test_backward_is_deterministic():
+    shape = CASES["bf16_gemm_gelu"][0]
+    p = Problem(shape, bias_std=0.05)
+    dy_arr = make_upstream_grad(shape)
+    a = run_train(p, dy_arr, 0.05)
+    b = run_train(p, dy_arr, 0.05)
+    for key in ("dx", "dWg", "dW1", "dW2", "db1", "db2", "dbg", "dz"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+def test_training_forward_matches_the_plain_forward():
+    shape = CASES["bf16_gemm_silu_reroute"][0]
+    p = Problem(shape, bias_std=0.05, activation="silu", drop_policy="reroute")
+    from .parity import run_forward
+    a = run_forward(p)
+    b = run_train(p, make_upstream_grad(shape), 0.0)
+    np.testing.assert_array_equal(a["y"], b["y"])
+    for key in ("topk_idx", "topk_w", "dest", "kept", "counts", "f", "L"):
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)

@@ -29,6 +29,7 @@ _CHUNK = 1 << 22
 STREAM_X, STREAM_WG, STREAM_BG, STREAM_W1, STREAM_B1, STREAM_W2, STREAM_B2 = 0, 1, 2, 3, 4, 5, 6
 STREAM_CENTRES, STREAM_CLUSTER, STREAM_NOISE = 7, 8, 9
 STREAM_W1S, STREAM_B1S, STREAM_W2S, STREAM_B2S = 10, 11, 12, 13
+STREAM_DY = 14
 
 N_CLUSTERS = 512
 CLUSTER_ZIPF_S = 1.2
@@ -173,3 +174,9 @@ def make_shared_expert(cfg: MoEShape, d_ffn_s: int, bias_std: float = 0.0) -> di
         b1s = _store(normal_f32(seed, STREAM_B1S, (d_ffn_s,), bias_std), dt)
         b2s = _store(normal_f32(seed, STREAM_B2S, (d,), bias_std), dt)
     return {"W1s": _store(W1s, dt), "b1s": b1s, "W2s": _store(W2s, dt), "b2s": b2s}
+
+
+def make_upstream_grad(cfg: MoEShape, std: float = 1.0) -> np.ndarray:
+    """The gradient arriving at the layer's output for the backward pass: dy [T, d] ~ N(0, std),
+    in storage form."""
+    return _store(normal_f32(cfg.seed, STREAM_DY, (cfg.T, cfg.d), std), cfg.dtype)
