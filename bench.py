@@ -52,6 +52,9 @@ def _args():
                     help="also compute the five routing statistics in the timed steps and report them")
     ap.add_argument("--capacity-factor", type=float, default=None,
                     help="override the workload's capacity factor (reported in config)")
+    ap.add_argument("--train", action="store_true",
+                    help="time the training step instead: moe_forward_train + moe_backward (one JSON line)")
+    ap.add_argument("--lam", type=float, default=0.01, help="weight of the balance loss in the training step")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -121,6 +124,71 @@ def cpu_baseline(shape, arrays, n_tokens: int, variant: dict | None = None) -> d
             "seconds": t1 - t0}
 
 
+def train_step(args, shape, cfg, tensors, variant, ops, torch) -> int:
+    """The training step: moe_forward_train then moe_backward on synthetic dy, K timed steps."""
+    from workloads import make_upstream_grad
+
+    plan = ops.TrainPlan(cfg, *tensors, keep_routing=False, variant=variant)
+    a = make_upstream_grad(shape)
+    dy = (torch.from_numpy(a.view("int16")).cuda().view(torch.bfloat16) if shape.dtype == "bf16"
+          else torch.from_numpy(a).cuda())
+    for _ in range(args.warmup):
+        plan.run()
+        plan.backward(dy, args.lam)
+    torch.cuda.synchronize()
+    fev = [ops.StageEvents() for _ in range(args.steps)]
+    bev = [ops.StageEvents(ops.MOE_BACKWARD_STAGES) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        plan.run(events=fev[i])
+        plan.backward(dy, args.lam, events=bev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    fst = {n: 0.0 for n in ops.STAGE_NAMES}
+    bst = {n: 0.0 for n in ops.BWD_STAGE_NAMES}
+    for evs, acc, names in ((fev, fst, ops.STAGE_NAMES), (bev, bst, ops.BWD_STAGE_NAMES)):
+        for ev in evs:
+            for n, v in zip(names, ev.accumulate()):
+                acc[n] += v / args.steps
+            ev.close()
+    kept = int(plan.out["kept"].sum().item())
+    T, d, E, k, dff = shape.T, shape.d, shape.E, shape.k, shape.d_ffn
+    gemm = 2.0 * d * dff * kept                   # one expert product over the kept rows
+    bwd_gemms = {n: gemm for n in ("dact_gemm", "dx_gemm", "wgrad_W2", "wgrad_W1")}
+    tflops = {n: f / (bst[n] * 1e-3) / 1e12 for n, f in bwd_gemms.items()}
+    dom = max(bwd_gemms, key=lambda n: bst[n])
+    fwd_ms, bwd_ms = sum(fst.values()), sum(bst.values())
+    line = {
+        "metric": "MoE-layer training step tokens/sec (forward + backward, bf16, 1 GPU)",
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded; workloads.make_inputs, make_upstream_grad)",
+        "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "d_ffn": dff,
+                   "capacity_factor": shape.capacity_factor, "lam": args.lam, "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": tflops[dom], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops[dom] / PEAK_BF16_TFLOPS, "traffic": None},
+        "forward_ms": fwd_ms,
+        "backward_ms": bwd_ms,
+        "backward_gemm_tflops": tflops,
+        "backward_gemm_frac": {n: v / PEAK_BF16_TFLOPS for n, v in tflops.items()},
+        "training_flops_frac": 6.0 * d * dff * kept / ((fwd_ms + bwd_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "stage_ms": fst,
+        "backward_stage_ms": bst,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _args()
     if args.gpus != 1:
@@ -176,6 +244,8 @@ def main() -> int:
             shared = tuple(dev(sh[n]) for n in ("W1s", "b1s", "W2s", "b2s"))
             variant_host["shared"] = sh
         variant = ops.make_variant(cfg, args.activation, args.noise_std, shared, args.drop_policy, route_stats)
+    if args.train:
+        return train_step(args, shape, cfg, tensors, variant, ops, torch)
     plan = ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant)
     for _ in range(args.warmup):
         plan.run()

@@ -11,7 +11,7 @@ hand-worked fixtures under ``tests/golden/``). The Philox generator is pinned to
 Philox-4x32-10 called as a library.
 """
 from . import philox
-from .moe_layer import (backward, balance_stats, brute_dense, capacity, combine, dispatch, dispatch_policy, dispatch_random,
+from .moe_layer import (backward, backward_entries, balance_stats, brute_dense, capacity, combine, dispatch, dispatch_policy, dispatch_random,
                         dispatch_reroute, expert, next_choices, reweight,
                         expert_ffn, forward, forward_rows, gelu, gelu_grad, logits, renormalise, route,
                         route_from_scores, routing_stats, scores, shared_expert, silu, silu_grad, softmax, temperature_at, topk)
@@ -19,5 +19,5 @@ from .moe_layer import (backward, balance_stats, brute_dense, capacity, combine,
 __all__ = ["philox", "capacity", "logits", "scores", "softmax", "topk", "renormalise", "route", "route_from_scores",
            "dispatch", "expert", "expert_ffn", "gelu", "silu", "combine", "balance_stats", "forward",
            "forward_rows", "brute_dense", "shared_expert", "temperature_at", "routing_stats", "dispatch_random",
-           "dispatch_reroute", "dispatch_policy", "next_choices", "reweight", "backward", "gelu_grad",
+           "dispatch_reroute", "dispatch_policy", "next_choices", "reweight", "backward", "backward_entries", "gelu_grad",
            "silu_grad"]

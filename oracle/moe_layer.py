@@ -571,3 +571,89 @@ def backward(x, Wg, bg, W1, b1, W2, b2, dy, *, k, capacity_factor, lam=0.0, tau=
     dx = dx + dz @ np.asarray(Wg, np.float64)
     return {"dx": dx, "dWg": dWg, "dbg": dbg, "dW1": dW1, "db1": db1, "dW2": dW2, "db2": db2, "dz": dz, "dw": dw,
             "w": w, "dest": dest, "final_idx": final_idx, "route": r, "dispatch": dsp}
+
+
+def backward_entries(x, Wg, bg, W1, b1, W2, b2, dy, *, tokens, w2_rows, w1_rows, k, capacity_factor, lam=0.0,
+                     tau=1.0, gumbel=False, seed=0, given_scores=None, act="gelu", noise_std=0.0,
+                     policy="token") -> dict:
+    """Selected entries of backward()'s gradients at any size, by the same steps restricted to
+    what they depend on: dx and dz rows of ``tokens``; rows m of dW2_e (and db2_e[m]) for
+    (e, m) in ``w2_rows``; rows n of dW1_e (and db1_e[n]) for (e, n) in ``w1_rows``.
+    Routing and dispatch cover all tokens; an expert's hidden layer is computed on all its
+    rows only when a dW2 row of it is asked for."""
+    x64 = np.asarray(x, np.float64)
+    dy64 = np.asarray(dy, np.float64)
+    T, d = x64.shape
+    E = Wg.shape[0]
+    r = route(x, Wg, bg, k, tau, gumbel, seed, given_scores, noise_std)
+    C = capacity(T, E, k, capacity_factor)
+    dsp, w = dispatch_policy(r, E, C, k, policy, seed)
+    final_idx = dsp.get("final_idx", r["idx"])
+    dest = dsp["dest"]
+    grad, fwd = ACTIVATION_GRADS[act], ACTIVATIONS[act]
+    p = r["p"]
+    f = dsp["counts"] / (k * T)
+
+    def pre(e, xs):
+        a = xs @ np.asarray(W1[e], np.float64).T
+        return a + np.asarray(b1[e], np.float64) if b1 is not None else a
+
+    def out(e, h):
+        o = h @ np.asarray(W2[e], np.float64).T
+        return o + np.asarray(b2[e], np.float64) if b2 is not None else o
+
+    def rows_of(e):                      # (t, j) of expert e's kept slots in row order
+        sl = sorted((int(dest[t, j]), t, j) for t in range(T) for j in range(k)
+                    if final_idx[t, j] == e and dest[t, j] >= 0)
+        return np.array([t for _, t, _ in sl], dtype=np.int64), np.array([j for _, _, j in sl], dtype=np.int64)
+
+    res = {"tokens": np.asarray(tokens), "dx": [], "dz": []}
+    for t in tokens:
+        dxt = np.zeros(d)
+        dw = np.zeros(k)
+        for j in range(k):
+            if dest[t, j] < 0:
+                continue
+            e = final_idx[t, j]
+            a = pre(e, x64[t][None, :])[0]
+            dw[j] = dy64[t] @ out(e, fwd(a)[None, :])[0]
+            da = (w[t, j] * dy64[t] @ np.asarray(W2[e], np.float64)) * grad(a)
+            dxt += da @ np.asarray(W1[e], np.float64)
+        S = p[t, final_idx[t]].sum()
+        dp = np.zeros(E)
+        corr = float(np.sum(dw * w[t]))
+        for j in range(k):
+            dp[final_idx[t, j]] += (dw[j] - corr) / S
+        dp += lam * E * f / T
+        dz = p[t] * (dp - np.sum(p[t] * dp)) / float(tau)
+        res["dz"].append(dz)
+        res["dx"].append(dxt + dz @ np.asarray(Wg, np.float64))
+    res["dx"], res["dz"] = np.array(res["dx"]).reshape(len(tokens), d), np.array(res["dz"]).reshape(len(tokens), E)
+    res["dW2"], res["db2"] = [], []
+    for e in sorted({e for e, _ in w2_rows}):
+        ts, js = rows_of(e)
+        h = fwd(pre(e, x64[ts])) if len(ts) else np.zeros((0, W1.shape[1]))
+        dO = w[ts, js][:, None] * dy64[ts]
+        for ee, m in w2_rows:
+            if ee == e:
+                res["dW2"].append(dO[:, m] @ h)
+                res["db2"].append(dO[:, m].sum())
+    res["dW1"], res["db1"] = [], []
+    for e, n in w1_rows:
+        ts, js = rows_of(e)
+        xs = x64[ts]
+        a_n = xs @ np.asarray(W1[e][n], np.float64) + (float(b1[e][n]) if b1 is not None else 0.0)
+        dh_n = (w[ts, js][:, None] * dy64[ts]) @ np.asarray(W2[e][:, n], np.float64)
+        da_n = dh_n * grad(a_n)
+        res["dW1"].append(da_n @ xs)
+        res["db1"].append(da_n.sum())
+    # entries in the order of the requests (dW2 rows grouped by expert above: restore)
+    order2 = sorted(range(len(w2_rows)), key=lambda i: (w2_rows[i][0], i))
+    dW2 = [None] * len(w2_rows)
+    db2 = [None] * len(w2_rows)
+    for pos, i in enumerate(order2):
+        dW2[i], db2[i] = res["dW2"][pos], res["db2"][pos]
+    res["dW2"], res["db2"] = np.array(dW2), np.array(db2)
+    res["dW1"], res["db1"] = np.array(res["dW1"]), np.array(res["db1"])
+    res["dispatch"], res["route"] = dsp, r
+    return res

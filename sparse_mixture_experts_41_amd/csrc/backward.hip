@@ -12,7 +12,7 @@
 //   GEMMs   dA = (w_r dy_t W2_e) * act'(a_r); dXp = dA W1_e                    (expert_gemm.hip)
 //           dW2_e = sum_r (w_r dy_t)^T h_r;  dW1_e = sum_r dA_r^T x_t          (wgrad mode)
 //   biases  db2_e = sum_r w_r dy_t; db1_e = sum_r dA_r                       (segment_rowsum)
-//   router  dW_g = dz^T x; db_g = sum_t dz_t                                   (dwg_*, colsum)
+//   router  dW_g = dz^T x; db_g = sum_t dz_t                                   (dwg_*)
 //   input   dx_t = sum_j dXp[dest_tj] + dz_t W_g                               (dx_kernel)
 // Every operand of the MFMA products is K-contiguous: the weights are transposed once per
 // call, and the weight-gradient products read each expert's rows as columns of transposed,
@@ -132,34 +132,58 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdRouterArgs a) {
   if (live) a.dz[static_cast<size_t>(t) * E + lane] = p * (dp - pdp) / a.tau;
 }
 
-// dst[b][c][r] = src[b][r][c] for [B][Rn][Cn] matrices (Rn, Cn multiples of 8); 64 x 64 tiles
-// through LDS, 4 elements per access (edge tiles guarded).
+// 16-byte vectors of a storage element type: 8 bf16 or 4 floats.
+template <typename T>
+struct Vec {
+  static constexpr int N = 16 / static_cast<int>(sizeof(T));
+  static constexpr int PAD = 4 / static_cast<int>(sizeof(T));   // one dword: odd row strides in dwords
+};
+
+// 16 bytes into LDS at a 4-byte aligned address (the padded tiles are not 16-byte aligned).
+__device__ __forceinline__ void lds_store16(void* p, const u32x4& q) {
+  uint32_t* d = static_cast<uint32_t*>(p);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) d[u] = q[u];
+}
+
+__device__ __forceinline__ float to_f32(u16 v) { return bf16_to_f32(v); }
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ void from_f32(float v, u16& o) { o = f32_to_bf16(v); }
+__device__ __forceinline__ void from_f32(float v, float& o) { o = v; }
+
+// dst[b][c][r] = src[b][r][c] for [B][Rn][Cn] matrices (Rn, Cn multiples of the vector width):
+// 64 x 64 tiles through LDS; 16-byte global loads and stores (a store packs one column's
+// vector of rows from LDS). The tile rows are 64 elements plus one dword, an odd number of
+// dwords, so the column gathers of a wave fall in distinct banks.
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ src, T* __restrict__ dst, int Rn,
                                                         int Cn) {
-  __shared__ T tile[64][64 + 4];
+  constexpr int V = Vec<T>::N, CH = 64 / V, P = 64 + Vec<T>::PAD;
+  __shared__ __attribute__((aligned(16))) T tile[64 * P];
   const int b = blockIdx.z;
-  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  // diagonal order: the workgroups running together read different source column blocks and
+  // write different destination row blocks, instead of striding one of them by a power of two
+  const int gx = gridDim.x, gy = gridDim.y;
+  const int lin = blockIdx.y * gx + blockIdx.x;
+  const int by = lin % gy, bx = (lin / gy + by) % gx;
+  const int r0 = by * 64, c0 = bx * 64;
   const T* s = src + static_cast<size_t>(b) * Rn * Cn;
   T* o = dst + static_cast<size_t>(b) * Rn * Cn;
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = ty + 16 * i;
-    if (r0 + r < Rn && c0 + 4 * tx < Cn) {   // Cn % 4 == 0: four columns together
-      const T* p = s + static_cast<size_t>(r0 + r) * Cn + c0 + 4 * tx;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) tile[r][4 * tx + u] = p[u];
-    }
+  for (int ch = threadIdx.x; ch < 64 * CH; ch += 256) {
+    const int r = ch / CH, cc = ch % CH;
+    if (r0 + r < Rn && c0 + V * cc < Cn)
+      lds_store16(&tile[r * P + V * cc],
+                  *reinterpret_cast<const u32x4*>(s + static_cast<size_t>(r0 + r) * Cn + c0 + V * cc));
   }
   __syncthreads();
+  for (int ch = threadIdx.x; ch < 64 * CH; ch += 256) {
+    const int c = ch / CH, rc = ch % CH;
+    if (c0 + c < Cn && r0 + V * rc < Rn) {
+      T v[V];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = ty + 16 * i;
-    if (c0 + c < Cn && r0 + 4 * tx < Rn) {   // Rn % 4 == 0
-      T* p = o + static_cast<size_t>(c0 + c) * Rn + r0 + 4 * tx;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) p[u] = tile[4 * tx + u][c];
+      for (int u = 0; u < V; ++u) v[u] = tile[(V * rc + u) * P + c];
+      *reinterpret_cast<u32x4*>(o + static_cast<size_t>(c0 + c) * Rn + r0 + V * rc) =
+          *reinterpret_cast<const u32x4*>(v);
     }
   }
 }
@@ -167,13 +191,15 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
 // Expert-sorted rows -> zero-padded columns: for expert e and i < K_e (kept[e] rounded up to
 // kWgradK), dst[n][koff[e] + i] = scale[r] * src[row(r)][n] with r = offsets[e] + i while
 // i < kept[e] (row(r) = rows[r] when gathering, else r; no scale when null), 0 past it.
-// Tiles of 32 padded positions x 64 columns; tile j belongs to the expert whose padded range
-// holds position 32 j; tiles past the last expert exit.
+// Tiles of 32 padded positions x 16 vectors of columns (128 bf16 or 64 floats); tile j
+// belongs to the expert whose padded range holds position 32 j; tiles past the last expert
+// exit. 16-byte loads of source rows; 16-byte stores of destination rows gathered from LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
-  __shared__ float tile[32][64 + 1];
+  constexpr int V = Vec<T>::N, TC = 16 * V, P = TC + Vec<T>::PAD, PC = 32 / V;
+  __shared__ __attribute__((aligned(16))) T tile[32 * P];
   __shared__ int s_e;
-  const int pos0 = blockIdx.y * 32, c0 = blockIdx.x * 64;
+  const int pos0 = blockIdx.y * 32, c0 = blockIdx.x * TC;
   if (threadIdx.x == 0) {
     int found = -1;
     for (int e = 0; e < a.E; ++e) {
@@ -187,59 +213,56 @@ __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
   if (e < 0) return;
   const int i0 = pos0 - a.koff[e];
   const int n_rows = a.kept[e];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const T* __restrict__ src = static_cast<const T*>(a.src);
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ii = ty + 4 * q;
-    float v = 0.0f;
-    if (i0 + ii < n_rows && c0 + tx < a.ncol) {
+  for (int ch = threadIdx.x; ch < 32 * 16; ch += 256) {
+    const int ii = ch / 16, cc = ch % 16;
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (i0 + ii < n_rows && c0 + V * cc < a.ncol) {
       const int r = a.offsets[e] + i0 + ii;
       const int sr = a.rows != nullptr ? a.rows[r] : r;
-      if constexpr (sizeof(T) == 2)
-        v = bf16_to_f32(src[static_cast<size_t>(sr) * a.ncol + c0 + tx]);
-      else
-        v = src[static_cast<size_t>(sr) * a.ncol + c0 + tx];
-      if (a.scale != nullptr) v *= a.scale[r];
+      q = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(sr) * a.ncol + c0 + V * cc);
+      if (a.scale != nullptr) {
+        const float sc = a.scale[r];
+        T* v = reinterpret_cast<T*>(&q);
+#pragma unroll
+        for (int u = 0; u < V; ++u) from_f32(to_f32(v[u]) * sc, v[u]);
+      }
     }
-    tile[ii][tx] = v;
+    lds_store16(&tile[ii * P + V * cc], q);
   }
   __syncthreads();
   T* __restrict__ dst = static_cast<T*>(a.dst);
-  // 64 destination rows of 32 positions each: 32 threads per row, 8 rows per pass
-  const int lr = threadIdx.x >> 5, lp = threadIdx.x & 31;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int c = lr + 8 * q;
+  for (int ch = threadIdx.x; ch < TC * PC; ch += 256) {
+    const int c = ch / PC, pc = ch % PC;
     if (c0 + c >= a.ncol) continue;
-    const float v = tile[lp][c];
-    T out;
-    if constexpr (sizeof(T) == 2)
-      out = f32_to_bf16(v);
-    else
-      out = v;
-    dst[static_cast<size_t>(c0 + c) * a.ld + pos0 + lp] = out;
+    T v[V];
+#pragma unroll
+    for (int u = 0; u < V; ++u) v[u] = tile[(V * pc + u) * P + c];
+    *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(c0 + c) * a.ld + pos0 + V * pc) =
+        *reinterpret_cast<const u32x4*>(v);
   }
 }
 
 // db[e][m] = sum of src[m][koff[e] .. koff[e] + K_e) (the padding is zero), 0 for an expert
-// without rows. One wave per (m, e): lane-strided float sums in a fixed order, xor butterfly.
+// without rows. One wave per (m, e): lane-strided 16-byte vectors summed in a fixed order,
+// then an xor butterfly.
 template <typename T>
 __global__ __launch_bounds__(256) void segment_rowsum_kernel(const T* __restrict__ src, const int32_t* __restrict__ kept,
                                                             const int32_t* __restrict__ koff, int M, int ld,
                                                             float* __restrict__ db) {
+  constexpr int V = Vec<T>::N;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int e = blockIdx.y;
   if (m >= M) return;
   const int lane = lane_id();
-  const int kp = (kept[e] + kWgradK - 1) / kWgradK * kWgradK;
+  const int kp = (kept[e] + kWgradK - 1) / kWgradK * kWgradK;   // a multiple of V
   const T* row = src + static_cast<size_t>(m) * ld + (kp > 0 ? koff[e] : 0);
   float acc = 0.0f;
-  for (int i = lane; i < kp; i += kWave) {
-    if constexpr (sizeof(T) == 2)
-      acc += bf16_to_f32(row[i]);
-    else
-      acc += row[i];
+  for (int i = lane * V; i < kp; i += kWave * V) {
+    const u32x4 q = *reinterpret_cast<const u32x4*>(row + i);
+    const T* v = reinterpret_cast<const T*>(&q);
+#pragma unroll
+    for (int u = 0; u < V; ++u) acc += to_f32(v[u]);
   }
   acc = wave_sum(acc);
   if (lane == 0) db[static_cast<size_t>(e) * M + m] = acc;
@@ -258,73 +281,190 @@ __global__ __launch_bounds__(256) void zero_empty_kernel(float* __restrict__ out
 }
 
 // dW_g partials: part[s][e][n] = sum over tokens t of chunk s (ascending) of dz[t][e] x[t][n].
-// One thread per column n; dz rows are uniform over the workgroup.
-template <bool BF16>
+// EB = E rounded up to 8, 16, 32 or 64; each thread owns EB experts x 64/EB consecutive
+// columns (64 accumulators), so a token costs one vector load of x and 64 FMAs; the chunk's
+// dz rows are staged in LDS 64 tokens at a time and read as 16-byte broadcasts. The blocks
+// of column block 0 also write the chunk's dz column sums (bpart, for db_g).
+template <bool BF16, int EB>
 __global__ __launch_bounds__(256) void dwg_partial_kernel(const void* __restrict__ x, const float* __restrict__ dz,
-                                                          int T, int d, int E, int chunk, float* __restrict__ part) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
+                                                          int T, int d, int E, int chunk, float* __restrict__ part,
+                                                          float* __restrict__ bpart) {
+  constexpr int CPT = 64 / EB, TB = 64;
+  __shared__ __attribute__((aligned(16))) float zs[TB][EB];
+  const int n0 = (blockIdx.x * 256 + threadIdx.x) * CPT;
   const int s = blockIdx.y;
   const int t0 = s * chunk, t1 = min(T, t0 + chunk);
-  float acc[kMaxE];
+  if (bpart != nullptr && blockIdx.x == 0 && threadIdx.x < E) {
+    float b = 0.0f;
+    for (int t = t0; t < t1; ++t) b += dz[static_cast<size_t>(t) * E + threadIdx.x];
+    bpart[static_cast<size_t>(s) * E + threadIdx.x] = b;
+  }
+  float acc[EB][CPT];
 #pragma unroll
-  for (int e = 0; e < kMaxE; ++e) acc[e] = 0.0f;
-  if (n < d) {
-    for (int t = t0; t < t1; ++t) {
-      const float xv = BF16 ? bf16_to_f32(static_cast<const u16*>(x)[static_cast<size_t>(t) * d + n])
-                            : static_cast<const float*>(x)[static_cast<size_t>(t) * d + n];
-      const float* zr = dz + static_cast<size_t>(t) * E;
+  for (int e = 0; e < EB; ++e)
 #pragma unroll
-      for (int e = 0; e < kMaxE; ++e)
-        if (e < E) acc[e] = fmaf(zr[e], xv, acc[e]);
+    for (int c = 0; c < CPT; ++c) acc[e][c] = 0.0f;
+  const bool live = n0 < d;
+  for (int tb = t0; tb < t1; tb += TB) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < TB * EB; i += 256) {
+      const int tt = i / EB, e = i % EB;
+      zs[tt][e] = (tb + tt < t1 && e < E) ? dz[static_cast<size_t>(tb + tt) * E + e] : 0.0f;
     }
+    __syncthreads();
+    const int nt = min(TB, t1 - tb);
+    if (!live) continue;
+#pragma unroll 8
+    for (int tt = 0; tt < nt; ++tt) {
+      float xv[CPT];
+      const size_t o = static_cast<size_t>(tb + tt) * d + n0;
+      if constexpr (BF16) {
+        typedef u16 raw_t __attribute__((ext_vector_type(CPT)));
+        const raw_t q = *reinterpret_cast<const raw_t*>(static_cast<const u16*>(x) + o);
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e)
-      if (e < E) part[(static_cast<size_t>(s) * E + e) * d + n] = acc[e];
+        for (int c = 0; c < CPT; ++c) xv[c] = bf16_to_f32(q[c]);
+      } else {
+        typedef float raw_t __attribute__((ext_vector_type(CPT)));
+        const raw_t q = *reinterpret_cast<const raw_t*>(static_cast<const float*>(x) + o);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) xv[c] = q[c];
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < EB; e4 += 4) {
+        const floatx4 z = *reinterpret_cast<const floatx4*>(&zs[tt][e4]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) acc[e4 + u][c] = fmaf(z[u], xv[c], acc[e4 + u][c]);
+      }
+    }
+  }
+  if (!live) return;
+#pragma unroll
+  for (int e = 0; e < EB; ++e)
+    if (e < E)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) part[(static_cast<size_t>(s) * E + e) * d + n0 + c] = acc[e][c];
+}
+
+// dWg[e][n] = sum over s of part[s][e][n]; dbg[e] likewise from bpart [S][E]. Workgroup = 64
+// outputs x 4 waves: wave g sums slices g, g + 4, g + 8, ... in ascending order, then the four
+// wave sums are added in wave order (a fixed order either way).
+__global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict__ part, int S, size_t En,
+                                                         float* __restrict__ dWg, const float* __restrict__ bpart,
+                                                         int E, float* __restrict__ dbg) {
+  __shared__ float red[4][64];
+  const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const size_t i = static_cast<size_t>(blockIdx.x) * 64 + l;
+  float acc = 0.0f, b = 0.0f;
+  const bool bias = dbg != nullptr && blockIdx.x == 0 && l < E;
+  for (int s = g; s < S; s += 4) {
+    if (i < En) acc += part[static_cast<size_t>(s) * En + i];
+    if (bias) b += bpart[static_cast<size_t>(s) * E + l];
+  }
+  red[g][l] = acc;
+  __syncthreads();
+  if (g == 0 && i < En) dWg[i] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    red[g][l] = b;
+    __syncthreads();
+    if (g == 0 && bias) dbg[l] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
   }
 }
 
-// dWg[e][n] = sum over s (ascending) of part[s][e][n].
-__global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict__ part, int S, size_t En,
-                                                         float* __restrict__ dWg) {
-  const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= En) return;
-  float acc = 0.0f;
-  for (int s = 0; s < S; ++s) acc += part[static_cast<size_t>(s) * En + i];
-  dWg[i] = acc;
-}
-
-// dx[t][n] = sum_j (dXp + dXp2)[dest_tj][n] (kept slots, j order) + sum_e dz[t][e] W_g[e][n].
-// Workgroup = 16 tokens x 256 columns, one column per thread; the thread's W_g column is read
-// once for the 16 tokens.
-template <bool BF16>
+// dx[t][n] = sum_j (dXp + dXp2)[dest_tj][n] (kept slots, j order) + sum_e dz[t][e] W_g[e][n]
+// (experts in order). Workgroup = 16 tokens x 512 columns; each thread owns 2 adjacent
+// columns of the 16 tokens (32 accumulators, few enough registers for four waves per SIMD):
+// 8-byte loads of dXp rows, all 16 of a slot issued together (a dropped slot reads row 0 and
+// adds nothing); W_g columns read 16 experts at a time and used for the 16 tokens; dz rows and
+// dest from LDS.
+template <bool BF16, bool SPLIT>
 __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
-  const int n = blockIdx.y * 256 + threadIdx.x;
-  const int t0 = blockIdx.x * kGroupTokens;
-  if (n >= a.d) return;
+  constexpr int TT = kGroupTokens;
+  __shared__ float zs[TT][kMaxE];
+  __shared__ int ds[TT][kMaxK];
+  const int t0 = blockIdx.x * TT;
+  const int n0 = (blockIdx.y * 256 + threadIdx.x) * 2;
   const int E = a.E, k = a.k, d = a.d;
-  float wg[kMaxE];
+  const int nt = min(TT, a.T - t0);
+  {
+    float zv[TT * kMaxE / 256];
 #pragma unroll
-  for (int e = 0; e < kMaxE; ++e)
-    wg[e] = e < E ? (BF16 ? bf16_to_f32(static_cast<const u16*>(a.Wg)[static_cast<size_t>(e) * d + n])
-                          : static_cast<const float*>(a.Wg)[static_cast<size_t>(e) * d + n])
-                  : 0.0f;
-  for (int t = t0; t < min(a.T, t0 + kGroupTokens); ++t) {
-    float acc = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int r = a.dest[static_cast<size_t>(t) * k + j];
-      if (r < 0) continue;
-      float v = a.dXp[static_cast<size_t>(r) * d + n];
-      if (a.dXp2 != nullptr) v += a.dXp2[static_cast<size_t>(r) * d + n];
-      acc += v;
+    for (int q = 0; q < TT * kMaxE / 256; ++q) {
+      const int i = threadIdx.x + 256 * q, tt = i / kMaxE, e = i % kMaxE;
+      zv[q] = (tt < nt && e < E) ? a.dz[static_cast<size_t>(t0 + tt) * E + e] : 0.0f;
     }
-    const float* zr = a.dz + static_cast<size_t>(t) * E;
 #pragma unroll
-    for (int e = 0; e < kMaxE; ++e)
-      if (e < E) acc = fmaf(zr[e], wg[e], acc);
-    if (BF16)
-      static_cast<u16*>(a.dx)[static_cast<size_t>(t) * d + n] = f32_to_bf16(acc);
-    else
-      static_cast<float*>(a.dx)[static_cast<size_t>(t) * d + n] = acc;
+    for (int q = 0; q < TT * kMaxE / 256; ++q) {
+      const int i = threadIdx.x + 256 * q;
+      zs[i / kMaxE][i % kMaxE] = zv[q];
+    }
+  }
+  if (threadIdx.x < TT * kMaxK) {
+    const int tt = threadIdx.x / kMaxK, j = threadIdx.x % kMaxK;
+    ds[tt][j] = (tt < nt && j < k) ? a.dest[static_cast<size_t>(t0 + tt) * k + j] : -1;
+  }
+  __syncthreads();
+  if (n0 >= d) return;
+  float2 acc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[tt] = float2{0.0f, 0.0f};
+  for (int j = 0; j < k; ++j) {
+    float2 v[TT];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int r = ds[tt][j];
+      v[tt] = *reinterpret_cast<const float2*>(a.dXp + static_cast<size_t>(r < 0 ? 0 : r) * d + n0);
+    }
+    if (SPLIT) {
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt) {
+        const int r = ds[tt][j];
+        const float2 v2 = *reinterpret_cast<const float2*>(a.dXp2 + static_cast<size_t>(r < 0 ? 0 : r) * d + n0);
+        v[tt].x += v2.x;
+        v[tt].y += v2.y;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+      if (ds[tt][j] >= 0) {
+        acc[tt].x += v[tt].x;
+        acc[tt].y += v[tt].y;
+      }
+  }
+  for (int e0 = 0; e0 < E; e0 += 16) {
+    float2 wg[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      wg[e] = float2{0.0f, 0.0f};
+      if (e0 + e < E) {
+        const size_t o = static_cast<size_t>(e0 + e) * d + n0;
+        if constexpr (BF16) {
+          const uint32_t q = *reinterpret_cast<const uint32_t*>(static_cast<const u16*>(a.Wg) + o);
+          wg[e] = float2{__uint_as_float(q << 16), __uint_as_float(q & 0xFFFF0000u)};
+        } else {
+          wg[e] = *reinterpret_cast<const float2*>(static_cast<const float*>(a.Wg) + o);
+        }
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float z = zs[tt][e0 + e];
+        acc[tt].x = fmaf(z, wg[e].x, acc[tt].x);
+        acc[tt].y = fmaf(z, wg[e].y, acc[tt].y);
+      }
+  }
+  for (int tt = 0; tt < nt; ++tt) {
+    const size_t o = static_cast<size_t>(t0 + tt) * d + n0;
+    if constexpr (BF16) {
+      *reinterpret_cast<uint32_t*>(static_cast<u16*>(a.dx) + o) =
+          static_cast<uint32_t>(f32_to_bf16(acc[tt].x)) | (static_cast<uint32_t>(f32_to_bf16(acc[tt].y)) << 16);
+    } else {
+      *reinterpret_cast<float2*>(static_cast<float*>(a.dx) + o) = acc[tt];
+    }
   }
 }
 
@@ -362,7 +502,8 @@ hipError_t launch_transpose(const void* src, void* dst, int B, int Rn, int Cn, i
 }
 
 hipError_t launch_rows_to_cols(const RowsToColsArgs& a, int bf16, hipStream_t stream) {
-  const dim3 grid((a.ncol + 63) / 64, a.ld / 32);
+  const int tc = bf16 ? 128 : 64;
+  const dim3 grid((a.ncol + tc - 1) / tc, a.ld / 32);
   if (bf16)
     hipLaunchKernelGGL(rows_to_cols_kernel<u16>, grid, dim3(256), 0, stream, a);
   else
@@ -390,37 +531,56 @@ hipError_t launch_zero_empty(float* out, const int32_t* kept, int E, size_t per_
   return hipGetLastError();
 }
 
-int dwg_slices(int T, int d) {
-  const int cols = (d + 255) / 256;
-  int s = (1024 + cols - 1) / cols;          // aim at >= 1024 workgroups
+static int dwg_block_cols(int E) {
+  const int EB = E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64));
+  return 256 * (64 / EB);
+}
+
+int dwg_slices(int T, int d, int E) {
+  const int cols = (d + dwg_block_cols(E) - 1) / dwg_block_cols(E);
+  int s = (2048 + cols - 1) / cols;          // aim at >= 2048 workgroups (8 per CU)
   const int max_s = (T + 15) / 16;           // at least 16 tokens per slice
   s = s < max_s ? s : max_s;
-  return s < 1 ? 1 : (s > 64 ? 64 : s);
+  return s < 1 ? 1 : (s > 512 ? 512 : s);
 }
 
 hipError_t launch_dwg(const void* x, const float* dz, int T, int d, int E, int bf16, float* part, float* dWg,
-                      hipStream_t stream) {
-  const int S = dwg_slices(T, d);
+                      float* dbg, hipStream_t stream) {
+  const int S = dwg_slices(T, d, E);
   const int chunk = (T + S - 1) / S;
-  const dim3 grid((d + 255) / 256, S);
-  if (bf16)
-    hipLaunchKernelGGL(dwg_partial_kernel<true>, grid, dim3(256), 0, stream, x, dz, T, d, E, chunk, part);
-  else
-    hipLaunchKernelGGL(dwg_partial_kernel<false>, grid, dim3(256), 0, stream, x, dz, T, d, E, chunk, part);
+  const size_t En = static_cast<size_t>(E) * d;
+  float* bpart = dbg != nullptr ? part + static_cast<size_t>(S) * En : nullptr;
+  const int EB = E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64));
+  const dim3 grid((d + dwg_block_cols(E) - 1) / dwg_block_cols(E), S);
+#define MOE_DWG(B, EBV)                                                                                       \
+  hipLaunchKernelGGL((dwg_partial_kernel<B, EBV>), grid, dim3(256), 0, stream, x, dz, T, d, E, chunk, part, \
+                     bpart)
+  if (bf16) {
+    if (EB == 8) MOE_DWG(true, 8); else if (EB == 16) MOE_DWG(true, 16);
+    else if (EB == 32) MOE_DWG(true, 32); else MOE_DWG(true, 64);
+  } else {
+    if (EB == 8) MOE_DWG(false, 8); else if (EB == 16) MOE_DWG(false, 16);
+    else if (EB == 32) MOE_DWG(false, 32); else MOE_DWG(false, 64);
+  }
+#undef MOE_DWG
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const size_t En = static_cast<size_t>(E) * d;
-  hipLaunchKernelGGL(dwg_reduce_kernel, dim3(static_cast<unsigned>((En + 255) / 256)), dim3(256), 0, stream, part, S,
-                     En, dWg);
+  hipLaunchKernelGGL(dwg_reduce_kernel, dim3(static_cast<unsigned>((En + 63) / 64)), dim3(256), 0, stream, part, S,
+                     En, dWg, bpart, E, dbg);
   return hipGetLastError();
 }
 
 hipError_t launch_dx(const DxArgs& a, int bf16, hipStream_t stream) {
-  const dim3 grid((a.T + kGroupTokens - 1) / kGroupTokens, (a.d + 255) / 256);
-  if (bf16)
-    hipLaunchKernelGGL(dx_kernel<true>, grid, dim3(256), 0, stream, a);
+  const dim3 grid((a.T + kGroupTokens - 1) / kGroupTokens, (a.d + 511) / 512);
+  const bool split = a.dXp2 != nullptr;
+  if (bf16 && split)
+    hipLaunchKernelGGL((dx_kernel<true, true>), grid, dim3(256), 0, stream, a);
+  else if (bf16)
+    hipLaunchKernelGGL((dx_kernel<true, false>), grid, dim3(256), 0, stream, a);
+  else if (split)
+    hipLaunchKernelGGL((dx_kernel<false, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(dx_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((dx_kernel<false, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -67,6 +67,12 @@ __device__ __forceinline__ float activation_grad(float v) {
   return EPI == kEpiGeluGrad ? gelu_grad_exact(v) : silu_grad_exact(v);
 }
 
+// The derivative for results rounded to bf16 (hardware exp2 and reciprocal).
+template <int EPI>
+__device__ __forceinline__ float activation_grad_bf16(float v) {
+  return EPI == kEpiGeluGrad ? gelu_grad_bf16_path(v) : silu_grad_bf16_path(v);
+}
+
 // Rows of expert e's segment; a segment that does not fit [0, R) or exceeds C counts as empty.
 // In wgrad mode every group with kept rows has M output rows.
 __device__ __forceinline__ int segment_rows(const GemmArgs& g, int e) {
@@ -260,12 +266,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     constexpr int NI = decltype(ni_const)::value;
     constexpr bool BIAS = decltype(bias_const)::value;
     constexpr bool PRE = decltype(pre_const)::value;       // also store the activation's input
-    constexpr bool GRAD = is_grad_epi(EPI);
     constexpr int OB = EPI == kEpiLinear ? 4 : 2;         // output bytes per element
     constexpr int PITCH = 128 * OB + 16;                   // bytes per staged row (padded)
     constexpr int CPRW = 128 * OB / 16;                    // 16-byte pieces per row
     constexpr int RPW = 64 / CPRW;                         // rows per wave store
     static_assert((EPI == kEpiLinear ? 4 : 8) * 32 * PITCH <= NS * STAGE, "epilogue staging fits the operand ring");
+    static_assert(4 * 32768 <= NS * STAGE, "the gradient epilogue's act_in blocks fit the operand ring");
     char* st = smem + wave * 32 * PITCH;
     char* st2 = smem + (4 + wave) * 32 * PITCH;            // staged inputs of the activation
     char* outb = static_cast<char*>(EPI != kEpiLinear ? g.out : (kpart == 0 ? g.out : g.out2));
@@ -284,21 +290,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     };
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      float scale = 0.0f;
-      if constexpr (GRAD) {
-        // stage the activation inputs of this row block (same whole-row pattern as the stores)
-#pragma unroll
-        for (int it = 0; it < 32 / RPW; ++it) {
-          const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
-          const int r = m0 + wm * 128 + i * 32 + rr;
-          const int c = n0 + wn * 128 + pc * 8;
-          if (r < m_e && c < N)
-            *reinterpret_cast<u32x4*>(st2 + rr * PITCH + pc * 16) = *reinterpret_cast<const u32x4*>(
-                static_cast<const char*>(g.act_in) + (static_cast<size_t>(row0 + r) * N + c) * 2);
-        }
-        const int r = min(m0 + wm * 128 + i * 32 + l32, m_e - 1);
-        scale = g.row_scale[row0 + r];
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -311,14 +302,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
                    (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + wn * 128 + cl + u, N - 1), true)
                          : 0.0f);
           char* dst = st + l32 * PITCH + cl * OB;
-          if constexpr (GRAD) {
-            const bf16x4 a = *reinterpret_cast<const bf16x4*>(st2 + l32 * PITCH + cl * 2);
-            bf16x4 pk;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-              pk[u] = static_cast<__bf16>(o[u] * scale * activation_grad<EPI>(static_cast<float>(a[u])));
-            *reinterpret_cast<bf16x4*>(dst) = pk;
-          } else if constexpr (EPI != kEpiLinear) {
+          if constexpr (EPI != kEpiLinear) {
             bf16x4 pk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) pk[u] = static_cast<__bf16>(activation_bf16<EPI>(o[u]));
@@ -335,8 +319,70 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
         }
       // the wave reads back only what it wrote itself: LDS keeps one wave's accesses in order
       rows_out(st, outb, i);
-      if constexpr (PRE && EPI != kEpiLinear && !GRAD) rows_out(st2, static_cast<char*>(g.pre), i);
+      if constexpr (PRE && EPI != kEpiLinear) rows_out(st2, static_cast<char*>(g.pre), i);
       __builtin_amdgcn_sched_barrier(0);   // one row block at a time: bounded register use
+    }
+  };
+
+  // Activation-gradient epilogue: out = acc * row_scale[r] * act'(act_in[r, n]), bf16. Each
+  // wave's act_in block (NI row blocks of 32 x 128 bf16) goes straight into the free operand
+  // ring with buffer -> LDS loads, all issued at once (32 KB per wave, 8 KB per row block,
+  // rows of 256 bytes whose 16-byte pieces are XOR-swizzled by row so that the fragment-order
+  // reads spread over the banks). Each lane then overwrites its own inputs with its outputs in
+  // place, and the block goes out as whole rows. Rows past the segment read as zero (the
+  // resource ends at the last valid row) and are never stored.
+  auto grad_epilogue = [&](auto ni_const) {
+    constexpr int NI = decltype(ni_const)::value;
+    char* region = smem + wave * 32768;
+    __syncthreads();                                       // every wave is done with the ring
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int rb = m0 + wm * 128 + i * 32;              // first tile row of the block
+      const int valid_rows = max(0, min(32, m_e - rb));
+      const char* base = static_cast<const char*>(g.act_in) +
+                         (static_cast<size_t>(row0 + rb) * N + n0 + wn * 128) * 2;
+      const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, valid_rows * N * 2);
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rr = 4 * it + lane / 16, pp = lane % 16;
+        const uint32_t off = static_cast<uint32_t>(rr * N * 2 + ((pp ^ (rr % 16)) * 16));
+        load_lds16(rs, off, region + i * 8192 + it * 1024);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      // this block's loads are older than every later block's 8 (the stores issued since are
+      // younger still, so the wait can only be stricter than needed)
+      if (i == 0) wait_vmcnt<(NI > 1 ? 8 * (NI - 1) : 0)>();
+      else if (i == 1) wait_vmcnt<(NI > 2 ? 8 * (NI - 2) : 0)>();
+      else if (i == 2) wait_vmcnt<(NI > 3 ? 8 : 0)>();
+      else wait_vmcnt<0>();
+      char* blk = region + i * 8192;
+      const int r = min(m0 + wm * 128 + i * 32 + l32, m_e - 1);
+      const float scale = g.row_scale[row0 + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          char* pa = blk + l32 * 256 + (((4 * j + q) ^ (l32 % 16)) * 16) + 8 * hi;
+          const bf16x4 a = *reinterpret_cast<const bf16x4*>(pa);
+          bf16x4 pk;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            pk[u] = static_cast<__bf16>(acc[i][j][4 * q + u] * scale *
+                                        activation_grad_bf16<EPI>(static_cast<float>(a[u])));
+          *reinterpret_cast<bf16x4*>(pa) = pk;
+        }
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int rr = 4 * it + lane / 16, pc = lane % 16;
+        const int rw = m0 + wm * 128 + i * 32 + rr;
+        const int c = n0 + wn * 128 + pc * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(blk + rr * 256 + ((pc ^ (rr % 16)) * 16));
+        if (rw < m_e && c < N)
+          *reinterpret_cast<u32x4*>(static_cast<char*>(g.out) + (static_cast<size_t>(row0 + rw) * N + c) * 2) = v;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   const bool add_bias = kpart == 0 && g.bias != nullptr;
@@ -412,6 +458,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       schedule(true);
     }
     wait_vmcnt<0>();     // the trailing re-loads must land before the workgroup's LDS is released
+    if constexpr (is_grad_epi(EPI)) {
+      grad_epilogue(ni_const);
+      return;
+    }
     if constexpr (EPI == kEpiGelu || EPI == kEpiSilu) {
       if (g.pre != nullptr) {
         if (add_bias)
@@ -513,7 +563,7 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
         const float val = acc[t][i] + bias;
         if constexpr (is_grad_epi(EPI)) {
           const float a = bf16_to_f32(static_cast<const u16*>(g.act_in)[o]);
-          static_cast<u16*>(g.out)[o] = f32_to_bf16(val * g.row_scale[row0 + r] * activation_grad<EPI>(a));
+          static_cast<u16*>(g.out)[o] = f32_to_bf16(val * g.row_scale[row0 + r] * activation_grad_bf16<EPI>(a));
         } else if constexpr (EPI != kEpiLinear) {
           static_cast<u16*>(g.out)[o] = f32_to_bf16(activation_bf16<EPI>(val));
           if (g.pre != nullptr) static_cast<u16*>(g.pre)[o] = f32_to_bf16(val);

@@ -208,7 +208,7 @@ Layout layout_of(const Derived& D) {
   L.HT = take(dff * ldz * es);
   L.dAT = take(dff * ldz * es);
   L.XT = take(d * ldz * es);
-  L.dwg = take(tr ? static_cast<size_t>(moe::dwg_slices(D.T, D.d)) * E * d * 4 : 0);
+  L.dwg = take(tr ? static_cast<size_t>(moe::dwg_slices(D.T, D.d, D.E)) * (E * d + E) * 4 : 0);
   L.dyp = take(tr && !bwd_gathers(D) ? R * d * es : 0);
   L.total = off;
   return L;
@@ -828,8 +828,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   if (db2 != nullptr) MOE_HIP(moe::launch_segment_rowsum(dOT, kept, koff, E, d, ld, bf, db2, st), "db2");
   if (db1 != nullptr) MOE_HIP(moe::launch_segment_rowsum(dAT, kept, koff, E, dff, ld, bf, db1, st), "db1");
   // 5. router weights and the input gradient
-  MOE_HIP(moe::launch_dwg(x, dz, T, d, E, bf, at<float>(ws, Lw.dwg), dWg, st), "dWg");
-  if (dbg != nullptr) MOE_HIP(moe::launch_colsum(dz, T, E, dbg, st), "dbg");
+  MOE_HIP(moe::launch_dwg(x, dz, T, d, E, bf, at<float>(ws, Lw.dwg), dWg, dbg, st), "dWg");
   moe::DxArgs xa{dXp, dXp2, dest, dz, Wg, T, d, E, D.k, dx};
   MOE_HIP(moe::launch_dx(xa, bf, st), "dx");
   if (ev) MOE_HIP(hipEventRecord(ev[8], st), "event");

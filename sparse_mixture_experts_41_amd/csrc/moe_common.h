@@ -141,6 +141,28 @@ __device__ __forceinline__ float silu_grad_exact(float v) {
   return s * (1.0f + v * (1.0f - s));
 }
 
+// The same derivatives for results rounded to bf16, from the hardware exp2 and reciprocal.
+// GeLU': Phi(v) from the tail h = Phi(-|v|) of gelu_bf16_path (A&S 7.1.26, |error| <= 0.75e-7)
+// and phi(v) = e^(-v^2/2) / sqrt(2 pi) from the same exponential; the v phi(v) term uses |v|
+// capped at 1e30 so that infinite inputs give 0 or 1. SiLU': s (1 + v (1 - s)) with
+// s = rcp(1 + 2^(-v log2 e)), v clamped to [-1e4, 1e4] (beyond it the value is 0 or 1).
+__device__ __forceinline__ float gelu_grad_bf16_path(float v) {
+  const float a = fabsf(v);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.23164189f, a, 1.0f));
+  const float poly =
+      t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.5307027f, -0.72657603f), 0.7107069f), -0.14224836f), 0.1274148f);
+  const float g = __builtin_amdgcn_exp2f((v * v) * -0.7213475f);        // e^(-v^2 / 2)
+  const float h = poly * g;
+  const float phi_big = v >= 0.0f ? 1.0f - h : h;
+  return fmaf(copysignf(fminf(a, 1e30f), v) * 0.39894228040143267794f, g, phi_big);
+}
+
+__device__ __forceinline__ float silu_grad_bf16_path(float v) {
+  const float vc = fminf(fmaxf(v, -1e4f), 1e4f);
+  const float s = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(vc * -1.4426950408889634f));
+  return s * fmaf(vc, 1.0f - s, 1.0f);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
 }  // namespace moe

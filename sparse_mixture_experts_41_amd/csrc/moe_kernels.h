@@ -248,10 +248,11 @@ hipError_t launch_segment_rowsum(const void* src, const int32_t* kept, const int
 // out[e] = 0 (per_expert floats) for every expert e with kept[e] = 0.
 hipError_t launch_zero_empty(float* out, const int32_t* kept, int E, size_t per_expert, hipStream_t stream);
 
-// dWg = dz^T x (float [E,d]) through part [dwg_slices(T,d), E, d] partial sums.
-int dwg_slices(int T, int d);
+// dWg = dz^T x (float [E,d]) and dbg = column sums of dz (float [E], nullable) through part
+// [dwg_slices(T,d,E) * (E*d + E)] partial sums.
+int dwg_slices(int T, int d, int E);
 hipError_t launch_dwg(const void* x, const float* dz, int T, int d, int E, int bf16, float* part, float* dWg,
-                      hipStream_t stream);
+                      float* dbg, hipStream_t stream);
 
 // dx[t] = sum_j (dXp + dXp2)[dest_tj] + dz_t W_g (dtype [T,d]).
 struct DxArgs {

@@ -5,7 +5,9 @@ same discrete decisions; every gradient is then compared as a whole tensor. Case
 float32 path (plain FMA products), the bf16 MFMA path (gathered dy, activation-gradient
 epilogue, weight-gradient mode), the bf16 GEMV path (at most 16 rows per expert), a split
 dx product together with a split forward GEMM2, experts without rows, every capacity policy,
-both activations, Gumbel and Gaussian noise, temperature and the balance term.
+both activations, Gumbel and Gaussian noise, temperature and the balance term. At full size
+(the Mixtral-like and switch-skew layers) sampled gradient entries are checked against
+oracle.backward_entries.
 
 Tolerances (relative Frobenius error of each gradient tensor, and max error over max |ref|):
   float32 storage: 3e-6 and 6e-6 (float32 sums of at most a few thousand terms: about
@@ -22,9 +24,10 @@ import pytest
 import torch
 
 import oracle
-from workloads import MoEShape, make_upstream_grad
+from sparse_mixture_experts_41_amd import ops
+from workloads import CONFIGS, MoEShape, make_upstream_grad
 
-from .parity import Problem, backward_errors, host_values, run_train
+from .parity import Problem, backward_errors, host_values, run_train, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -101,3 +104,53 @@ def test_training_forward_matches_the_plain_forward():
     np.testing.assert_array_equal(a["y"], b["y"])
     for key in ("topk_idx", "topk_w", "dest", "kept", "counts", "f", "L"):
         np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+
+
+FULL = {
+    # name: (shape, policy, lam)
+    "mixtral_like": (CONFIGS["mixtral_like"], "token", 0.01),
+    "switch_skew_reroute": (CONFIGS["switch_skew"], "reroute", 0.01),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FULL))
+def test_backward_full_size_sampled(name):
+    """The named workloads at full size: sampled gradient entries against oracle.backward_entries
+    (dx and dz rows of 24 tokens, 6 rows of dW2 / db2 from two experts, 8 rows of dW1 / db1)."""
+    shape, policy, lam = FULL[name]
+    print(f"[gpu] full-size backward {name} {shape} policy={policy}", flush=True)
+    p = Problem(shape, drop_policy=policy)
+    plan = ops.TrainPlan(p.cfg, *p.args(), variant=p.variant())
+    fwd = plan.run()
+    dy_arr = make_upstream_grad(shape)
+    g = plan.backward(to_device(dy_arr, shape.dtype), lam)
+    torch.cuda.synchronize()
+    scores = fwd["scores"].cpu().numpy()
+    dest = fwd["dest"].cpu().numpy()
+    kept = fwd["kept"].cpu().numpy()
+    rng = np.random.default_rng(0)
+    partial = np.flatnonzero(np.any(dest < 0, axis=1))
+    tokens = sorted(set(rng.choice(shape.T, 16, replace=False).tolist()) | set(partial[:8].tolist()))
+    busy = [int(e) for e in np.argsort(-kept)[:2]]
+    w2_rows = [(busy[i % 2], int(m)) for i, m in enumerate(rng.choice(shape.d, 6, replace=False))]
+    w1_rows = [(int(e), int(n)) for e, n in zip(rng.choice(np.flatnonzero(kept > 0), 8),
+                                                rng.choice(shape.d_ffn, 8, replace=False))]
+    ref = oracle.backward_entries(*p.host_args(), host_values(dy_arr, shape.dtype), tokens=tokens,
+                                  w2_rows=w2_rows, w1_rows=w1_rows, k=shape.k,
+                                  capacity_factor=shape.capacity_factor, lam=lam, tau=shape.temperature,
+                                  gumbel=shape.gumbel, seed=shape.seed, given_scores=scores, policy=policy)
+    np.testing.assert_array_equal(dest, ref["dispatch"]["dest"])
+    ti = torch.tensor(tokens, device="cuda")
+    got = {
+        "dx": g["dx"][ti].float().cpu().numpy(),
+        "dz": g["dz"][ti].cpu().numpy(),
+        "dW2": torch.stack([g["dW2"][e, m] for e, m in w2_rows]).cpu().numpy(),
+        "db2": torch.stack([g["db2"][e, m] for e, m in w2_rows]).cpu().numpy(),
+        "dW1": torch.stack([g["dW1"][e, n] for e, n in w1_rows]).cpu().numpy(),
+        "db1": torch.stack([g["db1"][e, n] for e, n in w1_rows]).cpu().numpy(),
+    }
+    errs = backward_errors(got, ref)
+    print(f"[gpu]   {name}: " + ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in errs.items()), flush=True)
+    fro, mx = TOL[shape.dtype]
+    for key, (e_fro, e_max) in errs.items():
+        assert e_fro <= fro and e_max <= mx, f"{key}: relative Frobenius {e_fro:.3e}, max {e_max:.3e}"

@@ -183,3 +183,21 @@ def test_balance_term_alone():
     want = lam * 6 / 50 * p * (f[None, :] - (p * f[None, :]).sum(1, keepdims=True)) / tau
     np.testing.assert_allclose(g["dz"], want, rtol=1e-12, atol=1e-15)
     assert np.all(g["dW1"] == 0.0) and np.all(g["dW2"] == 0.0)
+
+
+@pytest.mark.parametrize("policy", ["token", "random", "reroute"])
+def test_sampled_entries_equal_the_full_backward(policy):
+    prob = _problem(T=40, E=5, seed=11)
+    kw = dict(k=2, capacity_factor=0.7, lam=0.4, tau=0.9, act="silu", policy=policy, seed=3)
+    full = oracle.backward(*(prob[n] for n in NAMES), prob["dy"], **kw)
+    tokens = [0, 7, 39, 21]
+    w2_rows = [(3, 1), (0, 5), (3, 7), (1, 0)]
+    w1_rows = [(2, 11), (0, 0), (4, 3)]
+    got = oracle.backward_entries(*(prob[n] for n in NAMES), prob["dy"], tokens=tokens, w2_rows=w2_rows,
+                                  w1_rows=w1_rows, **kw)
+    np.testing.assert_allclose(got["dx"], full["dx"][tokens], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got["dz"], full["dz"][tokens], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got["dW2"], [full["dW2"][e, m] for e, m in w2_rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got["db2"], [full["db2"][e, m] for e, m in w2_rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got["dW1"], [full["dW1"][e, n] for e, n in w1_rows], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(got["db1"], [full["db1"][e, n] for e, n in w1_rows], rtol=1e-12, atol=1e-14)
