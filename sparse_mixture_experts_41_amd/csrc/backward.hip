@@ -87,12 +87,6 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(BwdRouterArgs a) {
       if (j < k && dst[j] >= 0) {
         float o[8];
         load8<false>(a.y_perm, static_cast<size_t>(dst[j]) * d + c0, o);
-        if (a.y_perm2 != nullptr) {
-          float o2[8];
-          load8<false>(a.y_perm2, static_cast<size_t>(dst[j]) * d + c0, o2);
-#pragma unroll
-          for (int u = 0; u < 8; ++u) o[u] += o2[u];
-        }
 #pragma unroll
         for (int u = 0; u < 8; ++u) part[j] = fmaf(g[u], o[u], part[j]);
       }
@@ -373,13 +367,13 @@ __global__ __launch_bounds__(256) void dwg_reduce_kernel(const float* __restrict
   }
 }
 
-// dx[t][n] = sum_j (dXp + dXp2)[dest_tj][n] (kept slots, j order) + sum_e dz[t][e] W_g[e][n]
+// dx[t][n] = sum_j dXp[dest_tj][n] (kept slots, j order) + sum_e dz[t][e] W_g[e][n]
 // (experts in order). Workgroup = 16 tokens x 512 columns; each thread owns 2 adjacent
 // columns of the 16 tokens (32 accumulators, few enough registers for four waves per SIMD):
 // 8-byte loads of dXp rows, all 16 of a slot issued together (a dropped slot reads row 0 and
 // adds nothing); W_g columns read 16 experts at a time and used for the 16 tokens; dz rows and
 // dest from LDS.
-template <bool BF16, bool SPLIT>
+template <bool BF16>
 __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
   constexpr int TT = kGroupTokens;
   __shared__ float zs[TT][kMaxE];
@@ -416,15 +410,6 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
     for (int tt = 0; tt < TT; ++tt) {
       const int r = ds[tt][j];
       v[tt] = *reinterpret_cast<const float2*>(a.dXp + static_cast<size_t>(r < 0 ? 0 : r) * d + n0);
-    }
-    if (SPLIT) {
-#pragma unroll
-      for (int tt = 0; tt < TT; ++tt) {
-        const int r = ds[tt][j];
-        const float2 v2 = *reinterpret_cast<const float2*>(a.dXp2 + static_cast<size_t>(r < 0 ? 0 : r) * d + n0);
-        v[tt].x += v2.x;
-        v[tt].y += v2.y;
-      }
     }
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
@@ -572,15 +557,10 @@ hipError_t launch_dwg(const void* x, const float* dz, int T, int d, int E, int b
 
 hipError_t launch_dx(const DxArgs& a, int bf16, hipStream_t stream) {
   const dim3 grid((a.T + kGroupTokens - 1) / kGroupTokens, (a.d + 511) / 512);
-  const bool split = a.dXp2 != nullptr;
-  if (bf16 && split)
-    hipLaunchKernelGGL((dx_kernel<true, true>), grid, dim3(256), 0, stream, a);
-  else if (bf16)
-    hipLaunchKernelGGL((dx_kernel<true, false>), grid, dim3(256), 0, stream, a);
-  else if (split)
-    hipLaunchKernelGGL((dx_kernel<false, true>), grid, dim3(256), 0, stream, a);
+  if (bf16)
+    hipLaunchKernelGGL(dx_kernel<true>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((dx_kernel<false, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(dx_kernel<false>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

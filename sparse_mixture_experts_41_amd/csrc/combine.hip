@@ -16,7 +16,6 @@ namespace {
 // Each thread produces 8 consecutive outputs of one token.
 template <bool BF16>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
-                                                      const float* __restrict__ y_perm2,
                                                       const float* __restrict__ y_shared,
                                                       const int32_t* __restrict__ dest,
                                                       const float* __restrict__ w, int T, int d, int k, int R,
@@ -38,16 +37,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       if (r < 0 || r >= R) continue;   // dropped (or out-of-range) slot: contributes zero
       const float wj = w[static_cast<size_t>(t) * k + j];
       const floatx4* src = reinterpret_cast<const floatx4*>(y_perm + static_cast<size_t>(r) * d + c);
-      floatx4 v0 = src[0], v1 = src[1];
-      if (y_perm2 != nullptr) {   // the two K halves of the second expert GEMM
-        const floatx4* src2 = reinterpret_cast<const floatx4*>(y_perm2 + static_cast<size_t>(r) * d + c);
-        const floatx4 u0 = src2[0], u1 = src2[1];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v0[q] = v0[q] + u0[q];
-          v1[q] = v1[q] + u1[q];
-        }
-      }
+      const floatx4 v0 = src[0], v1 = src[1];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc0[q] = fmaf(wj, v0[q], acc0[q]);
@@ -71,17 +61,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float* y_perm, const float* y_perm2, const float* y_shared, const int32_t* dest,
+hipError_t launch_combine(const float* y_perm, const float* y_shared, const int32_t* dest,
                           const float* w, int T, int d, int k, int R, int bf16, void* y, hipStream_t stream) {
   const long long items = static_cast<long long>(T) * (d / 8);
   long long blocks = (items + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (bf16)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y_perm, y_perm2,
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y_perm,
                        y_shared, dest, w, T, d, k, R, y);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y_perm, y_perm2,
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, y_perm,
                        y_shared, dest, w, T, d, k, R, y);
   return hipGetLastError();
 }

@@ -32,8 +32,9 @@ struct GemmArgs {
   const int32_t* offsets; // [E]
   int E, N, K;
   int R, C;               // rows of A/out and the capacity: segments outside them are skipped
-  int splits;             // K is split into this many equal parts (1 or 2)
-  void* out2;             // [R,N] float partial sums of the second K part (splits == 2)
+  int splits;             // > 1: the tiles of the last, partial round of 256 are split along K into at
+                          // most this many parts (linear epilogue only); see tail_plan
+  void* out2;             // float side buffer of those parts past the first: dense 256 x 256 tiles
   const int32_t* rows;    // [R] or null: A row of expert-sorted row r is rows[r] (fused gather)
   int a_rows;             // rows of A when `rows` is set (a_rows * K * 2 < 2^31)
   int dense;              // 1: one expert (E = 1) over all R rows; kept and offsets are unused
@@ -112,6 +113,26 @@ __device__ __forceinline__ int count_tiles(const GemmArgs& g, int BM, int tiles_
   return n;
 }
 
+// Tail split: the tiles of the whole rounds of 256 run unsplit; the L tiles of the last, partial
+// round are split along K into P parts (as many as fill the round, at most `max_parts`, each
+// at least 4 K steps), so the launch ends after about full/256 + 1/P rounds instead of a whole
+// extra round. Part 0 writes the output (with the bias); parts 1..P-1 write dense 256 x 256
+// float tiles to the side buffer, slot (tile - full) (P - 1) + part - 1, and
+// tail_fixup_kernel adds them in part order.
+struct TailPlan {
+  int full, L, P;
+};
+__device__ __forceinline__ TailPlan tail_plan(int n_tiles, int nk_total, int max_parts) {
+  const int rem = n_tiles % 256;
+  int P = rem > 0 ? 256 / rem : 1;
+  P = min(P, max_parts);
+  P = min(P, nk_total / 4);
+  if (max_parts <= 1 || rem == 0 || P < 2) return TailPlan{n_tiles, 0, 1};
+  return TailPlan{n_tiles - rem, rem, P};
+}
+constexpr int kTailMaxParts = 8;
+constexpr size_t kTailTile = 256 * 256;            // floats per side-buffer tile
+
 // The hardware hands workgroup b to XCD (b mod 8). Workgroups are renumbered so that each XCD
 // takes bundles of kBundle consecutive tiles (tiles that share an expert's operand panels, so
 // they meet in that XCD's L2), and bundles go round-robin over the 8 XCDs (so experts of very
@@ -187,28 +208,44 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 
   const int tiles_n = (g.N + BN - 1) / BN;
   const int n_tiles = count_tiles(g, BM, tiles_n);
-  const int n_units = n_tiles * g.splits;
+  const TailPlan plan = tail_plan(n_tiles, g.K / BK, EPI == kEpiLinear && !g.wgrad ? g.splits : 1);
+  const int n_units = plan.full + plan.L * plan.P;
   const int unit = xcd_tile_id(blockIdx.x);
   if (unit >= n_units) return;
-  const int kpart = unit / n_tiles;
+  int tile = unit, kpart = 0, parts = 1;
+  if (unit >= plan.full) {
+    const int u = unit - plan.full;
+    tile = plan.full + u / plan.P;
+    kpart = u % plan.P;
+    parts = plan.P;
+  }
+  // uniform by construction; said so, so that the buffer resources stay in scalar registers
+  tile = __builtin_amdgcn_readfirstlane(tile);
+  kpart = __builtin_amdgcn_readfirstlane(kpart);
+  parts = __builtin_amdgcn_readfirstlane(parts);
   int e, mt, nt;
-  decode_tile(unit - kpart * n_tiles, g, BM, tiles_n, e, mt, nt);
-  const int m_e = segment_rows(g, e);
-  const int row0 = (g.dense || g.wgrad) ? 0 : g.offsets[e];
+  decode_tile(tile, g, BM, tiles_n, e, mt, nt);
+  e = __builtin_amdgcn_readfirstlane(e);
+  mt = __builtin_amdgcn_readfirstlane(mt);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  const int m_e = __builtin_amdgcn_readfirstlane(segment_rows(g, e));
+  const int row0 = __builtin_amdgcn_readfirstlane((g.dense || g.wgrad) ? 0 : g.offsets[e]);
   const int m0 = mt * BM, n0 = nt * BN;
   const int N = g.N;
   const int lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
   const int K = g.wgrad ? (g.kept[e] + kWgradK - 1) / kWgradK * kWgradK : g.K;
   const size_t kofs = g.wgrad ? static_cast<size_t>(g.koff[e]) : 0;
-  const int nk = K / BK / g.splits;          // K steps of this part
+  const int k_first = __builtin_amdgcn_readfirstlane((K / BK) * kpart / parts);
+  const int k_last = __builtin_amdgcn_readfirstlane((K / BK) * (kpart + 1) / parts);
+  const int nk = k_last - k_first;           // K steps of this part
   const bool gathered = g.rows != nullptr;
   const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + kofs +
                                                  (gathered ? 0 : static_cast<size_t>(row0 + m0) * lda)) +
-                   static_cast<size_t>(kpart) * nk * ROWB;
+                   static_cast<size_t>(k_first) * ROWB;
   const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
                                                  (g.wgrad ? static_cast<size_t>(n0) * ldb
                                                           : (static_cast<size_t>(e) * N + n0) * ldb)) +
-                   static_cast<size_t>(kpart) * nk * ROWB;
+                   static_cast<size_t>(k_first) * ROWB;
   const size_t out_base = g.wgrad ? static_cast<size_t>(e) * g.M * N : 0;   // elements
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
@@ -274,18 +311,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     static_assert(4 * 32768 <= NS * STAGE, "the gradient epilogue's act_in blocks fit the operand ring");
     char* st = smem + wave * 32 * PITCH;
     char* st2 = smem + (4 + wave) * 32 * PITCH;            // staged inputs of the activation
-    char* outb = static_cast<char*>(EPI != kEpiLinear ? g.out : (kpart == 0 ? g.out : g.out2));
+    // the tile's output block and its row pitch: the output (part 0) or a side-buffer tile
+    const bool side = EPI == kEpiLinear && kpart > 0;
+    char* outb = side ? static_cast<char*>(g.out2) +
+                            ((static_cast<size_t>(tile - plan.full) * (plan.P - 1) + kpart - 1) * kTailTile) * 4
+                      : static_cast<char*>(g.out) + (out_base + static_cast<size_t>(row0 + m0) * N + n0) * OB;
+    const size_t pitch = side ? 256 : static_cast<size_t>(N);
     __syncthreads();                                       // every wave is done with the ring
-    // whole-row pieces of the wave's row block: LDS <-> global, 16 bytes per lane
-    auto rows_out = [&](const char* stage, char* base, int i) {
+    // whole-row pieces of the wave's row block: LDS <-> global, 16 bytes per lane (float outputs,
+    // read once by the next kernel, go out as non-temporal stores)
+    auto rows_out = [&](const char* stage, char* base, size_t bpitch, int i) {
 #pragma unroll
       for (int it = 0; it < 32 / RPW; ++it) {
         const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
-        const int r = m0 + wm * 128 + i * 32 + rr;
-        const int c = n0 + wn * 128 + pc * (16 / OB);
+        const int rl = wm * 128 + i * 32 + rr;
+        const int cl = wn * 128 + pc * (16 / OB);
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * PITCH + pc * 16);
-        if (r < m_e && c < N)
-          *reinterpret_cast<u32x4*>(base + (out_base + static_cast<size_t>(row0 + r) * N + c) * OB) = v;
+        if (m0 + rl < m_e && n0 + cl < N) {
+          u32x4* dst = reinterpret_cast<u32x4*>(base + (static_cast<size_t>(rl) * bpitch + cl) * OB);
+          if constexpr (EPI == kEpiLinear)
+            __builtin_nontemporal_store(v, dst);
+          else
+            *dst = v;
+        }
       }
     };
 #pragma unroll
@@ -318,8 +366,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
           }
         }
       // the wave reads back only what it wrote itself: LDS keeps one wave's accesses in order
-      rows_out(st, outb, i);
-      if constexpr (PRE && EPI != kEpiLinear) rows_out(st2, static_cast<char*>(g.pre), i);
+      rows_out(st, outb, pitch, i);
+      if constexpr (PRE && EPI != kEpiLinear)
+        rows_out(st2, static_cast<char*>(g.pre) + (static_cast<size_t>(row0 + m0) * N + n0) * OB, N, i);
       __builtin_amdgcn_sched_barrier(0);   // one row block at a time: bounded register use
     }
   };
@@ -622,6 +671,50 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
   }
 }
 
+// Adds the side-buffer parts of the split tail tiles to the output, parts 1, 2, ... in that
+// order after part 0 (already in the output). A work unit is kFixupRows rows of one split
+// tile; the fixed grid strides over the L * 256 / kFixupRows units so that the whole chip
+// shares the traffic, and each thread issues the loads of all parts before it adds.
+constexpr int kFixupRows = 8;
+constexpr int kFixupGrid = 1024;
+__global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs g) {
+  constexpr int BM = 256, BN = 256, BK = 32, SLABS = BM / kFixupRows, RPP = 256 / (BN / 4);
+  const int tiles_n = (g.N + BN - 1) / BN;
+  const TailPlan plan = tail_plan(count_tiles(g, BM, tiles_n), g.K / BK, g.splits);
+  const int N = g.N;
+  float* out = static_cast<float*>(g.out);
+  const int c = (threadIdx.x % (BN / 4)) * 4;
+  for (int u = blockIdx.x; u < plan.L * SLABS; u += gridDim.x) {
+    const int s = u / SLABS, slab = u % SLABS;
+    int e, mt, nt;
+    decode_tile(plan.full + s, g, BM, tiles_n, e, mt, nt);
+    const int m_e = segment_rows(g, e);
+    const int row0 = g.dense ? 0 : g.offsets[e];
+    const int m0 = mt * BM, n0 = nt * BN;
+    const float* side = static_cast<const float*>(g.out2) + static_cast<size_t>(s) * (plan.P - 1) * kTailTile;
+#pragma unroll
+    for (int j = 0; j < kFixupRows / RPP; ++j) {
+      const int r = slab * kFixupRows + j * RPP + static_cast<int>(threadIdx.x) / (BN / 4);
+      if (m0 + r >= m_e || n0 + c >= N) continue;
+      floatx4 w[kTailMaxParts - 1];
+#pragma unroll
+      for (int p = 1; p < kTailMaxParts; ++p)
+        if (p < plan.P)
+          w[p - 1] = __builtin_nontemporal_load(
+              reinterpret_cast<const floatx4*>(side + (p - 1) * kTailTile + r * BN + c));
+      floatx4* o = reinterpret_cast<floatx4*>(out + static_cast<size_t>(row0 + m0 + r) * N + n0 + c);
+      floatx4 v = *o;
+#pragma unroll
+      for (int p = 1; p < kTailMaxParts; ++p)
+        if (p < plan.P) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] += w[p - 1][q];
+        }
+      *o = v;
+    }
+  }
+}
+
 int tile_grid(int R, int E, int C, int BM, int N, int BN) {
   const long long by_rows = (R + BM - 1) / BM + E;
   const long long by_cap = static_cast<long long>(E) * ((C + BM - 1) / BM);
@@ -635,12 +728,9 @@ bool ffn_gathers(const FfnArgs& a) {
   return a.bf16 && a.C > 16 && static_cast<long long>(a.T) * a.d * 2 < (1ll << 31);
 }
 
-int ffn_splits(const FfnArgs& a) {
-  if (!a.bf16 || a.C <= 16) return 1;
-  const int tiles2 = tile_grid(a.R, a.E, a.C, 256, a.d, 256);
-  // weight-streaming shapes (every expert within two row tiles) gain nothing from splitting
-  return (a.C > 512 && tiles2 < 4 * 256 && a.d_ffn % 64 == 0 && a.d_ffn >= 1024) ? 2 : 1;
-}
+int ffn_splits(const FfnArgs& a) { return (a.bf16 && a.C > 16) ? kTailMaxParts : 1; }
+
+size_t tail_side_floats() { return static_cast<size_t>(255) * kTailTile; }
 
 template <int ACT>
 static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, int C, int R, int E, int N1, int N2,
@@ -664,18 +754,20 @@ static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, 
     return hipGetLastError();
   }
   const int grid1 = round_grid(tile_grid(R, E, C, 256, N1, 256));
-  const int grid2 = round_grid(tile_grid(R, E, C, 256, N2, 256) * g2.splits);
+  const int grid2 = round_grid(tile_grid(R, E, C, 256, N2, 256) + (g2.splits > 1 ? 256 : 0));
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, 32, 4>), dim3(grid1), dim3(256), 0, stream, g1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (g2.splits > 1) hipLaunchKernelGGL(tail_fixup_kernel, dim3(kFixupGrid), dim3(256), 0, stream, g2);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid) {
   GemmArgs g1{a.x_perm, a.W1, a.b1, a.H, a.kept, a.offsets, a.E, a.d_ffn, a.d, a.R, a.C, 1, nullptr, nullptr, 0, 0};
   g1.pre = a.pre;
-  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.y_perm2,
+  GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.side,
               nullptr, 0, 0};
   if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
     g1.A = a.x;
@@ -705,8 +797,13 @@ static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStrea
     hipLaunchKernelGGL(grouped_gemv_bf16_kernel<EPI>, dim3(g.E * ((g.N + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
                        stream, g);
   } else {
-    const int grid = round_grid(tile_grid(g.R, g.E, C, 256, g.N, 256) * g.splits);
+    const int grid = round_grid(tile_grid(g.R, g.E, C, 256, g.N, 256) + (g.splits > 1 ? 256 : 0));
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
+    if (EPI == kEpiLinear && g.splits > 1) {
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(tail_fixup_kernel, dim3(kFixupGrid), dim3(256), 0, stream, g);
+    }
   }
   return hipGetLastError();
 }
@@ -733,9 +830,8 @@ hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream) {
 }
 
 int bwd_dx_splits(int R, int E, int C, int d, int d_ffn, int bf16) {
-  if (!bf16 || C <= 16) return 1;
-  const int tiles = tile_grid(R, E, C, 256, d, 256);
-  return (C > 512 && tiles < 4 * 256 && d_ffn % 64 == 0 && d_ffn >= 1024) ? 2 : 1;
+  (void)R, (void)E, (void)d, (void)d_ffn;
+  return (bf16 && C > 16) ? kTailMaxParts : 1;
 }
 
 hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream) {
@@ -743,7 +839,7 @@ hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream) {
   g.A = a.dA;
   g.B = a.W1T;
   g.out = a.dXp;
-  g.out2 = a.dXp2;
+  g.out2 = a.side;
   g.kept = a.kept;
   g.offsets = a.offsets;
   g.E = a.E;
@@ -779,29 +875,6 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {
     const int grid = round_grid(a.E * ((a.M + 255) / 256) * ((a.N + 255) / 256));
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
   }
-  return hipGetLastError();
-}
-
-namespace {
-__global__ __launch_bounds__(256) void add_partials_kernel(float* __restrict__ y, const float* __restrict__ y2,
-                                                           const int32_t* __restrict__ kept,
-                                                           const int32_t* __restrict__ offsets, int E, int R, int d) {
-  const int total = min(offsets[E - 1] + kept[E - 1], R);
-  const long long n4 = static_cast<long long>(total) * d / 4;
-  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n4;
-       i += static_cast<long long>(gridDim.x) * blockDim.x) {
-    floatx4 a = reinterpret_cast<floatx4*>(y)[i];
-    const floatx4 b = reinterpret_cast<const floatx4*>(y2)[i];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = a[q] + b[q];
-    reinterpret_cast<floatx4*>(y)[i] = a;
-  }
-}
-}  // namespace
-
-hipError_t launch_add_partials(float* y_perm, const float* y_perm2, const int32_t* kept, const int32_t* offsets,
-                               int E, int R, int d, hipStream_t stream) {
-  hipLaunchKernelGGL(add_partials_kernel, dim3(4096), dim3(256), 0, stream, y_perm, y_perm2, kept, offsets, E, R, d);
   return hipGetLastError();
 }
 

@@ -39,9 +39,9 @@ struct Derived {
 
 struct Layout {
   size_t probsum, hist, blockbase, colsum, zpart, logits, scores, idx, w, offsets, dest, perm, x_perm, H, y_perm,
-      y_perm2, Hs, ys, ent, idx_next, cand, hist2, blockbase2, kept1, thresh,
+      side, Hs, ys, ent, idx_next, cand, hist2, blockbase2, kept1, thresh,
       // training: saved by moe_forward_train, then moe_backward's scratch
-      pre, kept_s, f_s, koff, wrow, dz, dA, dXp, dXp2, W2T, W1T, dOT, HT, dAT, XT, dwg, dyp, total;
+      pre, kept_s, f_s, koff, wrow, dz, dA, dXp, W2T, W1T, dOT, HT, dAT, XT, dwg, dyp, total;
   int ld;   // row pitch of the transposed, padded activations
 };
 
@@ -175,7 +175,7 @@ Layout layout_of(const Derived& D) {
   L.x_perm = take(R * static_cast<size_t>(D.d) * D.esize);
   L.H = take(R * static_cast<size_t>(D.dff) * D.esize);
   L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
-  L.y_perm2 = take(D.bf16 ? R * static_cast<size_t>(D.d) * 4 : 0);
+  L.side = take(D.bf16 && clamp_c(D) > 16 ? moe::tail_side_floats() * 4 : 0);
   L.Hs = take(D.dffs > 0 ? T * static_cast<size_t>(D.dffs) * D.esize : 0);
   L.ys = take(D.dffs > 0 ? T * static_cast<size_t>(D.d) * 4 : 0);
   const bool random = D.policy == MOE_DROP_RANDOM, reroute = D.policy == MOE_DROP_REROUTE;
@@ -192,7 +192,6 @@ Layout layout_of(const Derived& D) {
                      moe::kWgradK * moe::kWgradK;
   L.ld = tr ? static_cast<int>(ld) : 0;
   const size_t ldz = tr ? static_cast<size_t>(ld) : 0;
-  const bool dx_split = moe::bwd_dx_splits(D.R, D.E, clamp_c(D), D.d, D.dff, D.bf16 ? 1 : 0) == 2;
   L.pre = take(tr ? R * dff * es : 0);
   L.kept_s = take(tr ? E * 4 : 0);
   L.f_s = take(tr ? E * 4 : 0);
@@ -201,7 +200,6 @@ Layout layout_of(const Derived& D) {
   L.dz = take(tr ? T * E * 4 : 0);
   L.dA = take(tr ? R * dff * es : 0);
   L.dXp = take(tr ? R * d * 4 : 0);
-  L.dXp2 = take(tr && dx_split ? R * d * 4 : 0);
   L.W2T = take(tr ? E * d * dff * es : 0);
   L.W1T = take(tr ? E * d * dff * es : 0);
   L.dOT = take(d * ldz * es);
@@ -387,11 +385,9 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x_perm, const int32
   a.R = D.R;
   a.C = static_cast<int>(D.C < D.T ? D.C : D.T);
   a.bf16 = D.bf16 ? 1 : 0;
-  a.y_perm2 = at<float>(ws, L.y_perm2);
+  a.side = at<float>(ws, L.side);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   MOE_HIP(moe::launch_expert_ffn(a, st, nullptr), "expert_ffn");
-  if (moe::ffn_splits(a) == 2)
-    MOE_HIP(moe::launch_add_partials(y_perm, a.y_perm2, kept, offsets, D.E, D.R, D.d, st), "add_partials");
   return MOE_OK;
 }
 
@@ -415,7 +411,7 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const int32_t
   }
   MOE_CHECK(need_ws(D, ws, ws_bytes, &Lw));
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  MOE_HIP(moe::launch_combine(y_perm, nullptr, nullptr, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
+  MOE_HIP(moe::launch_combine(y_perm, nullptr, dest, topk_w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
           "combine");
   if (stats) MOE_HIP(moe::launch_stats(counts, prob_colsum, D.E, D.k, D.T, f, P, L, st), "stats");
   return MOE_OK;
@@ -584,7 +580,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   fa.R = D.R;
   fa.C = C;
   fa.bf16 = D.bf16 ? 1 : 0;
-  fa.y_perm2 = at<float>(ws, Lw.y_perm2);
+  fa.side = at<float>(ws, Lw.side);
   fa.act = D.act;
   fa.pre = train ? at<void>(ws, Lw.pre) : nullptr;
   if (moe::ffn_gathers(fa))
@@ -614,8 +610,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   }
   if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
   // 5. combine (adding the two K halves of GEMM2 when it was split, from the shared output)
-  const float* y_perm2 = moe::ffn_splits(fa) == 2 ? fa.y_perm2 : nullptr;
-  MOE_HIP(moe::launch_combine(y_perm, y_perm2, y_shared, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
+  MOE_HIP(moe::launch_combine(y_perm, y_shared, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
           "combine");
   if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");
   if (train) {
@@ -725,24 +720,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   float* wrow = at<float>(ws, Lw.wrow);
   float* dz = ax.dz != nullptr ? ax.dz : at<float>(ws, Lw.dz);
   void* dA = at<void>(ws, Lw.dA);
-  moe::FfnArgs fa{};                         // the forward's GEMM2 split decides whether y_perm2 holds a part
-  fa.E = E;
-  fa.d = d;
-  fa.d_ffn = dff;
-  fa.R = R;
-  fa.C = C;
-  fa.bf16 = bf;
-  const bool fwd_split = moe::ffn_splits(fa) == 2;
-  const bool dx_split = moe::bwd_dx_splits(R, E, C, d, dff, bf) == 2;
   float* dXp = at<float>(ws, Lw.dXp);
-  float* dXp2 = dx_split ? at<float>(ws, Lw.dXp2) : nullptr;
 
   if (ev) MOE_HIP(hipEventRecord(ev[0], st), "event");
   // 1. router backward: dw, the softmax backward and the balance term -> dz; row weights
   moe::BwdRouterArgs ra{};
   ra.dy = dy;
   ra.y_perm = at<float>(ws, Lw.y_perm);
-  ra.y_perm2 = fwd_split ? at<float>(ws, Lw.y_perm2) : nullptr;
   ra.dest = dest;
   ra.idx = at<int32_t>(ws, Lw.idx);
   ra.cand = D.policy == MOE_DROP_REROUTE ? at<int32_t>(ws, Lw.cand) : nullptr;
@@ -793,7 +777,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   da.act = D.act;
   MOE_HIP(moe::launch_bwd_dact(da, st), "bwd_dact");
   if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
-  moe::BwdDxArgs dxa{dA, W1T, dXp, dXp2, kept, offsets, E, d, dff, R, C, bf};
+  moe::BwdDxArgs dxa{dA, W1T, dXp, bf && C > 16 ? at<float>(ws, Lw.side) : nullptr, kept, offsets, E, d, dff, R, C, bf};
   MOE_HIP(moe::launch_bwd_dx(dxa, st), "bwd_dx");
   if (ev) MOE_HIP(hipEventRecord(ev[4], st), "event");
   // 4. weight gradients: each expert's rows as zero-padded columns, then per-expert products
@@ -829,7 +813,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   if (db1 != nullptr) MOE_HIP(moe::launch_segment_rowsum(dAT, kept, koff, E, dff, ld, bf, db1, st), "db1");
   // 5. router weights and the input gradient
   MOE_HIP(moe::launch_dwg(x, dz, T, d, E, bf, at<float>(ws, Lw.dwg), dWg, dbg, st), "dWg");
-  moe::DxArgs xa{dXp, dXp2, dest, dz, Wg, T, d, E, D.k, dx};
+  moe::DxArgs xa{dXp, dest, dz, Wg, T, d, E, D.k, dx};
   MOE_HIP(moe::launch_dx(xa, bf, st), "dx");
   if (ev) MOE_HIP(hipEventRecord(ev[8], st), "event");
   return MOE_OK;

@@ -110,7 +110,7 @@ struct FfnArgs {
   const void* b2;         // [E,d] or null
   void* H;                // [R,d_ffn]
   float* y_perm;          // [R,d]
-  float* y_perm2;         // [R,d] second K half of GEMM2 when ffn_splits() == 2
+  float* side;            // tail_side_floats() floats when ffn_splits() > 1: GEMM2's split-tail parts
   int E, d, d_ffn, R, C;
   int bf16;
   int act;                // kActGelu or kActSilu
@@ -119,10 +119,13 @@ struct FfnArgs {
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
 // copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
 bool ffn_gathers(const FfnArgs& a);
-// Number of K parts GEMM2 is split into (1 or 2): 2 when the capacity exceeds two 256-row tiles
-// (compute-bound experts) and its tiles would fill fewer than four
-// rounds of the 256 CUs. With 2, y_perm + y_perm2 (summed in float32) is the GEMM2 result.
+// Most K parts a tile of the last, partial round of GEMM2 is split into (1 = no tail split):
+// kTailMaxParts on the bf16 MFMA path, 1 elsewhere. Part 0 writes y_perm, the other parts
+// write `side`, and a fixup kernel adds them to y_perm in part order, so y_perm alone is the
+// GEMM2 result.
 int ffn_splits(const FfnArgs& a);
+// Floats of the side buffer of a tail-split product (255 dense 256 x 256 tiles).
+size_t tail_side_floats();
 // GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid);
 // The shared expert: one dense FFN over the T token rows of x (no routing):
@@ -140,13 +143,9 @@ struct SharedFfnArgs {
 };
 hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream);
 
-// y_perm[r] += y_perm2[r] for the sum(kept) valid rows (standalone expert FFN with 2 parts).
-hipError_t launch_add_partials(float* y_perm, const float* y_perm2, const int32_t* kept, const int32_t* offsets,
-                               int E, int R, int d, hipStream_t stream);
-
-// y_perm2 (nullable): second GEMM2 partial, added to y_perm before weighting. y_shared
+// y_shared
 // (nullable, [T,d] float): the shared expert's output, where each token's sum starts.
-hipError_t launch_combine(const float* y_perm, const float* y_perm2, const float* y_shared, const int32_t* dest,
+hipError_t launch_combine(const float* y_perm, const float* y_shared, const int32_t* dest,
                           const float* w, int T, int d, int k, int R, int bf16, void* y, hipStream_t stream);
 
 hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,
@@ -174,12 +173,12 @@ struct BwdDactArgs {
 hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream);
 
 // dXp[r] = dA[r] W1_e (float, [R, d]); W1T [E, d, d_ffn] is W1 transposed. With
-// bwd_dx_splits() == 2 the result is dXp + dXp2.
+// bwd_dx_splits() > 1 the last round's tiles are tail-split through `side` (tail_side_floats()).
 struct BwdDxArgs {
   const void* dA;
   const void* W1T;
   float* dXp;
-  float* dXp2;
+  float* side;
   const int32_t* kept;
   const int32_t* offsets;
   int E, d, d_ffn, R, C, bf16;
@@ -208,7 +207,6 @@ hipError_t launch_wgrad_offsets(const int32_t* kept, int E, int32_t* koff, hipSt
 struct BwdRouterArgs {
   const void* dy;         // [T,d] dtype
   const float* y_perm;    // [R,d] expert outputs (GEMM2 result)
-  const float* y_perm2;   // [R,d] or null: GEMM2's second K part
   const int32_t* dest;    // [T,k]
   const int32_t* idx;     // [T,k] the router's choices
   const int32_t* cand;    // [T,k] or null: rerouted experts (-1: the slot stays at idx)
@@ -254,10 +252,9 @@ int dwg_slices(int T, int d, int E);
 hipError_t launch_dwg(const void* x, const float* dz, int T, int d, int E, int bf16, float* part, float* dWg,
                       float* dbg, hipStream_t stream);
 
-// dx[t] = sum_j (dXp + dXp2)[dest_tj] + dz_t W_g (dtype [T,d]).
+// dx[t] = sum_j dXp[dest_tj] + dz_t W_g (dtype [T,d]).
 struct DxArgs {
   const float* dXp;
-  const float* dXp2;      // or null
   const int32_t* dest;
   const float* dz;
   const void* Wg;
