@@ -170,21 +170,35 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
+// acc += A_blk B_blk^T on one 16x16x32 bf16 block, operands given B first (so acc holds the
+// transposed block), with acc tied to its AGPRs; FIRST starts from zero (srcC = 0).
+template <bool FIRST>
+__device__ __forceinline__ void mfma_16x16x32(floatx4& acc, const bf16x8& b, const bf16x8& a) {
+  if constexpr (FIRST)
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
+  else
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
 // Workgroup barrier without the LDS-read wait that __syncthreads adds: the callers order
 // their own LDS traffic (vmcnt waits for the direct loads, register dependences for reads).
 __device__ __forceinline__ void barrier_no_lds_wait() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------
 // bf16 grouped GEMM C[r, n] = sum_k A[r, k] B_e[n, k] over each expert's row segment.
-// 256 x 256 workgroup tile, 4 waves in a 2x2 grid of 128 x 128 wave tiles, each a 4x4 grid of
-// v_mfma_f32_32x32x16_bf16 tiles (256 accumulators per lane). Operand tiles go from global
+// 256 x 256 workgroup tile, 4 waves in a 2x2 grid of 128 x 128 wave tiles, each an 8x8 grid of
+// v_mfma_f32_16x16x32_bf16 blocks (256 accumulators per lane). The 16x16x32 form moves a quarter
+// of the accumulator data per flop that 32x32x16 does and runs at a higher clock under load.
+// The MFMAs are written as inline asm with each accumulator tied to one AGPR quad (destination
+// = srcC): left to itself the compiler shuffles these 64 accumulators between register files.
+// Operand tiles go from global
 // memory straight into LDS (buffer_load_dwordx4 ... lds: 64 lanes fill one contiguous 1 KB
 // block; per-lane offsets are fixed, the K step moves the resource base in scalar registers)
 // through a ring of NS K-steps of BK; the 16-byte chunks of each row are XOR-swizzled so that
 // the 16-byte fragment reads of any 16 consecutive rows hit all 64 banks once.
-// The workgroup barrier sits before the last MFMA substep of each K step: after it, step s+1
-// is complete in LDS (its first fragments are read during step s's last MFMAs) and the buffer
-// of step s-1 is free for step s+NS-1, so NS-3 steps of loads stay in flight while waiting.
+// The workgroup barrier opens each K step s: after it, step s+1 is complete in LDS (its
+// fragments are read during step s's MFMAs) and the buffer of step s-1 is free for step
+// s+NS-1, so NS-3 steps of loads stay in flight while waiting.
 // Loads past the last K step re-read the last step into buffers nobody reads again, which keeps
 // the number of loads in flight the same in every iteration.
 // Rows past the segment (or past N) are loaded from the last valid row: they only feed output
@@ -200,10 +214,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   constexpr int STAGE = 2 * TILE;
   constexpr int LOADS = BM / RPI / 4;        // 1 KB loads per wave per operand per K step
   constexpr int PER_STAGE = 2 * LOADS;       // vm operations per thread per K step
-  constexpr int KK = BK / 16;                // MFMA K substeps per K step
   static_assert(NS >= 3 && NS * STAGE <= 160 * 1024, "LDS ring");
-  static_assert(KK % 2 == 0, "fragment double buffer parity");
-  static_assert(LOADS * 2 <= 8, "one load per interleave slot");
+  static_assert(BK == 32, "one v_mfma_f32_16x16x32_bf16 K step per K step");
+  static_assert(PER_STAGE == 8, "one operand load per 16-row MFMA block");
   __shared__ __attribute__((aligned(1024))) char smem[NS * STAGE];
 
   const int tiles_n = (g.N + BN - 1) / BN;
@@ -266,35 +279,29 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   // the clamped offsets stay below 256 rows of the pitch past the B resource base and below
   // the tile's (or, gathered, all of A's) rows past the A base; anything beyond reads as zero
   const int span = BM * ldb * 2, span_a = gathered ? g.a_rows * lda * 2 : BM * lda * 2;
-  auto issue = [&](int st) {   // loads of K step min(st, nk-1) into buffer st % NS
+  // load q (0..7) of K step min(st, nk-1) into buffer st % NS: A blocks 0..3, then B blocks
+  auto issue1 = [&](int st, int q) {
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
     const uint32_t kb = static_cast<uint32_t>(st < nk ? st : nk - 1) * ROWB;
-    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(Ab + kb, span_a), rb = buffer_rsrc(Bb + kb, span);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) load_lds16(ra, aoff[i], dst + i * 4096);
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) load_lds16(rb, boff[i], dst + TILE + i * 4096);
+    if (q < LOADS)
+      load_lds16(buffer_rsrc(Ab + kb, span_a), aoff[q], dst + q * 4096);
+    else
+      load_lds16(buffer_rsrc(Bb + kb, span), boff[q - LOADS], dst + TILE + (q - LOADS) * 4096);
   };
 
-  // fragment addressing: lane reads row (wave-tile row + l32), logical chunk 2 kk + hi
+  // fragment addressing: lane (l16, lg) reads row (wave-tile row + 16 i + l16), 16-byte chunk lg
+  // of the step's 64 bytes: the 8 K values an operand lane holds in v_mfma_f32_16x16x32_bf16
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int swz = (l32 / RPS) % CPR;
-  int slot[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk) slot[kk] = ((2 * kk + hi) ^ swz) * 16;
-  const int a_frag = (wm * 128 + l32) * ROWB;
-  const int b_frag = TILE + (wn * 128 + l32) * ROWB;
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{};
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int slot = (lg ^ ((l16 / RPS) % CPR)) * 16;
+  const int a_frag = (wm * 128 + l16) * ROWB + slot;
+  const int b_frag = TILE + (wn * 128 + l16) * ROWB + slot;
+  floatx4 acc[8][8];
 
   // Epilogue. The MFMAs take the B fragment as their first operand, so block (i, j) holds the
-  // transposed 32x32 result: lane (l32, hi) has tile row wm*128 + 32 i + l32 at columns
-  // wn*128 + 32 j + 8 q + 4 hi + (0..3), q = 0..3, four consecutive outputs of one row. Bias
-  // and GeLU are applied in registers; each 32x128 row block then goes through the wave's own
+  // transposed 16x16 result: lane (l16, lg) has tile row wm*128 + 16 i + l16 at columns
+  // wn*128 + 16 j + 4 lg + (0..3), four consecutive outputs of one row. Bias and GeLU are
+  // applied in registers; each 32x128 row block (MFMA rows 2 ib, 2 ib + 1) then goes through the wave's own
   // LDS region (8-byte bf16 or 16-byte float pieces) and back out as whole rows: 16 lanes
   // (bf16) or 32 lanes (float) store each row's 256 or 512 contiguous bytes, so every store
   // covers whole cache lines. N is a multiple of 64, so each 16-byte piece lies wholly inside
@@ -339,17 +346,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int cl = j * 32 + 8 * q + 4 * hi;            // column within the wave tile
+        for (int j = 0; j < 8; ++j) {
+          const int rl = 16 * h + l16;                      // row within the 32-row block
+          const int cl = j * 16 + 4 * lg;                   // column within the wave tile
           float o[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)   // one addition either way: GeLU then needs no canonicalisation
-            o[u] = acc[i][j][4 * q + u] +
+            o[u] = acc[2 * i + h][j][u] +
                    (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + wn * 128 + cl + u, N - 1), true)
                          : 0.0f);
-          char* dst = st + l32 * PITCH + cl * OB;
+          char* dst = st + rl * PITCH + cl * OB;
           if constexpr (EPI != kEpiLinear) {
             bf16x4 pk;
 #pragma unroll
@@ -359,7 +367,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
               bf16x4 pv;
 #pragma unroll
               for (int u = 0; u < 4; ++u) pv[u] = static_cast<__bf16>(o[u]);
-              *reinterpret_cast<bf16x4*>(st2 + l32 * PITCH + cl * OB) = pv;
+              *reinterpret_cast<bf16x4*>(st2 + rl * PITCH + cl * OB) = pv;
             }
           } else {
             *reinterpret_cast<floatx4*>(dst) = floatx4{o[0], o[1], o[2], o[3]};
@@ -407,21 +415,24 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       else if (i == 2) wait_vmcnt<(NI > 3 ? 8 : 0)>();
       else wait_vmcnt<0>();
       char* blk = region + i * 8192;
-      const int r = min(m0 + wm * 128 + i * 32 + l32, m_e - 1);
-      const float scale = g.row_scale[row0 + r];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int h = 0; h < 2; ++h) {
+        const int rl = 16 * h + l16;                        // row within the block; rl % 16 = l16
+        const int r = min(m0 + wm * 128 + i * 32 + rl, m_e - 1);
+        const float scale = g.row_scale[row0 + r];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          char* pa = blk + l32 * 256 + (((4 * j + q) ^ (l32 % 16)) * 16) + 8 * hi;
+        for (int j = 0; j < 8; ++j) {
+          // columns 16 j + 4 lg .. + 3: 16-byte piece 2 j + lg / 2, half lg % 2
+          char* pa = blk + rl * 256 + (((2 * j + (lg >> 1)) ^ l16) * 16) + 8 * (lg & 1);
           const bf16x4 a = *reinterpret_cast<const bf16x4*>(pa);
           bf16x4 pk;
 #pragma unroll
           for (int u = 0; u < 4; ++u)
-            pk[u] = static_cast<__bf16>(acc[i][j][4 * q + u] * scale *
+            pk[u] = static_cast<__bf16>(acc[2 * i + h][j][u] * scale *
                                         activation_grad_bf16<EPI>(static_cast<float>(a[u])));
           *reinterpret_cast<bf16x4*>(pa) = pk;
         }
+      }
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
         const int rr = 4 * it + lane / 16, pc = lane % 16;
@@ -441,71 +452,63 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   // the loads and takes every barrier.
   auto mainloop = [&](auto ni_const) {
     constexpr int NI = decltype(ni_const)::value;
-    bf16x8 fa[2][4], fb[2][4];
-    auto read_frags = [&](int st, int kk, int f) {
-      const char* buf = smem + (st % NS) * STAGE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < NI) fa[f][i] = *reinterpret_cast<const bf16x8*>(buf + a_frag + i * 32 * ROWB + slot[kk]);
-        if (NI > 0) fb[f][i] = *reinterpret_cast<const bf16x8*>(buf + b_frag + i * 32 * ROWB + slot[kk]);
-      }
+    constexpr int NR = 2 * NI;                         // 16-row MFMA blocks multiplied
+    // A fragments single-buffered (row i's next one is read once row i's MFMAs are issued), B
+    // fragments double-buffered by step parity (the next ones are read during rows 0..3)
+    bf16x8 fa[8], fb[2][8];
+    auto rd_a = [&](int st, int i) {
+      fa[i] = *reinterpret_cast<const bf16x8*>(smem + (st % NS) * STAGE + a_frag + i * 16 * ROWB);
     };
-    auto mfmas = [&](int f) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][j], fa[f][i], acc[i][j], 0, 0, 0);
+    auto rd_b = [&](int st, int f, int j) {
+      fb[f][j] = *reinterpret_cast<const bf16x8*>(smem + (st % NS) * STAGE + b_frag + j * 16 * ROWB);
     };
-    // Before the barrier: one fragment read after each of the first MFMAs of the substep.
-    // After it, with full tiles (16 MFMAs): one operand load after each of the first 8 MFMAs,
-    // one fragment read after each of the last 8 (reads issued last are needed last); with
-    // fewer MFMAs, a read and a load after each MFMA.
-    auto schedule = [&](bool with_loads) {
-      constexpr int NR = NI + (NI > 0 ? 4 : 0);     // fragment reads per substep
-      constexpr int NM = NI * 4;                     // MFMAs per substep
-      if (with_loads && NM == 16) {
-#pragma unroll
-        for (int q = 0; q < PER_STAGE; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-#pragma unroll
-        for (int q = 0; q < 16 - PER_STAGE; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        return;
-      }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (q < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (with_loads) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      }
-      if (NM > 8) __builtin_amdgcn_sched_group_barrier(0x008, NM - 8, 0);
-    };
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st) issue(st);
-    wait_vmcnt<(NS - 2) * PER_STAGE>();
-    __syncthreads();
-    read_frags(0, 0, 0);
-    for (int s = 0; s < nk; ++s) {
-#pragma unroll
-      for (int kk = 0; kk + 1 < KK; ++kk) {
-        read_frags(s, kk + 1, (kk + 1) & 1);
-        mfmas(kk & 1);
-      }
-      schedule(false);
+    // K step s: barrier, then per 16-row block i one operand load of step s+NS-1, the block's 8
+    // MFMAs on fragments of step s, and reads of step s+1's fragments. FIRST: srcC = 0.
+    auto step = [&](int s, auto f_const, auto first_const) {
+      constexpr int F = decltype(f_const)::value;
+      constexpr bool FIRST = decltype(first_const)::value;
       wait_vmcnt<(NS - 3) * PER_STAGE>();   // this thread's loads of step s+1 have landed
       // Everyone's have, and step s-1's buffer is free: every wave consumed its reads of step
-      // s-1 (issued before the previous barrier) in the MFMAs it ran before arriving here.
+      // s-1 (issued during step s-2) in the MFMAs it ran before arriving here.
       barrier_no_lds_wait();
-      issue(s + NS - 1);
-      read_frags(s + 1, 0, 0);              // past the last step this reads unused data
-      mfmas((KK - 1) & 1);
-      schedule(true);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        issue1(s + NS - 1, i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (i < NR) mfma_16x16x32<FIRST>(acc[i][j], fb[F][j], fa[i]);
+          if (NR > 0 && i < 4 && (j == 1 || j == 3)) rd_b(s + 1, F ^ 1, 2 * i + (j == 3));
+        }
+        if (i < NR) rd_a(s + 1, i);         // past the last step this reads unused data
+      }
+    };
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+#pragma unroll
+      for (int q = 0; q < PER_STAGE; ++q) issue1(st, q);
+    wait_vmcnt<(NS - 2) * PER_STAGE>();
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i < NR) rd_a(0, i);
+      if (NR > 0) rd_b(0, 0, i);
     }
+    using F0 = std::integral_constant<int, 0>;
+    using F1 = std::integral_constant<int, 1>;
+    step(0, F0{}, std::true_type{});                    // nk >= 1: K is at least one step
+    int s = 1;
+    for (; s + 1 < nk; s += 2) {
+      step(s, F1{}, std::false_type{});
+      step(s + 1, F0{}, std::false_type{});
+    }
+    if (s < nk) step(s, F1{}, std::false_type{});
+    // the asm MFMAs are invisible to the hazard checks: wait out the last ones' latency, then
+    // pin every later read of the accumulators behind that wait
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NR; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
     wait_vmcnt<0>();     // the trailing re-loads must land before the workgroup's LDS is released
     if constexpr (is_grad_epi(EPI)) {
       grad_epilogue(ni_const);
