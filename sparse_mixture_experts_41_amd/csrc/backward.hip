@@ -185,6 +185,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
 // Expert-sorted rows -> zero-padded columns: for expert e and i < K_e (kept[e] rounded up to
 // kWgradK), dst[n][koff[e] + i] = scale[r] * src[row(r)][n] with r = offsets[e] + i while
 // i < kept[e] (row(r) = rows[r] when gathering, else r; no scale when null), 0 past it.
+// With src_tiled the source row i of expert e is row i mod 256 of K-step-tiled panel
+// (row tiles of the experts before e) + i / 256.
 // Tiles of 32 padded positions x 16 vectors of columns (128 bf16 or 64 floats); tile j
 // belongs to the expert whose padded range holds position 32 j; tiles past the last expert
 // exit. 16-byte loads of source rows; 16-byte stores of destination rows gathered from LDS.
@@ -192,15 +194,17 @@ template <typename T>
 __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
   constexpr int V = Vec<T>::N, TC = 16 * V, P = TC + Vec<T>::PAD, PC = 32 / V;
   __shared__ __attribute__((aligned(16))) T tile[32 * P];
-  __shared__ int s_e;
+  __shared__ int s_e, s_mbase;
   const int pos0 = blockIdx.y * 32, c0 = blockIdx.x * TC;
   if (threadIdx.x == 0) {
-    int found = -1;
+    int found = -1, mbase = 0, mb = 0;
     for (int e = 0; e < a.E; ++e) {
       const int kp = (a.kept[e] + kWgradK - 1) / kWgradK * kWgradK;
-      if (kp > 0 && pos0 >= a.koff[e] && pos0 < a.koff[e] + kp) found = e;
+      if (kp > 0 && pos0 >= a.koff[e] && pos0 < a.koff[e] + kp) found = e, mbase = mb;
+      mb += (a.kept[e] + 255) / 256;
     }
     s_e = found;
+    s_mbase = mbase;
   }
   __syncthreads();
   const int e = s_e;
@@ -213,8 +217,14 @@ __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
     u32x4 q = {0u, 0u, 0u, 0u};
     if (i0 + ii < n_rows && c0 + V * cc < a.ncol) {
       const int r = a.offsets[e] + i0 + ii;
-      const int sr = a.rows != nullptr ? a.rows[r] : r;
-      q = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(sr) * a.ncol + c0 + V * cc);
+      if (a.src_tiled) {
+        const int i = i0 + ii, c = c0 + V * cc;
+        const size_t blk = static_cast<size_t>(s_mbase + i / 256) * (a.ncol / 32) + c / 32;
+        q = *reinterpret_cast<const u32x4*>(src + (blk * 256 + i % 256) * 32 + c % 32);
+      } else {
+        const int sr = a.rows != nullptr ? a.rows[r] : r;
+        q = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(sr) * a.ncol + c0 + V * cc);
+      }
       if (a.scale != nullptr) {
         const float sc = a.scale[r];
         T* v = reinterpret_cast<T*>(&q);

@@ -49,6 +49,13 @@ struct GemmArgs {
   int wgrad;
   int M;
   const int32_t* koff;    // [E]
+  // K-step-tiled panels (bf16 MFMA path): the rows of each (expert, 256-row tile) form one panel
+  // of K/32 contiguous 16 KB blocks, block s holding the panel's 256 rows x columns [32 s, 32 s +
+  // 32) in 64-byte rows; panel p = the tile's index in the tile order of all experts' row tiles.
+  // A load of one such block covers whole 128-byte lines, where a row-major tile row gives a half.
+  // The activation epilogues of the bf16 MFMA kernel always write out in this layout (N = its
+  // columns); a_tiled says that A is in it (K = its columns).
+  int a_tiled;
 };
 
 // GEMM1 (activation, bf16 or dtype out), GEMM2 (float out), and the backward's
@@ -85,8 +92,10 @@ __device__ __forceinline__ int segment_rows(const GemmArgs& g, int e) {
 
 // Tile t -> (expert, row tile, column tile); column tiles outer, row tiles inner so that the
 // workgroups sharing one weight panel are adjacent. Returns false past the last tile.
+// `mbase` = row tiles of the experts before e (the panel index of row tile mt is mbase + mt).
 __device__ __forceinline__ bool decode_tile(int tile, const GemmArgs& g, int BM, int tiles_n, int& e, int& mt,
-                                            int& nt) {
+                                            int& nt, int& mbase) {
+  mbase = 0;
   for (int ee = 0; ee < g.E; ++ee) {
     const int tm = (segment_rows(g, ee) + BM - 1) / BM;
     const int cnt = tm * tiles_n;
@@ -97,6 +106,7 @@ __device__ __forceinline__ bool decode_tile(int tile, const GemmArgs& g, int BM,
       return true;
     }
     tile -= cnt;
+    mbase += tm;
   }
   return false;
 }
@@ -236,9 +246,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   tile = __builtin_amdgcn_readfirstlane(tile);
   kpart = __builtin_amdgcn_readfirstlane(kpart);
   parts = __builtin_amdgcn_readfirstlane(parts);
-  int e, mt, nt;
-  decode_tile(tile, g, BM, tiles_n, e, mt, nt);
+  int e, mt, nt, mbase;
+  decode_tile(tile, g, BM, tiles_n, e, mt, nt, mbase);
   e = __builtin_amdgcn_readfirstlane(e);
+  const int panel = __builtin_amdgcn_readfirstlane(mbase + mt);   // K-step-tiled layouts
   mt = __builtin_amdgcn_readfirstlane(mt);
   nt = __builtin_amdgcn_readfirstlane(nt);
   const int m_e = __builtin_amdgcn_readfirstlane(segment_rows(g, e));
@@ -252,9 +263,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int k_last = __builtin_amdgcn_readfirstlane((K / BK) * (kpart + 1) / parts);
   const int nk = k_last - k_first;           // K steps of this part
   const bool gathered = g.rows != nullptr;
-  const char* Ab = reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + kofs +
-                                                 (gathered ? 0 : static_cast<size_t>(row0 + m0) * lda)) +
-                   static_cast<size_t>(k_first) * ROWB;
+  const bool a_tiled = g.a_tiled != 0;
+  const char* Ab = a_tiled ? static_cast<const char*>(g.A) + (static_cast<size_t>(panel) * (g.K / BK) + k_first) * TILE
+                           : reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + kofs +
+                                                           (gathered ? 0 : static_cast<size_t>(row0 + m0) * lda)) +
+                                 static_cast<size_t>(k_first) * ROWB;
   const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
                                                  (g.wgrad ? static_cast<size_t>(n0) * ldb
                                                           : (static_cast<size_t>(e) * N + n0) * ldb)) +
@@ -273,20 +286,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     const int c = lslot ^ ((r / RPS) % CPR);
     const int ra = r < a_last ? r : a_last;
     const uint32_t arow = gathered ? static_cast<uint32_t>(g.rows[row0 + m0 + ra]) : static_cast<uint32_t>(ra);
-    aoff[i] = static_cast<uint32_t>((arow * lda + c * 8) * 2);
+    aoff[i] = a_tiled ? static_cast<uint32_t>(ra * ROWB + c * 16) : static_cast<uint32_t>((arow * lda + c * 8) * 2);
     boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * ldb + c * 8) * 2);
   }
   // the clamped offsets stay below 256 rows of the pitch past the B resource base and below
   // the tile's (or, gathered, all of A's) rows past the A base; anything beyond reads as zero
-  const int span = BM * ldb * 2, span_a = gathered ? g.a_rows * lda * 2 : BM * lda * 2;
+  const int span = BM * ldb * 2, span_a = a_tiled ? TILE : gathered ? g.a_rows * lda * 2 : BM * lda * 2;
   // load q (0..7) of K step min(st, nk-1) into buffer st % NS: A blocks 0..3, then B blocks
   auto issue1 = [&](int st, int q) {
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
-    const uint32_t kb = static_cast<uint32_t>(st < nk ? st : nk - 1) * ROWB;
+    const uint32_t ks = static_cast<uint32_t>(st < nk ? st : nk - 1);
     if (q < LOADS)
-      load_lds16(buffer_rsrc(Ab + kb, span_a), aoff[q], dst + q * 4096);
+      load_lds16(buffer_rsrc(Ab + ks * (a_tiled ? TILE : ROWB), span_a), aoff[q], dst + q * 4096);
     else
-      load_lds16(buffer_rsrc(Bb + kb, span), boff[q - LOADS], dst + TILE + (q - LOADS) * 4096);
+      load_lds16(buffer_rsrc(Bb + ks * ROWB, span), boff[q - LOADS], dst + TILE + (q - LOADS) * 4096);
   };
 
   // fragment addressing: lane (l16, lg) reads row (wave-tile row + 16 i + l16), 16-byte chunk lg
@@ -343,6 +356,22 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
         }
       }
     };
+    // the same block into K-step-tiled panel `panel` of out: its 4 column chunks of 32 go to
+    // blocks (n0 + wn*128)/32 + j, 32 rows x 64 bytes each, two 1 KB stores per chunk. Lane
+    // (row rr, piece pc) with rr running fastest: 8 consecutive lanes read 8 staged rows, whose
+    // pitch puts them on distinct banks.
+    auto rows_out_tiled = [&](const char* stage, int i) {
+      char* pbase = static_cast<char*>(g.out) + static_cast<size_t>(panel) * (N / BK) * TILE;
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const int j = it >> 1, rr = 16 * (it & 1) + (lane & 15), pc = lane >> 4;
+        const int rl = wm * 128 + i * 32 + rr;             // row within the tile = row of the panel
+        const int cb = n0 + wn * 128 + 32 * j;             // first column of the chunk
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * PITCH + (32 * j + 8 * pc) * OB);
+        if (m0 + rl < m_e && cb < N)
+          *reinterpret_cast<u32x4*>(pbase + static_cast<size_t>(cb / BK) * TILE + rl * ROWB + pc * 16) = v;
+      }
+    };
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
 #pragma unroll
@@ -374,7 +403,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
           }
         }
       // the wave reads back only what it wrote itself: LDS keeps one wave's accesses in order
-      rows_out(st, outb, pitch, i);
+      if constexpr (EPI != kEpiLinear)
+        rows_out_tiled(st, i);
+      else
+        rows_out(st, outb, pitch, i);
       if constexpr (PRE && EPI != kEpiLinear)
         rows_out(st2, static_cast<char*>(g.pre) + (static_cast<size_t>(row0 + m0) * N + n0) * OB, N, i);
       __builtin_amdgcn_sched_barrier(0);   // one row block at a time: bounded register use
@@ -395,7 +427,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int rb = m0 + wm * 128 + i * 32;              // first tile row of the block
-      const int valid_rows = max(0, min(32, m_e - rb));
+      // uniform by construction; said so, so that the buffer resource stays in scalar registers
+      const int valid_rows = __builtin_amdgcn_readfirstlane(max(0, min(32, m_e - rb)));
       const char* base = static_cast<const char*>(g.act_in) +
                          (static_cast<size_t>(row0 + rb) * N + n0 + wn * 128) * 2;
       const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, valid_rows * N * 2);
@@ -637,7 +670,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
   __shared__ float Bs[16][17];
   const int tiles_n = (g.N + 15) / 16;
   int e, mt, nt;
-  if (!decode_tile(blockIdx.x, g, FBM, tiles_n, e, mt, nt)) return;
+  int mbase;
+  if (!decode_tile(blockIdx.x, g, FBM, tiles_n, e, mt, nt, mbase)) return;
   const int m_e = segment_rows(g, e);
   const int row0 = (g.dense || g.wgrad) ? 0 : g.offsets[e];
   const int m0 = mt * 16, n0 = nt * 16;
@@ -689,8 +723,8 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs g) {
   const int c = (threadIdx.x % (BN / 4)) * 4;
   for (int u = blockIdx.x; u < plan.L * SLABS; u += gridDim.x) {
     const int s = u / SLABS, slab = u % SLABS;
-    int e, mt, nt;
-    decode_tile(plan.full + s, g, BM, tiles_n, e, mt, nt);
+    int e, mt, nt, mbase;
+    decode_tile(plan.full + s, g, BM, tiles_n, e, mt, nt, mbase);
     const int m_e = segment_rows(g, e);
     const int row0 = g.dense ? 0 : g.offsets[e];
     const int m0 = mt * BM, n0 = nt * BN;
@@ -735,6 +769,13 @@ int ffn_splits(const FfnArgs& a) { return (a.bf16 && a.C > 16) ? kTailMaxParts :
 
 size_t tail_side_floats() { return static_cast<size_t>(255) * kTailTile; }
 
+bool ffn_h_tiled(int bf16, int C) { return bf16 && C > 16; }
+
+size_t ffn_h_rows(int R, int E, int C, int bf16) {
+  // at most R/256 + E row tiles: every expert's last one may be partial
+  return ffn_h_tiled(bf16, C) ? (static_cast<size_t>(R) / 256 + E) * 256 : static_cast<size_t>(R);
+}
+
 template <int ACT>
 static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, int C, int R, int E, int N1, int N2,
                              hipStream_t stream, hipEvent_t ev_mid) {
@@ -772,6 +813,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
   g1.pre = a.pre;
   GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.side,
               nullptr, 0, 0};
+  if (ffn_h_tiled(a.bf16, a.C)) g2.a_tiled = 1;   // GEMM1 runs the MFMA kernel: H is tiled
   if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
     g1.A = a.x;
     g1.rows = a.rows;
@@ -785,6 +827,7 @@ hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream) {
   // one dense expert over the T token rows in order: E = 1, no split of K
   GemmArgs g1{a.x, a.W1, a.b1, a.H, nullptr, nullptr, 1, a.d_ffn, a.d, a.T, a.T, 1, nullptr, nullptr, 0, 1};
   GemmArgs g2{a.H, a.W2, a.b2, a.y, nullptr, nullptr, 1, a.d, a.d_ffn, a.T, a.T, 1, nullptr, nullptr, 0, 1};
+  if (ffn_h_tiled(a.bf16, a.T)) g2.a_tiled = 1;
   return a.act == kActSilu ? launch_ffn<kEpiSilu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr)
                            : launch_ffn<kEpiGelu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr);
 }

@@ -173,10 +173,10 @@ Layout layout_of(const Derived& D) {
   L.dest = take(T * k * 4);
   L.perm = take(R * 4);
   L.x_perm = take(R * static_cast<size_t>(D.d) * D.esize);
-  L.H = take(R * static_cast<size_t>(D.dff) * D.esize);
+  L.H = take(moe::ffn_h_rows(static_cast<int>(R), static_cast<int>(E), clamp_c(D), D.bf16) * D.dff * D.esize);
   L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
   L.side = take(D.bf16 && clamp_c(D) > 16 ? moe::tail_side_floats() * 4 : 0);
-  L.Hs = take(D.dffs > 0 ? T * static_cast<size_t>(D.dffs) * D.esize : 0);
+  L.Hs = take(D.dffs > 0 ? moe::ffn_h_rows(static_cast<int>(T), 1, static_cast<int>(T), D.bf16) * D.dffs * D.esize : 0);
   L.ys = take(D.dffs > 0 ? T * static_cast<size_t>(D.d) * 4 : 0);
   const bool random = D.policy == MOE_DROP_RANDOM, reroute = D.policy == MOE_DROP_REROUTE;
   L.ent = take(D.stats ? ng * 4 : 0);
@@ -795,7 +795,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   rc.src = dy, rc.rows = perm, rc.scale = wrow, rc.ncol = d, rc.dst = dOT;
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols dO");
   rc.src = at<void>(ws, Lw.H), rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = HT;
+  rc.src_tiled = moe::ffn_h_tiled(bf, C) ? 1 : 0;
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols H");
+  rc.src_tiled = 0;
   rc.src = dA, rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = dAT;
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols dA");
   rc.src = x, rc.rows = perm, rc.scale = nullptr, rc.ncol = d, rc.dst = XT;

@@ -108,7 +108,7 @@ struct FfnArgs {
   const void* b1;         // [E,d_ffn] or null
   const void* W2;         // [E,d,d_ffn]
   const void* b2;         // [E,d] or null
-  void* H;                // [R,d_ffn]
+  void* H;                // ffn_h_rows(R, E, C, bf16) x d_ffn: row-major, or tiled panels (ffn_h_tiled)
   float* y_perm;          // [R,d]
   float* side;            // tail_side_floats() floats when ffn_splits() > 1: GEMM2's split-tail parts
   int E, d, d_ffn, R, C;
@@ -126,6 +126,13 @@ bool ffn_gathers(const FfnArgs& a);
 int ffn_splits(const FfnArgs& a);
 // Floats of the side buffer of a tail-split product (255 dense 256 x 256 tiles).
 size_t tail_side_floats();
+// Whether the hidden layer H between the two expert GEMMs is kept in K-step-tiled panels (the
+// bf16 MFMA path): the rows of each (expert, 256-row tile) form one panel of d_ffn/32 contiguous
+// 16 KB blocks of 256 rows x 32 columns, panels in the order of the experts' row tiles. Rows past
+// an expert's segment inside its last panel are never written.
+bool ffn_h_tiled(int bf16, int C);
+// Rows to allocate for H (and the shared expert's H, with R = T, E = 1, C = T).
+size_t ffn_h_rows(int R, int E, int C, int bf16);
 // GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid);
 // The shared expert: one dense FFN over the T token rows of x (no routing):
@@ -136,7 +143,7 @@ struct SharedFfnArgs {
   const void* b1;         // [d_ffn] or null
   const void* W2;         // [d,d_ffn]
   const void* b2;         // [d] or null
-  void* H;                // [T,d_ffn]
+  void* H;                // ffn_h_rows(T, 1, T, bf16) x d_ffn: row-major, or tiled panels (ffn_h_tiled)
   float* y;               // [T,d]
   int T, d, d_ffn;
   int bf16, act;
@@ -236,6 +243,7 @@ struct RowsToColsArgs {
   const int32_t* koff;
   int E, ncol, ld;
   void* dst;
+  int src_tiled;          // src is in the K-step-tiled panels of ffn_h_tiled (rows unused)
 };
 hipError_t launch_rows_to_cols(const RowsToColsArgs& a, int bf16, hipStream_t stream);
 
