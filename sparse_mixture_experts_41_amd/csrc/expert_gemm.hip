@@ -180,6 +180,23 @@ __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t vo
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, voff, 0, 0, 0);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at LDS address p (8-byte aligned).
+__device__ __forceinline__ v4i16 ds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(const_cast<char*>(p)));
+}
+
+// Slot of logical 16-byte chunk c of tile row r (64-byte rows) in LDS: c ^ chunk_swizzle(r).
+// The fragment reads of one instruction cover 16 consecutive rows at one logical chunk (lane
+// group lg reads chunk lg). Measured with SQ_LDS_BANK_CONFLICT, a swizzle on (r / 4) mod 4
+// doubles the LDS cycles of these reads, and (r / 2) mod 4 makes them conflict-free.
+__device__ __forceinline__ int chunk_swizzle(int r) { return (r >> 1) & 3; }
+
+// Chunk swizzle of the N-contiguous B tile's k-row kr: even, so chunk pairs stay together, and
+// distinct over the 8 rows {u, 8 + u} (u < 4) that one half-wave of a transpose read covers.
+__device__ __forceinline__ int bnm_swizzle(int kr) { return 2 * ((kr & 3) | (((kr >> 3) & 1) << 2)); }
+
 // acc += A_blk B_blk^T on one 16x16x32 bf16 block, operands given B first (so acc holds the
 // transposed block), with acc tied to its AGPRs; FIRST starts from zero (srcC = 0).
 template <bool FIRST>
@@ -188,6 +205,25 @@ __device__ __forceinline__ void mfma_16x16x32(floatx4& acc, const bf16x8& b, con
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(b), "v"(a));
   else
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(b), "v"(a));
+}
+
+// load_lds16 written as inline asm, for kernels that read LDS with ds_read_b64_tr_b16: the
+// compiler makes every such read wait for all buffer -> LDS loads in flight (vmcnt(0)), which
+// would drain the operand prefetch on every fragment read. Issued as asm, the loads are
+// invisible to that rule; the kernel orders them itself, as it does for the builtin's loads
+// (vmcnt waits before the barrier that publishes a stage). The resource is built by hand in
+// the layout buffer_rsrc gives (stride 0, num_records = bytes, dword 3 = 0x00020000); base,
+// bytes and the LDS target must be wave-uniform.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load_lds16_asm(const char* base, int bytes, uint32_t voff, void* lds) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const i32x4 rsrc = {__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))),
+                      __builtin_amdgcn_readfirstlane(static_cast<int>((b >> 32) & 0xffff)),
+                      __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+  const int m0 = __builtin_amdgcn_readfirstlane(
+      static_cast<int>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)(lds))));
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(m0)
+               : "memory", "m0");
 }
 
 // Workgroup barrier without the LDS-read wait that __syncthreads adds: the callers order
@@ -204,8 +240,8 @@ __device__ __forceinline__ void barrier_no_lds_wait() { asm volatile("s_barrier"
 // Operand tiles go from global
 // memory straight into LDS (buffer_load_dwordx4 ... lds: 64 lanes fill one contiguous 1 KB
 // block; per-lane offsets are fixed, the K step moves the resource base in scalar registers)
-// through a ring of NS K-steps of BK; the 16-byte chunks of each row are XOR-swizzled so that
-// the 16-byte fragment reads of any 16 consecutive rows hit all 64 banks once.
+// through a ring of NS K-steps of BK; the 16-byte chunks of each row are XOR-swizzled
+// (chunk_swizzle) so that the 16-byte fragment reads run without bank conflicts.
 // The workgroup barrier opens each K step s: after it, step s+1 is complete in LDS (its
 // fragments are read during step s's MFMAs) and the buffer of step s-1 is free for step
 // s+NS-1, so NS-3 steps of loads stay in flight while waiting.
@@ -213,12 +249,18 @@ __device__ __forceinline__ void barrier_no_lds_wait() { asm volatile("s_barrier"
 // the number of loads in flight the same in every iteration.
 // Rows past the segment (or past N) are loaded from the last valid row: they only feed output
 // rows (columns) that are never stored.
-template <int EPI, int BK, int NS>
+// BNM: B is N-contiguous, [E][K][N] (the layout of the forward weights seen from the backward's
+// products). Each K step's B tile is then 32 k-rows of 256 columns (512-byte rows, two whole rows
+// per 1 KB wave load), its 16-byte chunks XOR-swizzled by bnm_swizzle(k), and the fragments come
+// from ds_read_b64_tr_b16: in each 16-lane group, lane 4u + q names 4 consecutive elements of row
+// u of a 4 x 16 block and lane i receives column i of the block (one element from each of the
+// 4 rows), so two such reads give a lane the 8 consecutive k of its column that the MFMA takes.
+// Columns past N read neighbouring data or zeros and feed only outputs that are never stored.
+template <int EPI, int BK, int NS, bool BNM = false>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256;
   constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
   constexpr int RPI = 64 / CPR;              // tile rows per 1 KB wave load
-  constexpr int RPS = 256 / (BK * 2);        // tile rows per 256-byte bank sweep
   constexpr int ROWB = BK * 2;               // bytes per tile row
   constexpr int TILE = BM * ROWB;            // bytes of the A (or B) tile of one K step
   constexpr int STAGE = 2 * TILE;
@@ -268,10 +310,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
                            : reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + kofs +
                                                            (gathered ? 0 : static_cast<size_t>(row0 + m0) * lda)) +
                                  static_cast<size_t>(k_first) * ROWB;
-  const char* Bb = reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
-                                                 (g.wgrad ? static_cast<size_t>(n0) * ldb
-                                                          : (static_cast<size_t>(e) * N + n0) * ldb)) +
-                   static_cast<size_t>(k_first) * ROWB;
+  const char* Bb = BNM ? reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
+                                                      (static_cast<size_t>(e) * g.K + static_cast<size_t>(k_first) * BK) * N + n0)
+                      : reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
+                                                      (g.wgrad ? static_cast<size_t>(n0) * ldb
+                                                               : (static_cast<size_t>(e) * N + n0) * ldb)) +
+                            static_cast<size_t>(k_first) * ROWB;
   const size_t out_base = g.wgrad ? static_cast<size_t>(e) * g.M * N : 0;   // elements
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
@@ -283,32 +327,51 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int r = (wave + 4 * i) * RPI + lrow;
-    const int c = lslot ^ ((r / RPS) % CPR);
+    const int c = lslot ^ chunk_swizzle(r);
     const int ra = r < a_last ? r : a_last;
     const uint32_t arow = gathered ? static_cast<uint32_t>(g.rows[row0 + m0 + ra]) : static_cast<uint32_t>(ra);
     aoff[i] = a_tiled ? static_cast<uint32_t>(ra * ROWB + c * 16) : static_cast<uint32_t>((arow * lda + c * 8) * 2);
-    boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * ldb + c * 8) * 2);
+    if constexpr (BNM) {
+      const int kr = 2 * (wave + 4 * i) + (lane >> 5);     // k-row of the step's B tile
+      boff[i] = static_cast<uint32_t>(kr * N * 2 + (((lane & 31) ^ bnm_swizzle(kr)) * 16));
+    } else {
+      boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * ldb + c * 8) * 2);
+    }
   }
   // the clamped offsets stay below 256 rows of the pitch past the B resource base and below
   // the tile's (or, gathered, all of A's) rows past the A base; anything beyond reads as zero
-  const int span = BM * ldb * 2, span_a = a_tiled ? TILE : gathered ? g.a_rows * lda * 2 : BM * lda * 2;
+  const int span = BNM ? (BK * N - n0) * 2 : BM * ldb * 2;
+  const int span_a = a_tiled ? TILE : gathered ? g.a_rows * lda * 2 : BM * lda * 2;
+  const size_t b_step = BNM ? static_cast<size_t>(BK) * N * 2 : ROWB;   // bytes per K step of B
   // load q (0..7) of K step min(st, nk-1) into buffer st % NS: A blocks 0..3, then B blocks
   auto issue1 = [&](int st, int q) {
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
     const uint32_t ks = static_cast<uint32_t>(st < nk ? st : nk - 1);
-    if (q < LOADS)
-      load_lds16(buffer_rsrc(Ab + ks * (a_tiled ? TILE : ROWB), span_a), aoff[q], dst + q * 4096);
-    else
-      load_lds16(buffer_rsrc(Bb + ks * ROWB, span), boff[q - LOADS], dst + TILE + (q - LOADS) * 4096);
+    if constexpr (BNM) {
+      if (q < LOADS)
+        load_lds16_asm(Ab + ks * (a_tiled ? TILE : ROWB), span_a, aoff[q], dst + q * 4096);
+      else
+        load_lds16_asm(Bb + ks * b_step, span, boff[q - LOADS], dst + TILE + (q - LOADS) * 4096);
+    } else {
+      if (q < LOADS)
+        load_lds16(buffer_rsrc(Ab + ks * (a_tiled ? TILE : ROWB), span_a), aoff[q], dst + q * 4096);
+      else
+        load_lds16(buffer_rsrc(Bb + ks * b_step, span), boff[q - LOADS], dst + TILE + (q - LOADS) * 4096);
+    }
   };
 
   // fragment addressing: lane (l16, lg) reads row (wave-tile row + 16 i + l16), 16-byte chunk lg
   // of the step's 64 bytes: the 8 K values an operand lane holds in v_mfma_f32_16x16x32_bf16
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lg = lane >> 4;
-  const int slot = (lg ^ ((l16 / RPS) % CPR)) * 16;
+  const int slot = (lg ^ chunk_swizzle(l16)) * 16;   // rows 16 i + l16: same swizzle as row l16
   const int a_frag = (wm * 128 + l16) * ROWB + slot;
   const int b_frag = TILE + (wn * 128 + l16) * ROWB + slot;
+  // BNM transpose reads: lane (group lg, 4u + q) reads k-rows 8 lg + 4 h + u of block j at the
+  // 8 bytes of columns wn*128 + 16 j + 4 q; the swizzle depends on u and lg only (not on h)
+  const int tr_u = (lane & 15) >> 2, tr_q = lane & 3;
+  const int tr_sw = bnm_swizzle(8 * lg + tr_u);
+  const int b_tr = TILE + (8 * lg + tr_u) * 512 + (16 * wn + (tr_q >> 1)) * 16 + 8 * (tr_q & 1);
   floatx4 acc[8][8];
 
   // Epilogue. The MFMAs take the B fragment as their first operand, so block (i, j) holds the
@@ -493,7 +556,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       fa[i] = *reinterpret_cast<const bf16x8*>(smem + (st % NS) * STAGE + a_frag + i * 16 * ROWB);
     };
     auto rd_b = [&](int st, int f, int j) {
-      fb[f][j] = *reinterpret_cast<const bf16x8*>(smem + (st % NS) * STAGE + b_frag + j * 16 * ROWB);
+      if constexpr (BNM) {
+        const char* p = smem + (st % NS) * STAGE + b_tr + (((2 * j) ^ tr_sw) * 16);
+        const v4i16 lo = ds_read_tr16(p), hi = ds_read_tr16(p + 4 * 512);
+        fb[f][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else {
+        fb[f][j] = *reinterpret_cast<const bf16x8*>(smem + (st % NS) * STAGE + b_frag + j * 16 * ROWB);
+      }
     };
     // K step s: barrier, then per 16-row block i one operand load of step s+NS-1, the block's 8
     // MFMAs on fragments of step s, and reads of step s+1's fragments. FIRST: srcC = 0.
@@ -834,8 +903,9 @@ hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream) {
 
 // ---------------------------------------------------------------------------------------
 // Backward products (the weights already transposed, so every operand is K-contiguous).
+// bnm: on the bf16 MFMA path B is N-contiguous ([E][K][N]); elsewhere B is always [E][N][K].
 template <int EPI>
-static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStream_t stream) {
+static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStream_t stream, bool bnm = false) {
   if (!bf16) {
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<EPI>, dim3(tile_grid(g.R, g.E, C, FBM, g.N, 16)), dim3(256), 0,
                        stream, g);
@@ -844,7 +914,10 @@ static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStrea
                        stream, g);
   } else {
     const int grid = round_grid(tile_grid(g.R, g.E, C, 256, g.N, 256) + (g.splits > 1 ? 256 : 0));
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
+    if (bnm)
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 4, true>), dim3(grid), dim3(256), 0, stream, g);
+    else
+      hipLaunchKernelGGL((grouped_gemm_bf16_kernel<EPI, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
     if (EPI == kEpiLinear && g.splits > 1) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
@@ -854,12 +927,15 @@ static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStrea
   return hipGetLastError();
 }
 
+bool bwd_weights_transposed(int bf16, int C) { return !(bf16 && C > 16); }
+
 hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream) {
+  const bool bnm = !bwd_weights_transposed(a.bf16, a.C);
   GemmArgs g{};
   g.A = a.A;
   g.rows = a.rows;
   g.a_rows = a.a_rows;
-  g.B = a.W2T;
+  g.B = bnm ? a.W2 : a.W2T;
   g.out = a.dA;
   g.kept = a.kept;
   g.offsets = a.offsets;
@@ -871,8 +947,8 @@ hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream) {
   g.splits = 1;
   g.row_scale = a.wrow;
   g.act_in = a.pre;
-  return a.act == kActSilu ? launch_rows_gemm<kEpiSiluGrad>(g, a.bf16, a.C, stream)
-                           : launch_rows_gemm<kEpiGeluGrad>(g, a.bf16, a.C, stream);
+  return a.act == kActSilu ? launch_rows_gemm<kEpiSiluGrad>(g, a.bf16, a.C, stream, bnm)
+                           : launch_rows_gemm<kEpiGeluGrad>(g, a.bf16, a.C, stream, bnm);
 }
 
 int bwd_dx_splits(int R, int E, int C, int d, int d_ffn, int bf16) {
@@ -881,9 +957,10 @@ int bwd_dx_splits(int R, int E, int C, int d, int d_ffn, int bf16) {
 }
 
 hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream) {
+  const bool bnm = !bwd_weights_transposed(a.bf16, a.C);
   GemmArgs g{};
   g.A = a.dA;
-  g.B = a.W1T;
+  g.B = bnm ? a.W1 : a.W1T;
   g.out = a.dXp;
   g.out2 = a.side;
   g.kept = a.kept;
@@ -894,7 +971,7 @@ hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream) {
   g.R = a.R;
   g.C = a.C;
   g.splits = bwd_dx_splits(a.R, a.E, a.C, a.d, a.d_ffn, a.bf16);
-  return launch_rows_gemm<kEpiLinear>(g, a.bf16, a.C, stream);
+  return launch_rows_gemm<kEpiLinear>(g, a.bf16, a.C, stream, bnm);
 }
 
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {

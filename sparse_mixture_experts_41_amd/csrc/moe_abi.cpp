@@ -200,8 +200,9 @@ Layout layout_of(const Derived& D) {
   L.dz = take(tr ? T * E * 4 : 0);
   L.dA = take(tr ? R * dff * es : 0);
   L.dXp = take(tr ? R * d * 4 : 0);
-  L.W2T = take(tr ? E * d * dff * es : 0);
-  L.W1T = take(tr ? E * d * dff * es : 0);
+  const bool wt = tr && moe::bwd_weights_transposed(D.bf16, clamp_c(D));
+  L.W2T = take(wt ? E * d * dff * es : 0);
+  L.W1T = take(wt ? E * d * dff * es : 0);
   L.dOT = take(d * ldz * es);
   L.HT = take(dff * ldz * es);
   L.dAT = take(dff * ldz * es);
@@ -744,11 +745,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   MOE_HIP(moe::launch_bwd_router(ra, bf, st), "bwd_router");
   MOE_HIP(moe::launch_wgrad_offsets(kept, E, koff, st), "wgrad_offsets");
   if (ev) MOE_HIP(hipEventRecord(ev[1], st), "event");
-  // 2. the weights transposed: W2 [E,d,dff] -> W2T [E,dff,d]; W1 [E,dff,d] -> W1T [E,d,dff]
-  void* W2T = at<void>(ws, Lw.W2T);
-  void* W1T = at<void>(ws, Lw.W1T);
-  MOE_HIP(moe::launch_transpose(W2, W2T, E, d, dff, bf, st), "transpose W2");
-  MOE_HIP(moe::launch_transpose(W1, W1T, E, dff, d, bf, st), "transpose W1");
+  // 2. off the bf16 MFMA path, the weights transposed: W2 [E,d,dff] -> W2T [E,dff,d] and
+  // W1 [E,dff,d] -> W1T [E,d,dff] (the MFMA path reads them as given)
+  void* W2T = nullptr;
+  void* W1T = nullptr;
+  if (moe::bwd_weights_transposed(bf, C)) {
+    W2T = at<void>(ws, Lw.W2T);
+    W1T = at<void>(ws, Lw.W1T);
+    MOE_HIP(moe::launch_transpose(W2, W2T, E, d, dff, bf, st), "transpose W2");
+    MOE_HIP(moe::launch_transpose(W1, W1T, E, dff, d, bf, st), "transpose W1");
+  }
   if (ev) MOE_HIP(hipEventRecord(ev[2], st), "event");
   // 3. dA = (w dy W2) * act'(a); dXp = dA W1
   moe::BwdDactArgs da{};
@@ -762,6 +768,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
     MOE_HIP(moe::launch_gather(dy, perm, kept, offsets, E, R, static_cast<int>(d * D.esize), dyp, st), "gather dy");
     da.A = dyp;
   }
+  da.W2 = W2;
   da.W2T = W2T;
   da.wrow = wrow;
   da.pre = at<void>(ws, Lw.pre);
@@ -777,7 +784,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   da.act = D.act;
   MOE_HIP(moe::launch_bwd_dact(da, st), "bwd_dact");
   if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
-  moe::BwdDxArgs dxa{dA, W1T, dXp, bf && C > 16 ? at<float>(ws, Lw.side) : nullptr, kept, offsets, E, d, dff, R, C, bf};
+  moe::BwdDxArgs dxa{dA, W1, W1T, dXp, bf && C > 16 ? at<float>(ws, Lw.side) : nullptr, kept, offsets, E, d, dff, R, C, bf};
   MOE_HIP(moe::launch_bwd_dx(dxa, st), "bwd_dx");
   if (ev) MOE_HIP(hipEventRecord(ev[4], st), "event");
   // 4. weight gradients: each expert's rows as zero-padded columns, then per-expert products

@@ -162,13 +162,19 @@ hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k
 // Backward pass.
 constexpr int kWgradK = 32;   // rows of a weight-gradient product are padded to this granule
 
+// Whether the backward products need the weights transposed (W2T, W1T): off the bf16 MFMA path.
+// On it they read W2 and W1 as given, N-contiguous, through LDS transpose reads.
+bool bwd_weights_transposed(int bf16, int C);
+
 // dA[r] = (A_row(r) W2_e) * wrow[r] * act'(pre[r]) over each expert's segment rows, where
 // A_row(r) = A[rows[r]] (rows set: the bf16 MFMA path reads dy through the permutation) or A[r]
-// (an expert-sorted copy); W2T [E, d_ffn, d] is W2 transposed. dA and pre: [R, d_ffn] dtype.
+// (an expert-sorted copy). W2 [E, d, d_ffn] as given; W2T [E, d_ffn, d] is W2 transposed, read
+// (and needed) only when bwd_weights_transposed(). dA and pre: [R, d_ffn] dtype.
 struct BwdDactArgs {
   const void* A;
   const int32_t* rows;
   int a_rows;
+  const void* W2;
   const void* W2T;
   const float* wrow;
   const void* pre;
@@ -179,10 +185,12 @@ struct BwdDactArgs {
 };
 hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream);
 
-// dXp[r] = dA[r] W1_e (float, [R, d]); W1T [E, d, d_ffn] is W1 transposed. With
-// bwd_dx_splits() > 1 the last round's tiles are tail-split through `side` (tail_side_floats()).
+// dXp[r] = dA[r] W1_e (float, [R, d]); W1 [E, d_ffn, d] as given, W1T [E, d, d_ffn] its transpose
+// (read only when bwd_weights_transposed()). With bwd_dx_splits() > 1 the last round's tiles are
+// tail-split through `side` (tail_side_floats()).
 struct BwdDxArgs {
   const void* dA;
+  const void* W1;
   const void* W1T;
   float* dXp;
   float* side;
