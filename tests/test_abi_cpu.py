@@ -212,8 +212,18 @@ def test_training_entry_points_validate_on_the_host(lib):
     lib.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n_fwd))
     c = CONFIGS["mixtral_like"]
     R = min(c.k * c.T, c.E * oracle.capacity(c.T, c.E, c.k, c.capacity_factor))
-    # saved pre-activations, the two transposed weights and the transposed activations at least
-    assert n.value >= n_fwd.value + R * c.d_ffn * 2 + 2 * c.E * c.d * c.d_ffn * 2 + 2 * (c.d + c.d_ffn) * R * 2
+    # saved pre-activations and the transposed activations at least; the bf16 MFMA path reads the
+    # weights as given, so the workspace holds no transposed copy of them (2 E d d_ffn bf16)
+    need = n_fwd.value + R * c.d_ffn * 2 + 2 * (c.d + c.d_ffn) * R * 2
+    wt = 2 * c.E * c.d * c.d_ffn * 2
+    assert need <= n.value < need + wt
+    # the float32 path multiplies transposed weights: its workspace holds both copies
+    cfg32 = _cfg("tiny_fp32")
+    n32, n32_fwd = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.moe_workspace_size_train(ctypes.byref(cfg32), None, ctypes.byref(n32)) == MOE_OK
+    lib.moe_workspace_size(ctypes.byref(cfg32), ctypes.byref(n32_fwd))
+    t = CONFIGS["tiny_fp32"]
+    assert n32.value >= n32_fwd.value + 2 * t.E * t.d * t.d_ffn * 4
     shared = MoeVariant(shared_d_ffn=1024)
     assert lib.moe_workspace_size_train(ctypes.byref(cfg), ctypes.byref(shared), ctypes.byref(n)) == MOE_EUNSUPPORTED
     # moe_backward rejects bad arguments before any HIP call
