@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
 // kWgradK), dst[n][koff[e] + i] = scale[r] * src[row(r)][n] with r = offsets[e] + i while
 // i < kept[e] (row(r) = rows[r] when gathering, else r; no scale when null), 0 past it.
 // With src_tiled the source row i of expert e is row i mod 256 of K-step-tiled panel
-// (row tiles of the experts before e) + i / 256.
+// (row tiles of the experts before e) + i / 256. With dst_tiled, dst[n][p] sits at row n mod 256
+// of block p / 32 of panel n / 256 (ld / 32 blocks of 256 x 32 per panel).
 // Tiles of 32 padded positions x 16 vectors of columns (128 bf16 or 64 floats); tile j
 // belongs to the expert whose padded range holds position 32 j; tiles past the last expert
 // exit. 16-byte loads of source rows; 16-byte stores of destination rows gathered from LDS.
@@ -242,8 +243,11 @@ __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
     T v[V];
 #pragma unroll
     for (int u = 0; u < V; ++u) v[u] = tile[(V * pc + u) * P + c];
-    *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(c0 + c) * a.ld + pos0 + V * pc) =
-        *reinterpret_cast<const u32x4*>(v);
+    const int n = c0 + c;
+    const size_t o = a.dst_tiled ? (static_cast<size_t>(n / 256) * (a.ld / 32) + pos0 / 32) * (256 * 32) +
+                                       static_cast<size_t>(n % 256) * 32 + V * pc
+                                 : static_cast<size_t>(n) * a.ld + pos0 + V * pc;
+    *reinterpret_cast<u32x4*>(dst + o) = *reinterpret_cast<const u32x4*>(v);
   }
 }
 
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
 // then an xor butterfly.
 template <typename T>
 __global__ __launch_bounds__(256) void segment_rowsum_kernel(const T* __restrict__ src, const int32_t* __restrict__ kept,
-                                                            const int32_t* __restrict__ koff, int M, int ld,
+                                                            const int32_t* __restrict__ koff, int M, int ld, int tiled,
                                                             float* __restrict__ db) {
   constexpr int V = Vec<T>::N;
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -260,10 +264,16 @@ __global__ __launch_bounds__(256) void segment_rowsum_kernel(const T* __restrict
   if (m >= M) return;
   const int lane = lane_id();
   const int kp = (kept[e] + kWgradK - 1) / kWgradK * kWgradK;   // a multiple of V
-  const T* row = src + static_cast<size_t>(m) * ld + (kp > 0 ? koff[e] : 0);
+  const int k0 = kp > 0 ? koff[e] : 0;
+  const T* row = src + static_cast<size_t>(m) * ld + k0;
   float acc = 0.0f;
   for (int i = lane * V; i < kp; i += kWave * V) {
-    const u32x4 q = *reinterpret_cast<const u32x4*>(row + i);
+    // tiled: position k0 + i of row m is element (m mod 256, (k0 + i) mod 32) of block
+    // (k0 + i) / 32 of panel m / 256; a vector of V never crosses a block (k0, i multiples of V)
+    const T* p = tiled ? src + (static_cast<size_t>(m / 256) * (ld / 32) + (k0 + i) / 32) * (256 * 32) +
+                             static_cast<size_t>(m % 256) * 32 + (k0 + i) % 32
+                       : row + i;
+    const u32x4 q = *reinterpret_cast<const u32x4*>(p);
     const T* v = reinterpret_cast<const T*>(&q);
 #pragma unroll
     for (int u = 0; u < V; ++u) acc += to_f32(v[u]);
@@ -511,10 +521,10 @@ hipError_t launch_segment_rowsum(const void* src, const int32_t* kept, const int
   const dim3 grid((M + 3) / 4, E);
   if (bf16)
     hipLaunchKernelGGL(segment_rowsum_kernel<u16>, grid, dim3(256), 0, stream, static_cast<const u16*>(src), kept,
-                       koff, M, ld, db);
+                       koff, M, ld, wgrad_tiled(bf16) ? 1 : 0, db);
   else
     hipLaunchKernelGGL(segment_rowsum_kernel<float>, grid, dim3(256), 0, stream, static_cast<const float*>(src),
-                       kept, koff, M, ld, db);
+                       kept, koff, M, ld, wgrad_tiled(bf16) ? 1 : 0, db);
   return hipGetLastError();
 }
 

@@ -54,8 +54,11 @@ struct GemmArgs {
   // 32) in 64-byte rows; panel p = the tile's index in the tile order of all experts' row tiles.
   // A load of one such block covers whole 128-byte lines, where a row-major tile row gives a half.
   // The activation epilogues of the bf16 MFMA kernel always write out in this layout (N = its
-  // columns); a_tiled says that A is in it (K = its columns).
+  // columns); a_tiled says that A is in it (K = its columns). In the weight-gradient mode A and
+  // B are [M, ld] / [N, ld] in the layout of wgrad_tiled (a_tiled, b_tiled): panel = row tile,
+  // ld / 32 blocks per panel, and expert e's K steps start at block koff[e] / 32.
   int a_tiled;
+  int b_tiled;
 };
 
 // GEMM1 (activation, bf16 or dtype out), GEMM2 (float out), and the backward's
@@ -306,12 +309,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int nk = k_last - k_first;           // K steps of this part
   const bool gathered = g.rows != nullptr;
   const bool a_tiled = g.a_tiled != 0;
-  const char* Ab = a_tiled ? static_cast<const char*>(g.A) + (static_cast<size_t>(panel) * (g.K / BK) + k_first) * TILE
+  const bool b_tiled = !BNM && g.b_tiled != 0;
+  // tiled operands: panel index, blocks per panel and the first block of this tile's K range
+  const size_t a_blk0 = g.wgrad ? (static_cast<size_t>(mt) * (lda / BK) + kofs / BK)
+                                : static_cast<size_t>(panel) * (g.K / BK);
+  const char* Ab = a_tiled ? static_cast<const char*>(g.A) + (a_blk0 + k_first) * TILE
                            : reinterpret_cast<const char*>(static_cast<const u16*>(g.A) + kofs +
                                                            (gathered ? 0 : static_cast<size_t>(row0 + m0) * lda)) +
                                  static_cast<size_t>(k_first) * ROWB;
   const char* Bb = BNM ? reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
                                                       (static_cast<size_t>(e) * g.K + static_cast<size_t>(k_first) * BK) * N + n0)
+                  : b_tiled ? static_cast<const char*>(g.B) + (static_cast<size_t>(nt) * (ldb / BK) + kofs / BK + k_first) * TILE
                       : reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
                                                       (g.wgrad ? static_cast<size_t>(n0) * ldb
                                                                : (static_cast<size_t>(e) * N + n0) * ldb)) +
@@ -335,14 +343,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       const int kr = 2 * (wave + 4 * i) + (lane >> 5);     // k-row of the step's B tile
       boff[i] = static_cast<uint32_t>(kr * N * 2 + (((lane & 31) ^ bnm_swizzle(kr)) * 16));
     } else {
-      boff[i] = static_cast<uint32_t>((static_cast<uint32_t>(r < b_last ? r : b_last) * ldb + c * 8) * 2);
+      const uint32_t rb = static_cast<uint32_t>(r < b_last ? r : b_last);
+      boff[i] = b_tiled ? rb * ROWB + c * 16 : (rb * ldb + c * 8) * 2;
     }
   }
   // the clamped offsets stay below 256 rows of the pitch past the B resource base and below
   // the tile's (or, gathered, all of A's) rows past the A base; anything beyond reads as zero
-  const int span = BNM ? (BK * N - n0) * 2 : BM * ldb * 2;
+  const int span = BNM ? (BK * N - n0) * 2 : b_tiled ? TILE : BM * ldb * 2;
   const int span_a = a_tiled ? TILE : gathered ? g.a_rows * lda * 2 : BM * lda * 2;
-  const size_t b_step = BNM ? static_cast<size_t>(BK) * N * 2 : ROWB;   // bytes per K step of B
+  const size_t b_step = BNM ? static_cast<size_t>(BK) * N * 2 : b_tiled ? TILE : ROWB;   // bytes per K step of B
   // load q (0..7) of K step min(st, nk-1) into buffer st % NS: A blocks 0..3, then B blocks
   auto issue1 = [&](int st, int q) {
     char* dst = smem + (st % NS) * STAGE + wave * 1024;
@@ -929,6 +938,12 @@ static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStrea
 
 bool bwd_weights_transposed(int bf16, int C) { return !(bf16 && C > 16); }
 
+bool wgrad_tiled(int bf16) { return bf16 != 0; }   // the bf16 weight gradients run the MFMA kernel
+
+size_t wgrad_rows(int rows, int bf16) {
+  return wgrad_tiled(bf16) ? (static_cast<size_t>(rows) + 255) / 256 * 256 : static_cast<size_t>(rows);
+}
+
 hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream) {
   const bool bnm = !bwd_weights_transposed(a.bf16, a.C);
   GemmArgs g{};
@@ -991,6 +1006,7 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {
   g.C = a.C;
   g.splits = 1;
   g.wgrad = 1;
+  g.a_tiled = g.b_tiled = wgrad_tiled(a.bf16) ? 1 : 0;
   if (!a.bf16) {
     const int grid = a.E * ((a.M + 15) / 16) * ((a.N + 15) / 16);
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<kEpiLinear>, dim3(grid), dim3(256), 0, stream, g);

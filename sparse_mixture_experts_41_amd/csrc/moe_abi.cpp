@@ -203,10 +203,10 @@ Layout layout_of(const Derived& D) {
   const bool wt = tr && moe::bwd_weights_transposed(D.bf16, clamp_c(D));
   L.W2T = take(wt ? E * d * dff * es : 0);
   L.W1T = take(wt ? E * d * dff * es : 0);
-  L.dOT = take(d * ldz * es);
-  L.HT = take(dff * ldz * es);
-  L.dAT = take(dff * ldz * es);
-  L.XT = take(d * ldz * es);
+  L.dOT = take(moe::wgrad_rows(static_cast<int>(d), D.bf16) * ldz * es);
+  L.HT = take(moe::wgrad_rows(static_cast<int>(dff), D.bf16) * ldz * es);
+  L.dAT = take(moe::wgrad_rows(static_cast<int>(dff), D.bf16) * ldz * es);
+  L.XT = take(moe::wgrad_rows(static_cast<int>(d), D.bf16) * ldz * es);
   L.dwg = take(tr ? static_cast<size_t>(moe::dwg_slices(D.T, D.d, D.E)) * (E * d + E) * 4 : 0);
   L.dyp = take(tr && !bwd_gathers(D) ? R * d * es : 0);
   L.total = off;
@@ -799,6 +799,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   rc.koff = koff;
   rc.E = E;
   rc.ld = ld;
+  rc.dst_tiled = moe::wgrad_tiled(bf) ? 1 : 0;
   rc.src = dy, rc.rows = perm, rc.scale = wrow, rc.ncol = d, rc.dst = dOT;
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols dO");
   rc.src = at<void>(ws, Lw.H), rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = HT;

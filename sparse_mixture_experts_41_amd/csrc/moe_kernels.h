@@ -203,7 +203,9 @@ hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream);
 
 // out[e] = A[:, koff[e] : +K_e] B[:, koff[e] : +K_e]^T (float [E, M, N]) with K_e = kept[e]
 // rounded up to kWgradK; A [M, ld] and B [N, ld] dtype hold each expert's rows as columns, zero
-// past kept[e]. Experts with kept[e] = 0 are not written.
+// past kept[e]. Experts with kept[e] = 0 are not written. With wgrad_tiled() the [rows, ld]
+// operands are K-step-tiled: panel p (rows 256 p .. 256 p + 255) is ld/32 contiguous blocks of
+// 256 rows x 32 positions (64-byte rows), wgrad_rows(rows) rows allocated.
 struct WgradArgs {
   const void* A;
   const void* B;
@@ -212,6 +214,8 @@ struct WgradArgs {
   const int32_t* koff;
   int E, M, N, ld, C, bf16;
 };
+bool wgrad_tiled(int bf16);
+size_t wgrad_rows(int rows, int bf16);
 hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream);
 
 // koff[e] = sum over e' < e of kept[e'] rounded up to kWgradK; koff[E] = the total.
@@ -252,10 +256,12 @@ struct RowsToColsArgs {
   int E, ncol, ld;
   void* dst;
   int src_tiled;          // src is in the K-step-tiled panels of ffn_h_tiled (rows unused)
+  int dst_tiled;          // dst is in the K-step-tiled layout of wgrad_tiled (ncol rows)
 };
 hipError_t launch_rows_to_cols(const RowsToColsArgs& a, int bf16, hipStream_t stream);
 
-// db[e][m] = sum_i src[m][koff[e] + i] over expert e's padded columns (float [E, M]).
+// db[e][m] = sum_i src[m][koff[e] + i] over expert e's padded columns (float [E, M]); src in
+// the layout of wgrad_tiled(bf16).
 hipError_t launch_segment_rowsum(const void* src, const int32_t* kept, const int32_t* koff, int E, int M, int ld,
                                  int bf16, float* db, hipStream_t stream);
 
