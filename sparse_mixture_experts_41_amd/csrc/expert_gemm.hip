@@ -538,14 +538,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
           *reinterpret_cast<bf16x4*>(pa) = pk;
         }
       }
+      // out (dA) goes to K-step-tiled panel `panel`, as H does: chunk j (32 columns) of the
+      // block is 32 rows x 64 bytes at block (n0 + wn*128)/32 + j, two 1 KB stores per chunk;
+      // 16 lanes with one piece read 16 rows whose swizzle spreads them over the banks
+      char* pbase = static_cast<char*>(g.out) + static_cast<size_t>(panel) * (N / BK) * TILE;
 #pragma unroll
       for (int it = 0; it < 8; ++it) {
-        const int rr = 4 * it + lane / 16, pc = lane % 16;
-        const int rw = m0 + wm * 128 + i * 32 + rr;
-        const int c = n0 + wn * 128 + pc * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(blk + rr * 256 + ((pc ^ (rr % 16)) * 16));
-        if (rw < m_e && c < N)
-          *reinterpret_cast<u32x4*>(static_cast<char*>(g.out) + (static_cast<size_t>(row0 + rw) * N + c) * 2) = v;
+        const int j = it >> 1, rr = 16 * (it & 1) + (lane & 15), pc = lane >> 4;
+        const int rl = wm * 128 + i * 32 + rr;             // row within the tile = row of the panel
+        const int cb = n0 + wn * 128 + 32 * j;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(blk + rr * 256 + (((4 * j + pc) ^ (rr % 16)) * 16));
+        if (m0 + rl < m_e && cb < N)
+          *reinterpret_cast<u32x4*>(pbase + static_cast<size_t>(cb / BK) * TILE + rl * ROWB + pc * 16) = v;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -986,6 +990,7 @@ hipError_t launch_bwd_dx(const BwdDxArgs& a, hipStream_t stream) {
   g.R = a.R;
   g.C = a.C;
   g.splits = bwd_dx_splits(a.R, a.E, a.C, a.d, a.d_ffn, a.bf16);
+  g.a_tiled = ffn_h_tiled(a.bf16, a.C) ? 1 : 0;   // dA comes from the MFMA kernel's gradient epilogue
   return launch_rows_gemm<kEpiLinear>(g, a.bf16, a.C, stream, bnm);
 }
 

@@ -198,7 +198,7 @@ Layout layout_of(const Derived& D) {
   L.koff = take(tr ? (E + 1) * 4 : 0);
   L.wrow = take(tr ? R * 4 : 0);
   L.dz = take(tr ? T * E * 4 : 0);
-  L.dA = take(tr ? R * dff * es : 0);
+  L.dA = take(tr ? moe::ffn_h_rows(static_cast<int>(R), static_cast<int>(E), clamp_c(D), D.bf16) * dff * es : 0);
   L.dXp = take(tr ? R * d * 4 : 0);
   const bool wt = tr && moe::bwd_weights_transposed(D.bf16, clamp_c(D));
   L.W2T = take(wt ? E * d * dff * es : 0);
@@ -805,9 +805,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   rc.src = at<void>(ws, Lw.H), rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = HT;
   rc.src_tiled = moe::ffn_h_tiled(bf, C) ? 1 : 0;
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols H");
-  rc.src_tiled = 0;
-  rc.src = dA, rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = dAT;
+  rc.src = dA, rc.rows = nullptr, rc.scale = nullptr, rc.ncol = dff, rc.dst = dAT;   // tiled like H
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols dA");
+  rc.src_tiled = 0;
   rc.src = x, rc.rows = perm, rc.scale = nullptr, rc.ncol = d, rc.dst = XT;
   MOE_HIP(moe::launch_rows_to_cols(rc, bf, st), "rows_to_cols X");
   if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");

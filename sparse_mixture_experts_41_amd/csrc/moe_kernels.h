@@ -169,7 +169,8 @@ bool bwd_weights_transposed(int bf16, int C);
 // dA[r] = (A_row(r) W2_e) * wrow[r] * act'(pre[r]) over each expert's segment rows, where
 // A_row(r) = A[rows[r]] (rows set: the bf16 MFMA path reads dy through the permutation) or A[r]
 // (an expert-sorted copy). W2 [E, d, d_ffn] as given; W2T [E, d_ffn, d] is W2 transposed, read
-// (and needed) only when bwd_weights_transposed(). dA and pre: [R, d_ffn] dtype.
+// (and needed) only when bwd_weights_transposed(). pre: [R, d_ffn] dtype. dA: like H, in the
+// K-step-tiled panels of ffn_h_tiled() on the MFMA path (ffn_h_rows rows), else [R, d_ffn].
 struct BwdDactArgs {
   const void* A;
   const int32_t* rows;
