@@ -11,7 +11,9 @@ device synchronisations. Prints one JSON line:
   stage_ms      per-stage means from HIP events recorded inside moe_forward on its stream;
   roofline      the dominant expert GEMM kernel: algorithmic FLOPs (2 d d_ffn per kept row)
                 over its measured duration, against the bf16 dense MFMA peak (2.5 PFLOP/s);
-  cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the same workload.
+  cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the same workload;
+  cold_cache    the median event-measured forward when each call follows a 1 GiB write that
+                evicts L2 and the MALL (value and stage_ms are warm, back-to-back steps).
 """
 from __future__ import annotations
 
@@ -55,6 +57,9 @@ def _args():
     ap.add_argument("--train", action="store_true",
                     help="time the training step instead: moe_forward_train + moe_backward (one JSON line)")
     ap.add_argument("--lam", type=float, default=0.01, help="weight of the balance loss in the training step")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="after the timed steps, this many forwards each preceded by a 1 GiB write that "
+                         "evicts L2 and the 256 MB MALL, timed with HIP events (0: skip)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (3 times) and exit: the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -264,6 +269,23 @@ def main() -> int:
             stage[n] += v / args.steps
         ev.close()
 
+    # warm: the median event-measured forward of the timed steps; cold: forwards that each follow
+    # a 1 GiB write (L2 and MALL hold none of the inputs or weights when they start)
+    warm_event_ms = float(np.median([sum(ev.totals) / max(ev.samples, 1) for ev in events]))
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cold_ms = []
+        for r in range(args.cold_reps):
+            flush.fill_(r & 255)
+            ev = ops.StageEvents()
+            plan.run(events=ev)
+            cold_ms.append(sum(ev.accumulate()))
+            ev.close()
+        del flush
+        cold_med = float(np.median(cold_ms))
+        cold = {"ms_per_step": cold_med, "tokens_per_s": shape.T / (cold_med * 1e-3), "reps": args.cold_reps,
+                "flush_bytes": 1 << 30, "warm_event_ms_per_step": warm_event_ms}
     kept = int(plan.out["kept"].sum().item())
     counts = plan.out["counts"].cpu().numpy()
     T, d, E, k, dff = shape.T, shape.d, shape.E, shape.k, shape.d_ffn
@@ -318,6 +340,7 @@ def main() -> int:
             "peak_GB/s": PEAK_HBM_GBS,
         },
         "stage_ms": stage,
+        "cold_cache": cold,
         "counts_minmax": [int(counts.min()), int(counts.max())],
     }
     if route_stats is not None:
