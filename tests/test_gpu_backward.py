@@ -53,6 +53,13 @@ CASES = {
                              recipe="zipf_bias", wg_std=None, seed=4), 0.0, "gelu", 0.0, "random", 1.0),
     "bf16_split_dx": (S("bf16_split_dx", T=2048, d=256, E=4, k=2, d_ffn=1024, capacity_factor=1.0, seed=6), 0.0,
                       "gelu", 0.1, "token", 0.01),
+    # tiled-panel edges: two experts spill one row into a second 256-row panel (kept 249, 257,
+    # 257); d = 192 and d_ffn = 320 leave partial column panels in every product
+    "bf16_panel_257": (S("bf16_panel_257", T=771, d=192, E=3, k=1, d_ffn=320, capacity_factor=1.0, wg_std=None),
+                       0.05, "gelu", 0.0, "token", 0.2),
+    # three panels per expert (kept 712 to 758), SiLU, rerouted overflow
+    "bf16_edges_k2_silu": (S("bf16_edges_k2_silu", T=1100, d=192, E=3, k=2, d_ffn=320, capacity_factor=1.05,
+                             wg_std=None), 0.1, "silu", 0.0, "reroute", 0.1),
 }
 
 

@@ -47,6 +47,11 @@ SMALL = {
     # tokens spanning many 16-token routing groups and 64-token permutation waves, E not a multiple of 16
     "many_blocks": (MoEShape("many_blocks", T=3000, d=128, E=37, k=4, d_ffn=128, capacity_factor=1.1,
                              wg_std=None), 0.0),
+    # tiled-panel edges: C = 256, two experts keep exactly one full 256-row panel (kept 249, 256,
+    # 256); d = 192 and d_ffn = 320 leave partial column panels and a 6-step K
+    "panel_256": (MoEShape("panel_256", T=768, d=192, E=3, k=1, d_ffn=320, capacity_factor=1.0, wg_std=None), 0.05),
+    # C = 257: two experts spill one row into a second panel (kept 249, 257, 257)
+    "panel_257": (MoEShape("panel_257", T=771, d=192, E=3, k=1, d_ffn=320, capacity_factor=1.0, wg_std=None), 0.05),
 }
 
 
