@@ -843,6 +843,8 @@ int tile_grid(int R, int E, int C, int BM, int N, int BN) {
 
 }  // namespace
 
+bool ffn_gather_tiled(const FfnArgs& a) { return ffn_h_tiled(a.bf16, a.C) && a.d_ffn >= kTiledGatherMinDff; }
+
 bool ffn_gathers(const FfnArgs& a) {
   return a.bf16 && a.C > 16 && static_cast<long long>(a.T) * a.d * 2 < (1ll << 31);
 }
@@ -896,6 +898,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
   GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.side,
               nullptr, 0, 0};
   if (ffn_h_tiled(a.bf16, a.C)) g2.a_tiled = 1;   // GEMM1 runs the MFMA kernel: H is tiled
+  if (a.x_tiled) g1.a_tiled = 1;
   if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
     g1.A = a.x;
     g1.rows = a.rows;
