@@ -583,46 +583,7 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
   }
 }
 
-// x rows in expert-sorted order, written as the K-step-tiled panels GEMM1 reads (panel = row tile
-// of the experts in order, blocks of 256 rows x 32 columns, 64-byte rows). Workgroup g takes
-// 16-row group g of the experts' segments (each expert's rows in groups of 16, experts in order);
-// wave w copies 32-column chunks w, w + 4, ... of its 16 rows, lane (row lane & 15, 16-byte
-// piece lane >> 4), so each store instruction writes 16 consecutive rows of one block (1 KB).
-// Groups past the last expert's rows exit; rows past an expert's kept count are not written.
-__global__ __launch_bounds__(256) void gather_tiled_kernel(const u16* __restrict__ x, const int32_t* __restrict__ perm,
-                                                           const int32_t* __restrict__ kept,
-                                                           const int32_t* __restrict__ offsets, int E, int d,
-                                                           u16* __restrict__ xt) {
-  int g = blockIdx.x, e = -1, mbase = 0;
-  for (int ee = 0; ee < E; ++ee) {
-    const int n = (kept[ee] + 15) / 16;
-    if (g < n) {
-      e = ee;
-      break;
-    }
-    g -= n;
-    mbase += (kept[ee] + 255) / 256;
-  }
-  if (e < 0) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = 16 * g + (lane & 15), p = lane >> 4;      // row of the expert's segment, piece
-  if (i >= kept[e]) return;
-  const int t = perm[offsets[e] + i];
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + static_cast<size_t>(t) * d) + p;
-  u16* dst = xt + (static_cast<size_t>(mbase + i / 256) * (d / 32) * 256 + i % 256) * 32 + 8 * p;
-  for (int c = wave; c < d / 32; c += 4)
-    *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(c) * 256 * 32) = src[4 * c];
-}
-
 }  // namespace
-
-hipError_t launch_gather_tiled(const void* x, const int32_t* perm, const int32_t* kept, const int32_t* offsets, int E,
-                               int R, int d, void* x_tiled, hipStream_t stream) {
-  const int groups = R / 16 + E;    // at least sum over e of ceil(kept[e] / 16)
-  hipLaunchKernelGGL(gather_tiled_kernel, dim3(groups), dim3(256), 0, stream, static_cast<const u16*>(x), perm, kept,
-                     offsets, E, d, static_cast<u16*>(x_tiled));
-  return hipGetLastError();
-}
 
 hipError_t launch_colsum(const float* part, int ng, int E, float* out, hipStream_t stream) {
   hipLaunchKernelGGL(colsum_kernel, dim3(1), dim3(kScanThreads), 0, stream, part, ng, E, out);

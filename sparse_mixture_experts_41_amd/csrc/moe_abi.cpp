@@ -172,7 +172,7 @@ Layout layout_of(const Derived& D) {
   L.offsets = take(E * 4);
   L.dest = take(T * k * 4);
   L.perm = take(R * 4);
-  L.x_perm = take(moe::ffn_h_rows(static_cast<int>(R), static_cast<int>(E), clamp_c(D), D.bf16) * D.d * D.esize);
+  L.x_perm = take(R * static_cast<size_t>(D.d) * D.esize);
   L.H = take(moe::ffn_h_rows(static_cast<int>(R), static_cast<int>(E), clamp_c(D), D.bf16) * D.dff * D.esize);
   L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
   L.side = take(D.bf16 && clamp_c(D) > 16 ? moe::tail_side_floats() * 4 : 0);
@@ -584,16 +584,11 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   fa.side = at<float>(ws, Lw.side);
   fa.act = D.act;
   fa.pre = train ? at<void>(ws, Lw.pre) : nullptr;
-  if (moe::ffn_gather_tiled(fa)) {
-    // GEMM1 reads the token rows from K-step-tiled panels (whole-line loads)
-    MOE_HIP(moe::launch_gather_tiled(x, perm, kept, offsets, D.E, D.R, D.d, x_perm, st), "gather");
-    fa.x_tiled = 1;
-  } else if (moe::ffn_gathers(fa)) {
+  if (moe::ffn_gathers(fa))
     fa.rows = perm;   // GEMM1 reads the token rows of x through the permutation
-  } else {
+  else
     MOE_HIP(moe::launch_gather(x, perm, kept, offsets, D.E, D.R, static_cast<int>(D.d * D.esize), x_perm, st),
             "gather");
-  }
   if (ev) MOE_HIP(hipEventRecord(ev[3], st), "event");
   MOE_HIP(moe::launch_expert_ffn(fa, st, ev ? ev[4] : nullptr), "expert_ffn");
   // 4b. the shared expert on every token (timed with the second expert GEMM)

@@ -91,10 +91,6 @@ hipError_t launch_permute_reroute(const int32_t* idx, const int32_t* cand, const
 hipError_t launch_permute(const int32_t* idx, const int32_t* blockbase, const int32_t* offsets,
                           int T, int E, int k, int C, int32_t* dest, int32_t* perm, hipStream_t stream);
 
-// bf16 x rows in expert-sorted order (x[perm[r]]) written in the K-step-tiled panels of
-// ffn_h_tiled() (d columns, ffn_h_rows(R, E, C, 1) rows allocated).
-hipError_t launch_gather_tiled(const void* x, const int32_t* perm, const int32_t* kept, const int32_t* offsets, int E,
-                               int R, int d, void* x_tiled, hipStream_t stream);
 hipError_t launch_gather(const void* x, const int32_t* perm, const int32_t* kept, const int32_t* offsets,
                          int E, int R, int row_bytes, void* x_perm, hipStream_t stream);
 
@@ -105,7 +101,6 @@ struct FfnArgs {
   const void* x_perm;     // [R,d] (unused when rows is set)
   const void* x;          // [T,d] token rows, read through `rows` (bf16 MFMA path only)
   const int32_t* rows;    // [R] or null: x row of expert-sorted row r (perm); see ffn_gathers
-  int x_tiled;            // x_perm is in the tiled panels of ffn_h_tiled (launch_gather_tiled)
   int T;
   const int32_t* kept;    // [E]
   const int32_t* offsets; // [E]
@@ -124,13 +119,6 @@ struct FfnArgs {
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
 // copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
 bool ffn_gathers(const FfnArgs& a);
-// Whether the forward copies the token rows into K-step-tiled panels for GEMM1 instead
-// (launch_gather_tiled): on the MFMA path when d_ffn >= kTiledGatherMinDff. The copy moves
-// 4 R d bytes at copy speed, and the whole-line loads it buys GEMM1 save time in proportion to
-// d_ffn. Measured per forward: Mixtral-like (d_ffn 14336) -33 us GEMM1 for +21 us of copy;
-// d_ffn 8192: -218 us for +189 us; d_ffn 4096: nothing saved for +14 us.
-constexpr int kTiledGatherMinDff = 8192;
-bool ffn_gather_tiled(const FfnArgs& a);
 // Most K parts a tile of the last, partial round of GEMM2 is split into (1 = no tail split):
 // kTailMaxParts on the bf16 MFMA path, 1 elsewhere. Part 0 writes y_perm, the other parts
 // write `side`, and a fixup kernel adds them to y_perm in part order, so y_perm alone is the

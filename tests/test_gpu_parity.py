@@ -52,9 +52,9 @@ SMALL = {
     "panel_256": (MoEShape("panel_256", T=768, d=192, E=3, k=1, d_ffn=320, capacity_factor=1.0, wg_std=None), 0.05),
     # C = 257: two experts spill one row into a second panel (kept 249, 257, 257)
     "panel_257": (MoEShape("panel_257", T=771, d=192, E=3, k=1, d_ffn=320, capacity_factor=1.0, wg_std=None), 0.05),
-    # d_ffn >= 8192: the token rows are copied into tiled panels for GEMM1 (two panels per expert)
-    "tiled_gather": (MoEShape("tiled_gather", T=600, d=128, E=3, k=2, d_ffn=8192, capacity_factor=1.0,
-                              wg_std=None), 0.05),
+    # d_ffn = 8192: GEMM1 over 32 column panels with pair-staged A rows read through the
+    # permutation, two row panels per expert
+    "wide_ffn": (MoEShape("wide_ffn", T=600, d=128, E=3, k=2, d_ffn=8192, capacity_factor=1.0, wg_std=None), 0.05),
 }
 
 
