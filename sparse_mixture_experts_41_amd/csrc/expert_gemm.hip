@@ -259,13 +259,15 @@ __device__ __forceinline__ void barrier_no_lds_wait() { asm volatile("s_barrier"
 // u of a 4 x 16 block and lane i receives column i of the block (one element from each of the
 // 4 rows), so two such reads give a lane the 8 consecutive k of its column that the MFMA takes.
 // Columns past N read neighbouring data or zeros and feed only outputs that are never stored.
-// AP (row-major A, not tiled): A is staged by K-step pairs. Each A row's 128 bytes of steps 2q and
-// 2q+1 are one LDS row of pair buffer q mod 3 (three 32 KB buffers), so a 1 KB wave load covers
-// 8 rows x 128 bytes, whole lines, where a one-step stage takes 16 half lines; the 16-byte chunks
-// of a 128-byte row are swizzled by row mod 8 (conflict-free for the fragment reads, measured).
-// B keeps its NS-step ring after the pair buffers (96 + 64 KB of LDS). Step s issues B's loads of
-// step s+3 and, when s is even, A's loads of pair s/2 + 2, so every step's wait is vmcnt <= 12.
-template <int EPI, int BK, int NS, bool BNM = false, bool AP = false>
+// PAIR = 1 (row-major A, not tiled) or 2 (row-major B): that operand is staged by K-step pairs.
+// Each of its rows' 128 bytes of steps 2q and 2q+1 are one LDS row of pair buffer q mod 3 (three
+// 32 KB buffers), so a 1 KB wave load covers 8 rows x 128 bytes, whole lines, where a one-step
+// stage takes 16 half lines; the 16-byte chunks of a 128-byte row are swizzled by row mod 8
+// (conflict-free for the fragment reads, measured). The other operand keeps its NS-step ring
+// after the pair buffers (96 + 64 KB of LDS). Step s issues that operand's loads of step s+3
+// and, when s is even, the paired operand's loads of pair s/2 + 2, so every step's wait is
+// vmcnt <= 12.
+template <int EPI, int BK, int NS, bool BNM = false, int PAIR = 0>
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256;
   constexpr int CPR = BK / 8;                // 16-byte chunks per tile row
@@ -275,13 +277,15 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   constexpr int STAGE = 2 * TILE;
   constexpr int LOADS = BM / RPI / 4;        // 1 KB loads per wave per operand per K step
   constexpr int PER_STAGE = 2 * LOADS;       // vm operations per thread per K step
-  constexpr int PAIRB = 2 * ROWB;            // AP: bytes of an A row of a K-step pair
-  constexpr int APAIR = BM * PAIRB;          // AP: bytes of an A pair buffer
-  constexpr int NPA = 3;                     // AP: A pair buffers
-  constexpr int B_OFF = NPA * APAIR;         // AP: start of the B ring
-  constexpr int SMEM = AP ? B_OFF + NS * TILE : NS * STAGE;
+  constexpr bool AP = PAIR == 1, BP = PAIR == 2;
+  constexpr int PAIRB = 2 * ROWB;            // paired: bytes of a row of a K-step pair
+  constexpr int APAIR = BM * PAIRB;          // paired: bytes of a pair buffer
+  constexpr int NPA = 3;                     // paired: pair buffers
+  constexpr int RING = NPA * APAIR;          // paired: start of the other operand's ring
+  constexpr int SMEM = PAIR ? RING + NS * TILE : NS * STAGE;
   static_assert(NS >= 3 && SMEM <= 160 * 1024, "LDS ring");
-  static_assert(!AP || NS == 4, "the pair schedule assumes B loads three steps ahead");
+  static_assert(!PAIR || NS == 4, "the pair schedule assumes loads three steps ahead");
+  static_assert(!(BP && BNM), "N-major B has its own staging");
   static_assert(BK == 32, "one v_mfma_f32_16x16x32_bf16 K step per K step");
   static_assert(PER_STAGE == 8, "one operand load per 16-row MFMA block");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
@@ -342,7 +346,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 
   // direct loads: wave w fills 1 KB blocks w, w+4, ... of each operand tile
   const int lrow = lane / CPR, lslot = lane % CPR;
-  uint32_t aoff[AP ? 8 : LOADS], boff[LOADS];
+  uint32_t aoff[AP ? 8 : LOADS], boff[BP ? 8 : LOADS];
   const int a_last = m_e - 1 - m0, b_last = N - 1 - n0;
   if constexpr (AP) {
 #pragma unroll
@@ -353,6 +357,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       const int ra = r < a_last ? r : a_last;
       const uint32_t arow = gathered ? static_cast<uint32_t>(g.rows[row0 + m0 + ra]) : static_cast<uint32_t>(ra);
       aoff[j] = static_cast<uint32_t>((arow * lda + c * 8) * 2);
+    }
+  }
+  if constexpr (BP) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {   // as for A above, over B's rows
+      const int r = 8 * (wave + 4 * j) + (lane >> 3), c = (lane & 7) ^ (r & 7);
+      const uint32_t rb = static_cast<uint32_t>(r < b_last ? r : b_last);
+      boff[j] = (rb * ldb + c * 8) * 2;
     }
   }
 #pragma unroll
@@ -367,7 +379,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     if constexpr (BNM) {
       const int kr = 2 * (wave + 4 * i) + (lane >> 5);     // k-row of the step's B tile
       boff[i] = static_cast<uint32_t>(kr * N * 2 + (((lane & 31) ^ bnm_swizzle(kr)) * 16));
-    } else {
+    } else if constexpr (!BP) {
       const uint32_t rb = static_cast<uint32_t>(r < b_last ? r : b_last);
       boff[i] = b_tiled ? rb * ROWB + c * 16 : (rb * ldb + c * 8) * 2;
     }
@@ -377,28 +389,36 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int span = BNM ? (BK * N - n0) * 2 : b_tiled ? TILE : BM * ldb * 2;
   const int span_a = a_tiled ? TILE : gathered ? g.a_rows * lda * 2 : BM * lda * 2;
   const size_t b_step = BNM ? static_cast<size_t>(BK) * N * 2 : b_tiled ? TILE : ROWB;   // bytes per K step of B
-  // LDS start of step st's B tile and of its A tile (AP: of its pair's buffer)
-  auto b_stage = [&](int st) { return AP ? B_OFF + (st % NS) * TILE : (st % NS) * STAGE + TILE; };
-  auto a_stage = [&](int st) { return AP ? ((st >> 1) % NPA) * APAIR : (st % NS) * STAGE; };
+  // LDS start of step st's A and B tiles (of its pair's buffer for the paired operand)
+  auto a_stage = [&](int st) {
+    return AP ? ((st >> 1) % NPA) * APAIR : BP ? RING + (st % NS) * TILE : (st % NS) * STAGE;
+  };
+  auto b_stage = [&](int st) {
+    return BP ? ((st >> 1) % NPA) * APAIR : AP ? RING + (st % NS) * TILE : (st % NS) * STAGE + TILE;
+  };
   auto load = [&](const char* base, int bytes, uint32_t voff, char* lds) {
     if constexpr (BNM)
       load_lds16_asm(base, bytes, voff, lds);
     else
       load_lds16(buffer_rsrc(base, bytes), voff, lds);
   };
-  // load q (0..7) of K step min(st, nk-1): A blocks 0..3 (not AP), then B blocks
+  // load q (0..7) of K step min(st, nk-1): A blocks 0..3, then B blocks (not the paired operand)
   auto issue1 = [&](int st, int q) {
     const uint32_t ks = static_cast<uint32_t>(st < nk ? st : nk - 1);
     if (!AP && q < LOADS)
       load(Ab + ks * (a_tiled ? TILE : ROWB), span_a, aoff[q], smem + a_stage(st) + wave * 1024 + q * 4096);
-    else if (q >= LOADS)
+    else if (!BP && q >= LOADS)
       load(Bb + ks * b_step, span, boff[q - LOADS], smem + b_stage(st) + wave * 1024 + (q - LOADS) * 4096);
   };
-  // AP: A load j (0..7) of pair min(pq, last pair) into buffer pq mod 3
+  // paired operand: load j (0..7) of pair min(pq, last pair) into buffer pq mod 3
   auto issue_pair = [&](int pq, int j) {
     const int last = (nk - 1) >> 1;
     const uint32_t qq = static_cast<uint32_t>(pq < last ? pq : last);
-    load(Ab + qq * PAIRB, span_a, aoff[j], smem + (pq % NPA) * APAIR + (wave + 4 * j) * 1024);
+    char* dst = smem + (pq % NPA) * APAIR + (wave + 4 * j) * 1024;
+    if constexpr (AP)
+      load(Ab + qq * PAIRB, span_a, aoff[j], dst);
+    else
+      load(Bb + qq * PAIRB, span, boff[j], dst);
   };
 
   // fragment addressing: lane (l16, lg) reads row (wave-tile row + 16 i + l16), 16-byte chunk lg
@@ -407,7 +427,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int slot = (lg ^ chunk_swizzle(l16)) * 16;   // rows 16 i + l16: same swizzle as row l16
   const int a_frag = (wm * 128 + l16) * ROWB + slot;
-  const int a_frag_ap = (wm * 128 + l16) * PAIRB;    // AP: row of the pair buffer; swizzle l16 mod 8
+  const int a_frag_ap = (wm * 128 + l16) * PAIRB;    // paired A: row of the pair buffer; swizzle l16 mod 8
+  const int b_frag_bp = (wn * 128 + l16) * PAIRB;    // paired B
   const int b_frag = (wn * 128 + l16) * ROWB + slot;
   // BNM transpose reads: lane (group lg, 4u + q) reads k-rows 8 lg + 4 h + u of block j at the
   // 8 bytes of columns wn*128 + 16 j + 4 q; the swizzle depends on u and lg only (not on h)
@@ -610,6 +631,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
         const char* p = smem + b_stage(st) + b_tr + (((2 * j) ^ tr_sw) * 16);
         const v4i16 lo = ds_read_tr16(p), hi = ds_read_tr16(p + 4 * 512);
         fb[f][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      } else if constexpr (BP) {
+        fb[f][j] = *reinterpret_cast<const bf16x8*>(smem + b_stage(st) + b_frag_bp + j * 16 * PAIRB +
+                                                    (((4 * (st & 1) + lg) ^ (l16 & 7)) * 16));
       } else {
         fb[f][j] = *reinterpret_cast<const bf16x8*>(smem + b_stage(st) + b_frag + j * 16 * ROWB);
       }
@@ -619,18 +643,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     auto step = [&](int s, auto f_const, auto first_const) {
       constexpr int F = decltype(f_const)::value;
       constexpr bool FIRST = decltype(first_const)::value;
-      // this thread's loads of step s+1 have landed (AP: the loads issued after B's of step s+1
-      // are A's of pair (s-2)/2 + 2 when s is even, then step s-1's: 12 either way)
-      wait_vmcnt<AP ? 12 : (NS - 3) * PER_STAGE>();
+      // this thread's loads of step s+1 have landed (paired: the loads issued after the other
+      // operand's of step s+1 are the pair's of (s-2)/2 + 2 when s is even, then step s-1's: 12
+      // either way)
+      wait_vmcnt<PAIR ? 12 : (NS - 3) * PER_STAGE>();
       // Everyone's have, and step s-1's buffer is free: every wave consumed its reads of step
-      // s-1 (issued during step s-2) in the MFMAs it ran before arriving here. AP: pair
+      // s-1 (issued during step s-2) in the MFMAs it ran before arriving here. Paired: pair
       // (s-2)/2's buffer is free at an even step s, which refills it with pair s/2 + 2.
       barrier_no_lds_wait();
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (AP) {
+        if constexpr (PAIR) {
           if (i < 4) {
-            issue1(s + NS - 1, LOADS + i);
+            issue1(s + NS - 1, AP ? LOADS + i : i);
           } else if (F == 0) {
             issue_pair((s >> 1) + 2, 2 * (i - 4));
             issue_pair((s >> 1) + 2, 2 * (i - 4) + 1);
@@ -646,19 +671,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
         if (i < NR) rd_a(s + 1, i);         // past the last step this reads unused data
       }
     };
-    if constexpr (AP) {
-      // the loop's pattern for steps -4..-1: pair 0, B 0, B 1 and pair 1, B 2
+    if constexpr (PAIR) {
+      // the loop's pattern for steps -4..-1: pair 0, other 0, other 1 and pair 1, other 2
+      constexpr int Q0 = AP ? LOADS : 0;     // the other operand's loads
 #pragma unroll
       for (int j = 0; j < 8; ++j) issue_pair(0, j);
 #pragma unroll
       for (int st = 0; st < 2; ++st)
 #pragma unroll
-        for (int q = LOADS; q < PER_STAGE; ++q) issue1(st, q);
+        for (int q = Q0; q < Q0 + LOADS; ++q) issue1(st, q);
 #pragma unroll
       for (int j = 0; j < 8; ++j) issue_pair(1, j);
 #pragma unroll
-      for (int q = LOADS; q < PER_STAGE; ++q) issue1(2, q);
-      wait_vmcnt<16>();                      // pair 0 and B 0 have landed
+      for (int q = Q0; q < Q0 + LOADS; ++q) issue1(2, q);
+      wait_vmcnt<16>();                      // pair 0 and the other operand's step 0 have landed
     } else {
 #pragma unroll
       for (int st = 0; st < NS - 1; ++st)
@@ -945,13 +971,15 @@ static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, 
   }
   const int grid1 = round_grid(tile_grid(R, E, C, 256, N1, 256));
   const int grid2 = round_grid(tile_grid(R, E, C, 256, N2, 256) + (g2.splits > 1 ? 256 : 0));
-  if (g1.a_tiled)
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, 32, 4>), dim3(grid1), dim3(256), 0, stream, g1);
-  else   // the token rows row-major (gathered through the permutation or a plain copy): pair staging
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, 32, 4, false, true>), dim3(grid1), dim3(256), 0, stream, g1);
+  // GEMM1's A (the token rows, gathered or a plain copy) and GEMM2's B (W2) are row-major:
+  // pair staging for them; GEMM2's A (H) is K-step-tiled
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, 32, 4, false, 1>), dim3(grid1), dim3(256), 0, stream, g1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
+  if (g2.a_tiled)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4, false, 2>), dim3(grid2), dim3(256), 0, stream, g2);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (g2.splits > 1) hipLaunchKernelGGL(tail_fixup_kernel, dim3(kFixupGrid), dim3(256), 0, stream, g2);
   return hipGetLastError();
