@@ -13,7 +13,12 @@ device synchronisations. Prints one JSON line:
                 over its measured duration, against the bf16 dense MFMA peak (2.5 PFLOP/s);
   cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the same workload;
   cold_cache    the median event-measured forward when each call follows a 1 GiB write that
-                evicts L2 and the MALL (value and stage_ms are warm, back-to-back steps).
+                evicts L2 and the MALL (value and stage_ms are warm, back-to-back steps);
+  weights       --weights packed (the default where the shape allows it: bf16, d and d_ffn
+                multiples of 256) hands W1 and W2 over in the panel layout of
+                moe_pack_expert_weights, packed once before the warm-up as a server does when
+                it loads the weights (pack_ms). row_major repeats the timing with nn.Linear's
+                layout; both give bit-identical outputs.
 """
 from __future__ import annotations
 
@@ -57,6 +62,8 @@ def _args():
     ap.add_argument("--train", action="store_true",
                     help="time the training step instead: moe_forward_train + moe_backward (one JSON line)")
     ap.add_argument("--lam", type=float, default=0.01, help="weight of the balance loss in the training step")
+    ap.add_argument("--weights", choices=("packed", "row-major"), default="packed",
+                    help="expert weight layout of the forward (packed where the shape allows it)")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="after the timed steps, this many forwards each preceded by a 1 GiB write that "
                          "evicts L2 and the 256 MB MALL, timed with HIP events (0: skip)")
@@ -251,23 +258,47 @@ def main() -> int:
         variant = ops.make_variant(cfg, args.activation, args.noise_std, shared, args.drop_policy, route_stats)
     if args.train:
         return train_step(args, shape, cfg, tensors, variant, ops, torch)
+
+    def timed(plan):
+        """W warm-up steps, then K timed steps: (host ms per step, mean stage ms, the events)."""
+        for _ in range(args.warmup):
+            plan.run()
+        torch.cuda.synchronize()
+        events = [ops.StageEvents() for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            plan.run(events=events[i])
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        stage = {n: 0.0 for n in ops.STAGE_NAMES}
+        for ev in events:
+            for n, v in zip(ops.STAGE_NAMES, ev.accumulate()):
+                stage[n] += v / args.steps
+            ev.close()
+        return (t1 - t0) * 1e3 / args.steps, stage, events
+
+    packed = (args.weights == "packed" and shape.dtype == "bf16" and shape.d % 256 == 0
+              and shape.d_ffn % 256 == 0)
+    row_major = None
+    pack_ms = None
+    if packed:
+        rm_ms, rm_stage, _ = timed(ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant))
+        row_major = {"ms_per_step": rm_ms, "tokens_per_s": shape.T / (rm_ms * 1e-3),
+                     "expert_gemm1_gelu_ms": rm_stage["expert_gemm1_gelu"],
+                     "expert_gemm2_ms": rm_stage["expert_gemm2"]}
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        W1p, W2p = ops.pack_expert_weights(tensors[3]), ops.pack_expert_weights(tensors[5])
+        end.record()
+        torch.cuda.synchronize()
+        pack_ms = start.elapsed_time(end)
+        tensors = tensors[:3] + [W1p, tensors[4], W2p, tensors[6]]
+        shared = variant[1].get("shared") if variant is not None else None
+        variant = ops.make_variant(cfg, args.activation, args.noise_std, shared, args.drop_policy, route_stats,
+                                   packed_weights=True)
     plan = ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant)
-    for _ in range(args.warmup):
-        plan.run()
-    torch.cuda.synchronize()
-    events = [ops.StageEvents() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        plan.run(events=events[i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    stage = {n: 0.0 for n in ops.STAGE_NAMES}
-    for ev in events:
-        for n, v in zip(ops.STAGE_NAMES, ev.accumulate()):
-            stage[n] += v / args.steps
-        ev.close()
+    ms_per_step, stage, events = timed(plan)
 
     # warm: the median event-measured forward of the timed steps; cold: forwards that each follow
     # a 1 GiB write (L2 and MALL hold none of the inputs or weights when they start)
@@ -324,6 +355,7 @@ def main() -> int:
         "config": {"workload": shape.name, "T": T, "d": d, "E": E, "k": k, "d_ffn": dff,
                    "capacity_factor": shape.capacity_factor, "temperature": shape.temperature,
                    "gumbel": shape.gumbel, "parallelism": "none (one GPU)",
+                   "weights": "packed" if packed else "row-major",
                    **({"variant": {"activation": args.activation, "noise_std": args.noise_std,
                                    "shared_d_ffn": args.shared_d_ffn, "drop_policy": args.drop_policy,
                                    "route_stats": args.route_stats}} if with_variant else {})},
@@ -341,6 +373,8 @@ def main() -> int:
         },
         "stage_ms": stage,
         "cold_cache": cold,
+        "row_major": row_major,
+        "pack_ms": pack_ms,
         "counts_minmax": [int(counts.min()), int(counts.max())],
     }
     if route_stats is not None:

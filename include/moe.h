@@ -178,6 +178,15 @@ typedef enum {
                                weights                                                         */
 } moe_drop_policy;
 
+/* Storage of W1 and W2 (the routed experts' weights; a shared expert's stay row-major). */
+typedef enum {
+  MOE_WEIGHTS_LINEAR = 0,   /* nn.Linear's row-major [E,d_ffn,d] and [E,d,d_ffn]                */
+  MOE_WEIGHTS_PACKED = 1    /* the same bytes reordered by moe_pack_expert_weights: a layout for
+                               serving, packed once when the weights are loaded. bf16 only, d
+                               and d_ffn multiples of 256; the results are bit-identical to the
+                               row-major layout's. Not taken by the training entry points.     */
+} moe_weight_layout;
+
 /* Number of floats moe_variant.route_stats receives. */
 #define MOE_ROUTE_STATS 5
 
@@ -200,7 +209,7 @@ typedef struct moe_variant {
   const void* W2s;         /* [d, shared_d_ffn] dtype (required when shared_d_ffn > 0)        */
   const void* b2s;         /* [d] dtype, nullable                                             */
   int32_t drop_policy;     /* moe_drop_policy                                                 */
-  int32_t reserved;        /* must be 0                                                       */
+  int32_t weight_layout;   /* moe_weight_layout of W1 and W2                                    */
   float* route_stats;      /* nullable; else [MOE_ROUTE_STATS] f32 on the device, written by the
                               layer from the counts before capacity (u_e = counts_e / T) and
                               the full softmax p, each in float64 rounded once to float32
@@ -214,8 +223,9 @@ typedef struct moe_variant {
 
 /* Workspace bytes of moe_forward_ex for `cfg` and `variant` (nullable). Host only.
  * MOE_EINVAL for an unknown activation or drop policy, a negative or non-finite noise_std,
- * noise_std > 0 together with gumbel = 1, a nonzero reserved field, or a misaligned
- * route_stats; MOE_EUNSUPPORTED for a shared_d_ffn the dtype cannot take. */
+ * noise_std > 0 together with gumbel = 1, an unknown weight_layout, or a misaligned
+ * route_stats; MOE_EUNSUPPORTED for a shared_d_ffn the dtype cannot take, or packed weights
+ * with float32, or d or d_ffn not a multiple of 256. */
 moe_status moe_workspace_size_ex(const moe_config* cfg, const moe_variant* variant, size_t* bytes);
 
 /* The layer with the variant's activation, router noise and shared expert; arguments as
@@ -226,6 +236,21 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_variant* variant, con
                           const void* W2, const void* b2, void* y, float* f, float* P, float* L,
                           int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws,
                           size_t ws_bytes, moe_stream_t stream);
+
+/* Packs one expert weight tensor for variant.weight_layout = MOE_WEIGHTS_PACKED: W [E,rows,cols]
+ * row-major bf16 (W1 with rows = d_ffn, cols = d; W2 with rows = d, cols = d_ffn) -> W_packed,
+ * E*rows*cols bf16 values in panels: panel e*(rows/256) + p holds rows [256 p, 256 p + 256) of
+ * expert e as cols/32 consecutive blocks of 256 rows x 32 columns, each row of a block the 64
+ * contiguous bytes of its 32 values. The expert GEMMs then load each K step of a 256-row tile
+ * as one contiguous 16 KB block (whole cache lines) instead of 256 half lines. Pure data
+ * movement, no rounding. Both pointers are device pointers, 16-byte aligned, caller-owned and
+ * must not overlap. Asynchronous on `stream`.
+ * MOE_EINVAL: a NULL or misaligned pointer, overlapping buffers, E < 1, rows < 1, cols < 1, any
+ * of them above 2^20, or E*rows*cols above 2^40;
+ * MOE_EUNSUPPORTED: rows not a multiple of 256 or cols not a multiple of 32; MOE_EHIP: the
+ * launch failed. */
+moe_status moe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* W, void* W_packed,
+                                   moe_stream_t stream);
 
 /* ---------------------------------------------------------------------------------------
  * Backward pass (kwkr.cn page on sparse activation, sections 2.2, 2.3 and 3.3): the gradients

@@ -40,13 +40,14 @@ class MoeForwardAux(ctypes.Structure):
 MOE_ACT_GELU, MOE_ACT_SILU = 0, 1
 MOE_DROP_TOKEN_ORDER, MOE_DROP_RANDOM, MOE_DROP_REROUTE = 0, 1, 2
 MOE_ROUTE_STATS = 5
+MOE_WEIGHTS_LINEAR, MOE_WEIGHTS_PACKED = 0, 1
 
 
 class MoeVariant(ctypes.Structure):
     _fields_ = [
         ("activation", ctypes.c_int32), ("noise_std", ctypes.c_float), ("shared_d_ffn", ctypes.c_int64),
         ("W1s", ctypes.c_void_p), ("b1s", ctypes.c_void_p), ("W2s", ctypes.c_void_p), ("b2s", ctypes.c_void_p),
-        ("drop_policy", ctypes.c_int32), ("reserved", ctypes.c_int32), ("route_stats", ctypes.c_void_p),
+        ("drop_policy", ctypes.c_int32), ("weight_layout", ctypes.c_int32), ("route_stats", ctypes.c_void_p),
     ]
 
 
@@ -81,6 +82,7 @@ _SIGS = {
                                          ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),
     "moe_backward": (ctypes.c_int, [_CFG, _VAR, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.POINTER(MoeBackwardAux), _P, ctypes.c_size_t, _P]),
+    "moe_pack_expert_weights": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
     "moe_temperature_at": (ctypes.c_float, [ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_float]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),

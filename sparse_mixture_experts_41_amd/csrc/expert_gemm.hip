@@ -56,7 +56,9 @@ struct GemmArgs {
   // The activation epilogues of the bf16 MFMA kernel always write out in this layout (N = its
   // columns); a_tiled says that A is in it (K = its columns). In the weight-gradient mode A and
   // B are [M, ld] / [N, ld] in the layout of wgrad_tiled (a_tiled, b_tiled): panel = row tile,
-  // ld / 32 blocks per panel, and expert e's K steps start at block koff[e] / 32.
+  // ld / 32 blocks per panel, and expert e's K steps start at block koff[e] / 32. Outside that
+// mode, b_tiled says that B holds packed weights: panel e N/256 + t is rows [256 t, 256 t + 256)
+// of expert e's [N, K] matrix (N a multiple of 256), as pack_weights_kernel writes them.
   int a_tiled;
   int b_tiled;
 };
@@ -335,7 +337,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
                                  static_cast<size_t>(k_first) * ROWB;
   const char* Bb = BNM ? reinterpret_cast<const char*>(static_cast<const u16*>(g.B) +
                                                       (static_cast<size_t>(e) * g.K + static_cast<size_t>(k_first) * BK) * N + n0)
-                  : b_tiled ? static_cast<const char*>(g.B) + (static_cast<size_t>(nt) * (ldb / BK) + kofs / BK + k_first) * TILE
+                  : b_tiled ? static_cast<const char*>(g.B) + ((g.wgrad ? static_cast<size_t>(nt)
+                                                           : static_cast<size_t>(e) * tiles_n + nt) * (ldb / BK) +
+                                                  kofs / BK + k_first) * TILE
                       : reinterpret_cast<const char*>(static_cast<const u16*>(g.B) + kofs +
                                                       (g.wgrad ? static_cast<size_t>(n0) * ldb
                                                                : (static_cast<size_t>(e) * N + n0) * ldb)) +
@@ -767,11 +771,17 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
   const int ar = row0 + (r16 < m_e ? r16 : m_e - 1);
   const u16* __restrict__ ap = static_cast<const u16*>(g.A) +
                                static_cast<size_t>(g.rows != nullptr ? g.rows[ar] : ar) * K + 16 * grp;
+  // a lane's 16 elements of row n at K offset kc + 16 grp lie at bp + kc * kstep: in row-major
+  // weights, and in packed ones, where those 16 sit in one 64-byte row of K block kc/32 + grp/2
   const u16* bp[2];
+  const int kstep = g.b_tiled ? 256 : 1;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n = min(nbase + t * 16 + r16, N - 1);
-    bp[t] = static_cast<const u16*>(g.B) + (static_cast<size_t>(e) * N + n) * K + 16 * grp;
+    bp[t] = static_cast<const u16*>(g.B) +
+            (g.b_tiled ? ((static_cast<size_t>(e) * (N / 256) + n / 256) * (K / 32) + (grp >> 1)) * 8192 +
+                             (n % 256) * 32 + 16 * (grp & 1)
+                       : (static_cast<size_t>(e) * N + n) * K + 16 * grp);
   }
   floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   int kc = 0;
@@ -781,8 +791,8 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
     for (int c = 0; c < GV_BATCH; ++c) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        b[c][t][0] = *reinterpret_cast<const bf16x8*>(bp[t] + kc + c * 64);
-        b[c][t][1] = *reinterpret_cast<const bf16x8*>(bp[t] + kc + c * 64 + 8);
+        b[c][t][0] = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc + c * 64) * kstep);
+        b[c][t][1] = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc + c * 64) * kstep + 8);
       }
       a[c][0] = *reinterpret_cast<const bf16x8*>(ap + kc + c * 64);
       a[c][1] = *reinterpret_cast<const bf16x8*>(ap + kc + c * 64 + 8);
@@ -800,8 +810,8 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
     const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bp[t] + kc);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bp[t] + kc + 8);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc) * kstep);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc) * kstep + 8);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
     }
@@ -829,6 +839,27 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
         }
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Weight packing: W [E][rows][cols] row-major bf16 -> the K-step-tiled panels the expert GEMMs
+// read as B (b_tiled): panel e rows/256 + p holds rows [256 p, 256 p + 256) of expert e as
+// cols/32 contiguous blocks of 256 rows x 32 columns (64-byte rows). Thread i moves 16-byte
+// piece i of the packed array, so the stores are contiguous; the loads take 64 contiguous bytes
+// of each of 16 rows per wave. rows is a multiple of 256 and cols of 32.
+__global__ __launch_bounds__(256) void pack_weights_kernel(const u16* __restrict__ W, u16* __restrict__ Wp,
+                                                           int cols, size_t pieces) {
+  const int nkb = cols / 32;
+  for (size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x; i < pieces;
+       i += static_cast<size_t>(gridDim.x) * 256) {
+    const int q = static_cast<int>(i & 3);                 // 16-byte piece of a 64-byte row
+    const int r = static_cast<int>((i >> 2) & 255);        // row within the panel
+    const size_t blk = i >> 10;                            // panel * nkb + block
+    const size_t panel = blk / nkb;
+    const int kb = static_cast<int>(blk - panel * nkb);
+    const size_t src = (panel * 256 + r) * cols + kb * 32 + q * 8;   // panel*256 = e rows + 256 p
+    *reinterpret_cast<u32x4*>(Wp + i * 8) = *reinterpret_cast<const u32x4*>(W + src);
   }
 }
 
@@ -971,12 +1002,15 @@ static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, 
   }
   const int grid1 = round_grid(tile_grid(R, E, C, 256, N1, 256));
   const int grid2 = round_grid(tile_grid(R, E, C, 256, N2, 256) + (g2.splits > 1 ? 256 : 0));
-  // GEMM1's A (the token rows, gathered or a plain copy) and GEMM2's B (W2) are row-major:
-  // pair staging for them; GEMM2's A (H) is K-step-tiled
+  // GEMM1's A (the token rows, gathered or a plain copy) is row-major: pair staging for it.
+  // GEMM2's A (H) is K-step-tiled; its B (W2) is pair-staged when row-major, and packed weights
+  // are K-step-tiled like H
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<ACT, 32, 4, false, 1>), dim3(grid1), dim3(256), 0, stream, g1);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (ev_mid && (err = hipEventRecord(ev_mid, stream)) != hipSuccess) return err;
-  if (g2.a_tiled)
+  if (g2.a_tiled && g2.b_tiled)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
+  else if (g2.a_tiled)
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4, false, 2>), dim3(grid2), dim3(256), 0, stream, g2);
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid2), dim3(256), 0, stream, g2);
@@ -991,6 +1025,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
   GemmArgs g2{a.H, a.W2, a.b2, a.y_perm, a.kept, a.offsets, a.E, a.d, a.d_ffn, a.R, a.C, ffn_splits(a), a.side,
               nullptr, 0, 0};
   if (ffn_h_tiled(a.bf16, a.C)) g2.a_tiled = 1;   // GEMM1 runs the MFMA kernel: H is tiled
+  g1.b_tiled = g2.b_tiled = a.w_packed;          // bf16 only, d and d_ffn multiples of 256
   if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
     g1.A = a.x;
     g1.rows = a.rows;
@@ -1007,6 +1042,16 @@ hipError_t launch_shared_ffn(const SharedFfnArgs& a, hipStream_t stream) {
   if (ffn_h_tiled(a.bf16, a.T)) g2.a_tiled = 1;
   return a.act == kActSilu ? launch_ffn<kEpiSilu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr)
                            : launch_ffn<kEpiGelu>(g1, g2, a.bf16, a.T, a.T, 1, a.d_ffn, a.d, stream, nullptr);
+}
+
+hipError_t launch_pack_weights(const void* W, void* W_packed, int64_t E, int64_t rows, int64_t cols,
+                               hipStream_t stream) {
+  const size_t pieces = static_cast<size_t>(E) * rows * cols / 8;
+  const size_t blocks = (pieces + 255) / 256;
+  const int grid = static_cast<int>(blocks < 4096 ? blocks : 4096);
+  hipLaunchKernelGGL(pack_weights_kernel, dim3(grid), dim3(256), 0, stream, static_cast<const u16*>(W),
+                     static_cast<u16*>(W_packed), static_cast<int>(cols), pieces);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------------------

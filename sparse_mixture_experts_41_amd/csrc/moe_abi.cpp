@@ -34,6 +34,7 @@ struct Derived {
   int policy;       // MOE_DROP_*
   bool stats;       // routing statistics requested
   bool train;       // the workspace also holds what moe_backward needs, and its scratch
+  bool packed = false;   // W1 and W2 come packed by moe_pack_expert_weights
   uint32_t key0, key1;
 };
 
@@ -106,6 +107,7 @@ moe_status check_config(const moe_config* cfg, Derived* D) {
   D->policy = MOE_DROP_TOKEN_ORDER;
   D->stats = false;
   D->train = false;
+  D->packed = false;
   D->key0 = static_cast<uint32_t>(cfg->seed & 0xffffffffull);
   D->key1 = static_cast<uint32_t>(cfg->seed >> 32);
   return MOE_OK;
@@ -134,7 +136,14 @@ moe_status check_variant(const moe_variant* v, Derived* D) {
   D->dffs = static_cast<int>(v->shared_d_ffn);
   if (v->drop_policy != MOE_DROP_TOKEN_ORDER && v->drop_policy != MOE_DROP_RANDOM && v->drop_policy != MOE_DROP_REROUTE)
     return fail(MOE_EINVAL, "unknown drop_policy");
-  if (v->reserved != 0) return fail(MOE_EINVAL, "variant reserved must be 0");
+  if (v->weight_layout != MOE_WEIGHTS_LINEAR && v->weight_layout != MOE_WEIGHTS_PACKED)
+    return fail(MOE_EINVAL, "unknown weight_layout");
+  if (v->weight_layout == MOE_WEIGHTS_PACKED) {
+    if (!D->bf16) return fail(MOE_EUNSUPPORTED, "packed weights need the bf16 dtype");
+    if (D->d % 256 != 0 || D->dff % 256 != 0)
+      return fail(MOE_EUNSUPPORTED, "packed weights need d and d_ffn multiples of 256");
+    D->packed = true;
+  }
   if (v->route_stats != nullptr && (reinterpret_cast<uintptr_t>(v->route_stats) & 3u) != 0)
     return fail(MOE_EINVAL, "route_stats is not 4-byte aligned");
   D->policy = v->drop_policy;
@@ -430,6 +439,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   MOE_CHECK(check_variant(variant, &D));
   D.train = train;
   if (train && D.dffs > 0) return fail(MOE_EUNSUPPORTED, "the backward pass does not cover a shared expert");
+  if (train && D.packed) return fail(MOE_EUNSUPPORTED, "training takes the row-major weights");
   if (D.dffs > 0) {
     MOE_CHECK(need(variant->W1s, 16, "W1s"));
     MOE_CHECK(need(variant->b1s, D.esize, "b1s", true));
@@ -583,6 +593,7 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   fa.bf16 = D.bf16 ? 1 : 0;
   fa.side = at<float>(ws, Lw.side);
   fa.act = D.act;
+  fa.w_packed = D.packed ? 1 : 0;
   fa.pre = train ? at<void>(ws, Lw.pre) : nullptr;
   if (moe::ffn_gathers(fa))
     fa.rows = perm;   // GEMM1 reads the token rows of x through the permutation
@@ -648,6 +659,23 @@ moe_status moe_forward_ex(const moe_config* cfg, const moe_variant* variant, con
   return forward_impl(cfg, variant, x, Wg, bg, W1, b1, W2, b2, y, f, P, L, counts, kept, aux, ws, ws_bytes, stream);
 }
 
+moe_status moe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const void* W, void* W_packed,
+                                   moe_stream_t stream) {
+  if (E < 1 || rows < 1 || cols < 1) return fail(MOE_EINVAL, "E, rows and cols must be >= 1");
+  if (E > (int64_t{1} << 20) || rows > (int64_t{1} << 20) || cols > (int64_t{1} << 20) ||
+      E * rows > (int64_t{1} << 40) / cols)
+    return fail(MOE_EINVAL, "E*rows*cols must be below 2^40");
+  if (rows % 256 != 0) return fail(MOE_EUNSUPPORTED, "rows must be a multiple of 256");
+  if (cols % 32 != 0) return fail(MOE_EUNSUPPORTED, "cols must be a multiple of 32");
+  MOE_CHECK(need(W, 16, "W"));
+  MOE_CHECK(need(W_packed, 16, "W_packed"));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(W), b = reinterpret_cast<uintptr_t>(W_packed);
+  const uintptr_t n = static_cast<uintptr_t>(E * rows * cols * 2);
+  if (a < b + n && b < a + n) return fail(MOE_EINVAL, "W and W_packed overlap");
+  MOE_HIP(moe::launch_pack_weights(W, W_packed, E, rows, cols, reinterpret_cast<hipStream_t>(stream)), "pack");
+  return MOE_OK;
+}
+
 moe_status moe_workspace_size_ex(const moe_config* cfg, const moe_variant* variant, size_t* bytes) {
   Derived D;
   MOE_CHECK(check_config(cfg, &D));
@@ -662,6 +690,7 @@ moe_status moe_workspace_size_train(const moe_config* cfg, const moe_variant* va
   MOE_CHECK(check_config(cfg, &D));
   MOE_CHECK(check_variant(variant, &D));
   if (D.dffs > 0) return fail(MOE_EUNSUPPORTED, "the backward pass does not cover a shared expert");
+  if (D.packed) return fail(MOE_EUNSUPPORTED, "training takes the row-major weights");
   if (bytes == nullptr) return fail(MOE_EINVAL, "bytes is NULL");
   D.train = true;
   *bytes = layout_of(D).total;
@@ -685,6 +714,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
   MOE_CHECK(check_config(cfg, &D));
   MOE_CHECK(check_variant(variant, &D));
   if (D.dffs > 0) return fail(MOE_EUNSUPPORTED, "the backward pass does not cover a shared expert");
+  if (D.packed) return fail(MOE_EUNSUPPORTED, "training takes the row-major weights");
   if (!std::isfinite(lam)) return fail(MOE_EINVAL, "lam must be finite");
   D.train = true;
   MOE_CHECK(need(x, 16, "x"));

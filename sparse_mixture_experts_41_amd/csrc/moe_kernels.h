@@ -115,6 +115,8 @@ struct FfnArgs {
   int bf16;
   int act;                // kActGelu or kActSilu
   void* pre;              // [R,d_ffn] or null: GEMM1 also stores its pre-activation (training)
+  int w_packed;           // 1: W1 and W2 in the packed panels of launch_pack_weights (bf16, d and
+                          // d_ffn multiples of 256)
 };
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
 // copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
@@ -135,6 +137,11 @@ bool ffn_h_tiled(int bf16, int C);
 size_t ffn_h_rows(int R, int E, int C, int bf16);
 // GEMM1 (+bias, GeLU) then GEMM2 (+bias). `ev_mid` (nullable) is recorded between them.
 hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev_mid);
+// W [E][rows][cols] row-major bf16 -> W_packed, the same bytes as K-step-tiled panels: panel
+// e rows/256 + p is rows [256 p, 256 p + 256) of expert e as cols/32 contiguous blocks of 256
+// rows x 32 columns (64-byte rows). rows a multiple of 256, cols of 32.
+hipError_t launch_pack_weights(const void* W, void* W_packed, int64_t E, int64_t rows, int64_t cols,
+                               hipStream_t stream);
 // The shared expert: one dense FFN over the T token rows of x (no routing):
 // H = act(x W1ᵀ + b1) [T, d_ffn], y = H W2ᵀ + b2 [T, d] float.
 struct SharedFfnArgs {

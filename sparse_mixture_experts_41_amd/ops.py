@@ -207,17 +207,19 @@ ROUTE_STAT_NAMES = ("loss_sq", "loss_quant", "loss_var", "usage_std", "entropy")
 
 
 def make_variant(cfg: MoeConfig, activation: str = "gelu", noise_std: float = 0.0, shared=None,
-                 drop_policy: str = "token", route_stats=None):
+                 drop_policy: str = "token", route_stats=None, packed_weights: bool = False):
     """A moe_variant: expert activation ("gelu" or "silu"), Gaussian router noise std, an
     optional shared expert ``shared = (W1s [ds,d], b1s [ds] or None, W2s [d,ds], b2s [d] or
-    None)``, the capacity policy ("token", "random", "reroute") and an optional float32 device
-    tensor of MOE_ROUTE_STATS elements for the routing statistics (ROUTE_STAT_NAMES order).
+    None)``, the capacity policy ("token", "random", "reroute"), an optional float32 device
+    tensor of MOE_ROUTE_STATS elements for the routing statistics (ROUTE_STAT_NAMES order), and
+    whether W1 and W2 come from pack_expert_weights (MOE_WEIGHTS_PACKED).
     Returns (variant, tensors kept alive for it)."""
     sd = _storage_dtype(cfg)
     v = _lib.MoeVariant()
     v.activation = {"gelu": _lib.MOE_ACT_GELU, "silu": _lib.MOE_ACT_SILU}[activation]
     v.noise_std = float(noise_std)
     v.drop_policy = DROP_POLICIES[drop_policy]
+    v.weight_layout = _lib.MOE_WEIGHTS_PACKED if packed_weights else _lib.MOE_WEIGHTS_LINEAR
     keep = {}
     if shared is not None:
         W1s, b1s, W2s, b2s = shared
@@ -234,6 +236,19 @@ def make_variant(cfg: MoeConfig, activation: str = "gelu", noise_std: float = 0.
         v.route_stats = _ptr(route_stats)
         keep["route_stats"] = route_stats
     return v, keep
+
+
+def pack_expert_weights(W, stream=None):
+    """moe_pack_expert_weights: a new tensor of W's shape [E, rows, cols] (bf16, on W's device)
+    holding W's values in the packed panel order that moe_forward_ex reads when the variant says
+    packed_weights. Its element order is not W's: it is meant only for that call."""
+    if W.dtype != torch.bfloat16 or W.dim() != 3 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous [E, rows, cols] bfloat16 tensor")
+    out = torch.empty_like(W)
+    E, rows, cols = W.shape
+    _lib.check(_lib.load().moe_pack_expert_weights(int(E), int(rows), int(cols), _ptr(W), _ptr(out),
+                                                    _stream(stream)))
+    return out
 
 
 def workspace_size_ex(cfg: MoeConfig, variant) -> int:

@@ -55,11 +55,13 @@ def to_device(arr, dtype, device="cuda"):
 class Problem:
     """Seeded inputs of one shape, on the host (exact values) and on the GPU (storage dtype).
 
-    Forward variants: ``activation`` ("gelu"/"silu"), Gaussian router ``noise_std``, and a
-    shared expert of hidden width ``shared_d_ffn`` (seeded weights; 0 = none)."""
+    Forward variants: ``activation`` ("gelu"/"silu"), Gaussian router ``noise_std``, a shared
+    expert of hidden width ``shared_d_ffn`` (seeded weights; 0 = none), and ``packed_weights``
+    (W1 and W2 handed over packed by moe_pack_expert_weights)."""
 
     def __init__(self, shape: MoEShape, bias_std: float = 0.0, arrays: dict | None = None, activation: str = "gelu",
-                 noise_std: float = 0.0, shared_d_ffn: int = 0, drop_policy: str = "token", route_stats: bool = False):
+                 noise_std: float = 0.0, shared_d_ffn: int = 0, drop_policy: str = "token", route_stats: bool = False,
+                 packed_weights: bool = False):
         self.shape = shape
         self.cfg = config_of(shape)
         self.arrays = arrays if arrays is not None else make_inputs(shape, bias_std)
@@ -68,6 +70,10 @@ class Problem:
         self.dev = {n: to_device(a, dt) for n, a in self.arrays.items()}
         self.activation, self.noise_std, self.shared_d_ffn = activation, float(noise_std), int(shared_d_ffn)
         self.drop_policy, self.route_stats = drop_policy, bool(route_stats)
+        self.packed_weights = bool(packed_weights)
+        if self.packed_weights:
+            self.dev["W1p"] = ops.pack_expert_weights(self.dev["W1"])
+            self.dev["W2p"] = ops.pack_expert_weights(self.dev["W2"])
         self.shared_host = self.shared_dev = None
         if self.shared_d_ffn:
             sh = make_shared_expert(shape, self.shared_d_ffn, bias_std)
@@ -77,13 +83,14 @@ class Problem:
     @property
     def has_variant(self) -> bool:
         return (self.activation != "gelu" or self.noise_std > 0.0 or self.shared_d_ffn > 0
-                or self.drop_policy != "token" or self.route_stats)
+                or self.drop_policy != "token" or self.route_stats or self.packed_weights)
 
     def variant(self):
         if not self.has_variant:
             return None
         stats = torch.full((len(ops.ROUTE_STAT_NAMES),), float("nan"), device="cuda") if self.route_stats else None
-        return ops.make_variant(self.cfg, self.activation, self.noise_std, self.shared_dev, self.drop_policy, stats)
+        return ops.make_variant(self.cfg, self.activation, self.noise_std, self.shared_dev, self.drop_policy, stats,
+                                packed_weights=self.packed_weights)
 
     def oracle_kw(self) -> dict:
         """The variant's keyword arguments of oracle.forward / forward_rows."""
@@ -91,6 +98,8 @@ class Problem:
 
     def args(self):
         d = self.dev
+        if self.packed_weights:
+            return (d["x"], d["Wg"], d["bg"], d["W1p"], d["b1"], d["W2p"], d["b2"])
         return (d["x"], d["Wg"], d["bg"], d["W1"], d["b1"], d["W2"], d["b2"])
 
     def host_args(self):

@@ -144,7 +144,7 @@ def test_variant_struct_layout(lib):
     assert ctypes.sizeof(MoeVariant) == 64
     assert MoeVariant.noise_std.offset == 4 and MoeVariant.shared_d_ffn.offset == 8 and MoeVariant.W1s.offset == 16
     assert MoeVariant.b2s.offset == 40
-    assert MoeVariant.drop_policy.offset == 48 and MoeVariant.reserved.offset == 52
+    assert MoeVariant.drop_policy.offset == 48 and MoeVariant.weight_layout.offset == 52
     assert MoeVariant.route_stats.offset == 56
 
 
@@ -186,7 +186,7 @@ def test_variant_policy_and_stats_validation(lib):
     n0 = _ws_ex(lib, cfg, None)[1].value
     assert _ws_ex(lib, cfg, MoeVariant(drop_policy=3))[0] == MOE_EINVAL
     assert _ws_ex(lib, cfg, MoeVariant(drop_policy=-1))[0] == MOE_EINVAL
-    assert _ws_ex(lib, cfg, MoeVariant(reserved=1))[0] == MOE_EINVAL
+    assert _ws_ex(lib, cfg, MoeVariant(weight_layout=2))[0] == MOE_EINVAL
     assert _ws_ex(lib, cfg, MoeVariant(route_stats=MIS + 2))[0] == MOE_EINVAL
     assert b"route_stats" in lib.moe_last_error()
     ng, TE = (cfg.T + 15) // 16, cfg.T * cfg.k
@@ -194,6 +194,32 @@ def test_variant_policy_and_stats_validation(lib):
     assert st == MOE_OK and rnd.value >= n0 + 2 * ng * cfg.E * 4 + cfg.E * 8
     st, rr = _ws_ex(lib, cfg, MoeVariant(drop_policy=MOE_DROP_REROUTE, route_stats=A16))
     assert st == MOE_OK and rr.value >= n0 + 2 * TE * 4 + 2 * ng * cfg.E * 4 + cfg.E * 4 + ng * 4
+
+
+def test_packed_weight_layout_validation(lib):
+    """Packed weights: bf16 only, d and d_ffn multiples of 256, forward only; the pack entry point
+    checks its sizes and pointers before it launches anything."""
+    from sparse_mixture_experts_41_amd._lib import MOE_WEIGHTS_PACKED, MoeVariant
+    packed = MoeVariant(weight_layout=MOE_WEIGHTS_PACKED)
+    for name in ("mixtral_like", "switch_skew", "decode", "gumbel_longtail"):
+        c = CONFIGS[name]
+        want = MOE_OK if (c.d % 256 == 0 and c.d_ffn % 256 == 0) else MOE_EUNSUPPORTED
+        assert _ws_ex(lib, _cfg(name), packed)[0] == want, name
+    assert _ws_ex(lib, _cfg("tiny_fp32"), packed)[0] == MOE_EUNSUPPORTED          # float32
+    assert b"bf16" in lib.moe_last_error()
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size_train(ctypes.byref(_cfg("mixtral_like")), ctypes.byref(packed),
+                                        ctypes.byref(n)) == MOE_EUNSUPPORTED
+    assert b"row-major" in lib.moe_last_error()
+    pack = lib.moe_pack_expert_weights
+    assert pack(8, 14336, 4096, None, A16, None) == MOE_EINVAL
+    assert pack(8, 14336, 4096, A16, MIS + 2, None) == MOE_EINVAL                  # misaligned
+    assert pack(0, 256, 32, A16, A16 + (1 << 30), None) == MOE_EINVAL
+    assert pack(8, 100, 4096, A16, A16 + (1 << 30), None) == MOE_EUNSUPPORTED      # rows % 256
+    assert pack(8, 256, 40, A16, A16 + (1 << 30), None) == MOE_EUNSUPPORTED        # cols % 32
+    assert pack(1 << 21, 256, 32, A16, A16 + (1 << 40), None) == MOE_EINVAL        # too large
+    assert pack(2, 256, 32, A16, A16 + 256 * 32 * 2, None) == MOE_EINVAL           # overlap
+    assert b"overlap" in lib.moe_last_error()
 
 
 def test_temperature_schedule_matches_the_oracle(lib):
