@@ -14,11 +14,11 @@ device synchronisations. Prints one JSON line:
   cpu_baseline  the CPU oracle (numpy float64) on a bounded sample of the same workload;
   cold_cache    the median event-measured forward when each call follows a 1 GiB write that
                 evicts L2 and the MALL (value and stage_ms are warm, back-to-back steps);
-  weights       --weights packed (the default where the shape allows it: bf16, d and d_ffn
-                multiples of 256) hands W1 and W2 over in the panel layout of
-                moe_pack_expert_weights, packed once before the warm-up as a server does when
-                it loads the weights (pack_ms). row_major repeats the timing with nn.Linear's
-                layout; both give bit-identical outputs.
+  weights       where the shape allows it (bf16, d and d_ffn multiples of 256) the timed
+                forward takes W1 and W2 in the panel layout of moe_pack_expert_weights, packed
+                once before the warm-up as a server does when it loads the weights (pack_ms).
+                With --weights both (the default) row_major holds the same timing with
+                nn.Linear's layout, run first; both layouts give bit-identical outputs.
 """
 from __future__ import annotations
 
@@ -62,8 +62,9 @@ def _args():
     ap.add_argument("--train", action="store_true",
                     help="time the training step instead: moe_forward_train + moe_backward (one JSON line)")
     ap.add_argument("--lam", type=float, default=0.01, help="weight of the balance loss in the training step")
-    ap.add_argument("--weights", choices=("packed", "row-major"), default="packed",
-                    help="expert weight layout of the forward (packed where the shape allows it)")
+    ap.add_argument("--weights", choices=("both", "packed", "row-major"), default="both",
+                    help="expert weight layout of the timed forward (packed where the shape allows it); "
+                         "both: also time the row-major layout first")
     ap.add_argument("--cold-reps", type=int, default=10,
                     help="after the timed steps, this many forwards each preceded by a 1 GiB write that "
                          "evicts L2 and the 256 MB MALL, timed with HIP events (0: skip)")
@@ -86,13 +87,14 @@ def gemm_source_digest() -> str:
     return h.hexdigest()
 
 
-def stored_traffic(path: str, kernel: str):
-    """Measured HBM bytes per launch of `kernel`, or None if absent or taken on other code."""
+def stored_traffic(path: str, kernel: str, weights: str):
+    """Measured HBM bytes per launch of `kernel`, or None if absent or taken on other code or on
+    the other weight layout."""
     if not path or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("gemm_source_sha256") != gemm_source_digest():
+    if rec.get("gemm_source_sha256") != gemm_source_digest() or rec.get("weights", "row-major") != weights:
         return None
     return rec.get("bytes_per_launch", {}).get(kernel)
 
@@ -278,15 +280,16 @@ def main() -> int:
             ev.close()
         return (t1 - t0) * 1e3 / args.steps, stage, events
 
-    packed = (args.weights == "packed" and shape.dtype == "bf16" and shape.d % 256 == 0
+    packed = (args.weights != "row-major" and shape.dtype == "bf16" and shape.d % 256 == 0
               and shape.d_ffn % 256 == 0)
     row_major = None
     pack_ms = None
     if packed:
-        rm_ms, rm_stage, _ = timed(ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant))
-        row_major = {"ms_per_step": rm_ms, "tokens_per_s": shape.T / (rm_ms * 1e-3),
-                     "expert_gemm1_gelu_ms": rm_stage["expert_gemm1_gelu"],
-                     "expert_gemm2_ms": rm_stage["expert_gemm2"]}
+        if args.weights == "both":
+            rm_ms, rm_stage, _ = timed(ops.ForwardPlan(cfg, *tensors, keep_routing=False, variant=variant))
+            row_major = {"ms_per_step": rm_ms, "tokens_per_s": shape.T / (rm_ms * 1e-3),
+                         "expert_gemm1_gelu_ms": rm_stage["expert_gemm1_gelu"],
+                         "expert_gemm2_ms": rm_stage["expert_gemm2"]}
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         W1p, W2p = ops.pack_expert_weights(tensors[3]), ops.pack_expert_weights(tensors[5])
@@ -329,7 +332,8 @@ def main() -> int:
     dom_name, dom_ms = ("expert_gemm1_gelu", g1) if g1 >= g2 else ("expert_gemm2", g2)
     achieved = stage_flops[dom_name] / (dom_ms * 1e-3) / 1e12
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{shape.name}.json")
-    traffic = None if (with_variant or args.capacity_factor is not None) else stored_traffic(traffic_path, dom_name)
+    traffic = (None if (with_variant or args.capacity_factor is not None)
+               else stored_traffic(traffic_path, dom_name, "packed" if packed else "row-major"))
     ng = (T + 15) // 16
     router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + ng * E * 8
     # GEMM1 reads the token rows through the permutation (no gathered copy) on the bf16 MFMA
