@@ -152,7 +152,7 @@ constexpr size_t kTailTile = 256 * 256;            // floats per side-buffer til
 // takes bundles of kBundle consecutive tiles (tiles that share an expert's operand panels, so
 // they meet in that XCD's L2), and bundles go round-robin over the 8 XCDs (so experts of very
 // different sizes still spread evenly over the chip). Covers [0, 8*kBundle*ceil(n/(8*kBundle))).
-constexpr int kBundle = 8;
+constexpr int kBundle = 16;
 __device__ __forceinline__ int xcd_tile_id(int bid) {
   const int x = bid & 7, j = bid >> 3;
   return ((j / kBundle) * 8 + x) * kBundle + j % kBundle;
