@@ -128,6 +128,52 @@ __device__ __forceinline__ int count_tiles(const GemmArgs& g, int BM, int tiles_
   return n;
 }
 
+// The same tile order for the bf16 kernel without a dependent scalar load per expert: lane l of
+// every wave loads expert l's segment (E <= 64), and prefix sums over the wave give each
+// expert's first tile and first row tile. A tile's expert is then the first lane whose
+// inclusive tile count exceeds it.
+struct TileScan {
+  int rows;       // segment rows of expert `lane` (0 past E)
+  int tm;         // its row tiles
+  int cnt_incl;   // tiles of experts 0..lane
+  int tm_incl;    // row tiles of experts 0..lane
+  int total;      // all tiles (uniform)
+};
+
+__device__ __forceinline__ int wave_scan_incl(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ TileScan scan_tiles(const GemmArgs& g, int BM, int tiles_n) {
+  const int lane = threadIdx.x & 63;
+  TileScan s;
+  s.rows = lane < g.E ? segment_rows(g, lane) : 0;
+  s.tm = (s.rows + BM - 1) / BM;
+  s.cnt_incl = wave_scan_incl(s.tm * tiles_n);
+  s.tm_incl = wave_scan_incl(s.tm);
+  s.total = __builtin_amdgcn_readlane(s.cnt_incl, 63);
+  return s;
+}
+
+// Tile t < total -> (e, mt, nt, mbase) as decode_tile gives them, and e's segment rows.
+__device__ __forceinline__ void locate_tile(const TileScan& s, int tile, int tiles_n, int& e, int& mt, int& nt,
+                                            int& mbase, int& m_e) {
+  const unsigned long long past = __ballot(s.cnt_incl > tile);
+  e = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(past)));
+  const int tm = __builtin_amdgcn_readlane(s.tm, e);
+  const int t = tile - (__builtin_amdgcn_readlane(s.cnt_incl, e) - tm * tiles_n);
+  nt = t / tm;
+  mt = t - nt * tm;
+  mbase = __builtin_amdgcn_readlane(s.tm_incl, e) - tm;
+  m_e = __builtin_amdgcn_readlane(s.rows, e);
+}
+
 // Tail split: the tiles of the whole rounds of 256 run unsplit; the L tiles of the last, partial
 // round are split along K into P parts (as many as fill the round, at most `max_parts`, each
 // at least 4 K steps), so the launch ends after about full/256 + 1/P rounds instead of a whole
@@ -293,7 +339,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   const int tiles_n = (g.N + BN - 1) / BN;
-  const int n_tiles = count_tiles(g, BM, tiles_n);
+  const TileScan scan = scan_tiles(g, BM, tiles_n);
+  const int n_tiles = scan.total;
   const TailPlan plan = tail_plan(n_tiles, g.K / BK, EPI == kEpiLinear && !g.wgrad ? g.splits : 1);
   const int n_units = plan.full + plan.L * plan.P;
   const int unit = xcd_tile_id(blockIdx.x);
@@ -309,13 +356,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   tile = __builtin_amdgcn_readfirstlane(tile);
   kpart = __builtin_amdgcn_readfirstlane(kpart);
   parts = __builtin_amdgcn_readfirstlane(parts);
-  int e, mt, nt, mbase;
-  decode_tile(tile, g, BM, tiles_n, e, mt, nt, mbase);
-  e = __builtin_amdgcn_readfirstlane(e);
+  int e, mt, nt, mbase, m_e;
+  locate_tile(scan, tile, tiles_n, e, mt, nt, mbase, m_e);
   const int panel = __builtin_amdgcn_readfirstlane(mbase + mt);   // K-step-tiled layouts
   mt = __builtin_amdgcn_readfirstlane(mt);
   nt = __builtin_amdgcn_readfirstlane(nt);
-  const int m_e = __builtin_amdgcn_readfirstlane(segment_rows(g, e));
   const int row0 = __builtin_amdgcn_readfirstlane((g.dense || g.wgrad) ? 0 : g.offsets[e]);
   const int m0 = mt * BM, n0 = nt * BN;
   const int N = g.N;
