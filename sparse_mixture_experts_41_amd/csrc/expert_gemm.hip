@@ -121,13 +121,6 @@ __device__ __forceinline__ float load_bias(const void* bias, size_t i, bool bf16
   return bf16 ? bf16_to_f32(static_cast<const u16*>(bias)[i]) : static_cast<const float*>(bias)[i];
 }
 
-// Number of (expert, row tile, column tile) tiles.
-__device__ __forceinline__ int count_tiles(const GemmArgs& g, int BM, int tiles_n) {
-  int n = 0;
-  for (int e = 0; e < g.E; ++e) n += (segment_rows(g, e) + BM - 1) / BM * tiles_n;
-  return n;
-}
-
 // The same tile order for the bf16 kernel without a dependent scalar load per expert: lane l of
 // every wave loads expert l's segment (E <= 64), and prefix sums over the wave give each
 // expert's first tile and first row tile. A tile's expert is then the first lane whose
@@ -965,15 +958,15 @@ constexpr int kFixupGrid = 1024;
 __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, BK = 32, SLABS = BM / kFixupRows, RPP = 256 / (BN / 4);
   const int tiles_n = (g.N + BN - 1) / BN;
-  const TailPlan plan = tail_plan(count_tiles(g, BM, tiles_n), g.K / BK, g.splits);
+  const TileScan scan = scan_tiles(g, BM, tiles_n);
+  const TailPlan plan = tail_plan(scan.total, g.K / BK, g.splits);
   const int N = g.N;
   float* out = static_cast<float*>(g.out);
   const int c = (threadIdx.x % (BN / 4)) * 4;
   for (int u = blockIdx.x; u < plan.L * SLABS; u += gridDim.x) {
     const int s = u / SLABS, slab = u % SLABS;
-    int e, mt, nt, mbase;
-    decode_tile(plan.full + s, g, BM, tiles_n, e, mt, nt, mbase);
-    const int m_e = segment_rows(g, e);
+    int e, mt, nt, mbase, m_e;
+    locate_tile(scan, plan.full + s, tiles_n, e, mt, nt, mbase, m_e);
     const int row0 = g.dense ? 0 : g.offsets[e];
     const int m0 = mt * BM, n0 = nt * BN;
     const float* side = static_cast<const float*>(g.out2) + static_cast<size_t>(s) * (plan.P - 1) * kTailTile;
