@@ -131,6 +131,8 @@ struct TileScan {
   int cnt_incl;   // tiles of experts 0..lane
   int tm_incl;    // row tiles of experts 0..lane
   int total;      // all tiles (uniform)
+  int kept;       // kept[lane] (0 past E or for one dense group)
+  int off;        // offsets[lane], or koff[lane] in the weight-gradient mode (0 past E or dense)
 };
 
 __device__ __forceinline__ int wave_scan_incl(int v) {
@@ -146,6 +148,9 @@ __device__ __forceinline__ int wave_scan_incl(int v) {
 __device__ __forceinline__ TileScan scan_tiles(const GemmArgs& g, int BM, int tiles_n) {
   const int lane = threadIdx.x & 63;
   TileScan s;
+  const bool per_expert = lane < g.E && !g.dense;
+  s.kept = per_expert ? g.kept[lane] : 0;
+  s.off = per_expert ? (g.wgrad ? g.koff[lane] : g.offsets[lane]) : 0;
   s.rows = lane < g.E ? segment_rows(g, lane) : 0;
   s.tm = (s.rows + BM - 1) / BM;
   s.cnt_incl = wave_scan_incl(s.tm * tiles_n);
@@ -354,12 +359,12 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int panel = __builtin_amdgcn_readfirstlane(mbase + mt);   // K-step-tiled layouts
   mt = __builtin_amdgcn_readfirstlane(mt);
   nt = __builtin_amdgcn_readfirstlane(nt);
-  const int row0 = __builtin_amdgcn_readfirstlane((g.dense || g.wgrad) ? 0 : g.offsets[e]);
+  const int row0 = (g.dense || g.wgrad) ? 0 : __builtin_amdgcn_readlane(scan.off, e);
   const int m0 = mt * BM, n0 = nt * BN;
   const int N = g.N;
   const int lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
-  const int K = g.wgrad ? (g.kept[e] + kWgradK - 1) / kWgradK * kWgradK : g.K;
-  const size_t kofs = g.wgrad ? static_cast<size_t>(g.koff[e]) : 0;
+  const int K = g.wgrad ? (__builtin_amdgcn_readlane(scan.kept, e) + kWgradK - 1) / kWgradK * kWgradK : g.K;
+  const size_t kofs = g.wgrad ? static_cast<size_t>(__builtin_amdgcn_readlane(scan.off, e)) : 0;
   const int k_first = __builtin_amdgcn_readfirstlane((K / BK) * kpart / parts);
   const int k_last = __builtin_amdgcn_readfirstlane((K / BK) * (kpart + 1) / parts);
   const int nk = k_last - k_first;           // K steps of this part
@@ -967,7 +972,7 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs g) {
     const int s = u / SLABS, slab = u % SLABS;
     int e, mt, nt, mbase, m_e;
     locate_tile(scan, plan.full + s, tiles_n, e, mt, nt, mbase, m_e);
-    const int row0 = g.dense ? 0 : g.offsets[e];
+    const int row0 = g.dense ? 0 : __builtin_amdgcn_readlane(scan.off, e);
     const int m0 = mt * BM, n0 = nt * BN;
     const float* side = static_cast<const float*>(g.out2) + static_cast<size_t>(s) * (plan.P - 1) * kTailTile;
 #pragma unroll
