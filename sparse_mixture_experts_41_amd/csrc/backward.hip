@@ -197,15 +197,26 @@ __global__ __launch_bounds__(256) void rows_to_cols_kernel(RowsToColsArgs a) {
   __shared__ __attribute__((aligned(16))) T tile[32 * P];
   __shared__ int s_e, s_mbase;
   const int pos0 = blockIdx.y * 32, c0 = blockIdx.x * TC;
-  if (threadIdx.x == 0) {
-    int found = -1, mbase = 0, mb = 0;
-    for (int e = 0; e < a.E; ++e) {
-      const int kp = (a.kept[e] + kWgradK - 1) / kWgradK * kWgradK;
-      if (kp > 0 && pos0 >= a.koff[e] && pos0 < a.koff[e] + kp) found = e, mbase = mb;
-      mb += (a.kept[e] + 255) / 256;
+  if (threadIdx.x < 64) {   // wave 0, lane l = expert l (E <= 64): the expert whose K range holds pos0
+    const int l = threadIdx.x;
+    const int kept = l < a.E ? a.kept[l] : 0;
+    const int kp = (kept + kWgradK - 1) / kWgradK * kWgradK;
+    const int ko = l < a.E ? a.koff[l] : 0;
+    const int own = (kept + 255) / 256;      // row tiles of expert l
+    int mb = own;                            // ... of experts 0..l
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(mb, o, 64);
+      if (l >= o) mb += t;
     }
-    s_e = found;
-    s_mbase = mbase;
+    // the K ranges are disjoint: at most one lane matches
+    const unsigned long long hit = __ballot(l < a.E && kp > 0 && pos0 >= ko && pos0 < ko + kp);
+    const int found = hit ? static_cast<int>(__builtin_ctzll(hit)) : -1;
+    const int base = __shfl(mb - own, found < 0 ? 0 : found, 64);
+    if (l == 0) {
+      s_e = found;
+      s_mbase = found < 0 ? 0 : base;
+    }
   }
   __syncthreads();
   const int e = s_e;
