@@ -473,7 +473,11 @@ __global__ __launch_bounds__(256) void dx_kernel(DxArgs a) {
         acc[tt].y = fmaf(z, wg[e].y, acc[tt].y);
       }
   }
-  for (int tt = 0; tt < nt; ++tt) {
+  // unrolled with a guard: a loop bounded by nt would index acc at run time and move it to
+  // scratch memory
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    if (tt >= nt) continue;
     const size_t o = static_cast<size_t>(t0 + tt) * d + n0;
     if constexpr (BF16) {
       *reinterpret_cast<uint32_t*>(static_cast<u16*>(a.dx) + o) =
@@ -555,6 +559,12 @@ static int dwg_block_cols(int E) {
 int dwg_slices(int T, int d, int E) {
   const int cols = (d + dwg_block_cols(E) - 1) / dwg_block_cols(E);
   int s = (2048 + cols - 1) / cols;          // aim at >= 2048 workgroups (8 per CU)
+  // each slice writes (and the reduction reads) an E x d float32 partial while reading
+  // (T/S) x d of x: with many experts, keep that traffic near x's own (S <= T / (2E)), as long
+  // as about 256 workgroups remain
+  const int by_traffic = T / (2 * E), by_width = (256 + cols - 1) / cols;
+  const int cap = by_traffic > by_width ? by_traffic : by_width;
+  s = s < cap ? s : cap;
   const int max_s = (T + 15) / 16;           // at least 16 tokens per slice
   s = s < max_s ? s : max_s;
   return s < 1 ? 1 : (s > 512 ? 512 : s);
