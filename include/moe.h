@@ -192,7 +192,7 @@ typedef enum {
 
 typedef struct moe_variant {
   int32_t activation;      /* moe_activation of every expert (routed and shared): GeLU, or
-                              SiLU(v) = v sigmoid(v) (aberweb.com page, section 3.2)         */
+                              SiLU(v) = v sigmoid(v) (lpnh.cn page, section 3.2)            */
   float noise_std;         /* 0: no Gaussian noise. > 0 (needs gumbel = 0): s = (z + g)/tau,
                               g = noise_std * n with n standard normal per (token, expert)
                               (kwkr.cn page, section 3.3): from the Philox block of the Gumbel
@@ -200,7 +200,7 @@ typedef struct moe_variant {
                               word 1 + 1/2) 2^-32, n = sqrt(-2 ln u1) cos(2 pi u2) in float64,
                               and g = noise_std * n rounded once to float32                 */
   int64_t shared_d_ffn;    /* 0: none. Else the hidden width of one shared expert that every
-                              token uses (aberweb.com page, section 2.3):
+                              token uses (lpnh.cn page, section 2.3):
                               y[t] = FFN_s(x[t]) + sum_j w[t,j] FFN_e(x[t]); the float32 sum
                               starts from FFN_s and adds the slots in j order. bf16 needs a
                               multiple of 64.                                                 */
@@ -213,7 +213,7 @@ typedef struct moe_variant {
   float* route_stats;      /* nullable; else [MOE_ROUTE_STATS] f32 on the device, written by the
                               layer from the counts before capacity (u_e = counts_e / T) and
                               the full softmax p, each in float64 rounded once to float32
-                              (aberweb.com page, sections 2.4 and 3.6; mhpn.cn page, 3.1):
+                              (lpnh.cn page, sections 2.4 and 3.6; mhpn.cn page, 3.1):
                               [0] sum_e u_e^2; [1] 0.5 Q50 + 0.3 Q90 + 0.2 Q99 of u, Qq by
                               linear interpolation at position (E-1) q of the sorted u;
                               [2] sum_e (counts_e - mean counts)^2; [3] population standard
@@ -299,8 +299,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_variant* variant, const
                         float* db2, const moe_backward_aux* aux, void* ws, size_t ws_bytes,
                         moe_stream_t stream);
 
-/* Temperature schedule tau_t = max(tau_min, tau0 - rate * step) (aberweb.com page, section
- * 3.2: tau0 = 1, tau_min = 0.5, rate = 1e-4; mhpn.cn page: rate 1e-3), computed in double and
+/* Temperature schedule tau_t = max(tau_min, tau0 - rate * step) (lpnh.cn page, section 3.3:
+ * tau0 = 1, tau_min = 0.5, rate = 1e-4; aberweb.com page, section 3.3: rate 1e-3), computed in double and
  * rounded once to float; the result goes to moe_config.temperature. Host only. */
 float moe_temperature_at(int64_t step, float tau0, float tau_min, float rate);
 

@@ -14,16 +14,18 @@ Sources (pages cited by title or address and section):
   [D]  "MoE模型：动态计算架构解析与实践指南" (intelliparadigm.com), sections 2.1 (expert =
        Linear -> GeLU -> Linear), 2.3 (balance loss = E * sum(one-hot mean * softmax mean)),
        3.1 (dense loop: every expert on every token, masked by routing).
-  [L]  "Mixture of Experts (MoE) 原理与工程落地全指南" (lpnh.cn), section 2.2 (Gumbel noise
-       added to the logits, divided by a temperature, then softmax).
-  [A]  "为什么92%的AI团队误用MoE？…" (aberweb.com), sections 2.3 (a shared expert that every
-       token uses, plus the routed experts), 3.2 (experts Linear -> SiLU -> Linear; the
-       temperature schedule tau = max(0.5, 1.0 - 0.0001 * step)).
-  [M]  "MoE架构揭秘：参数规模≠计算量…" (mhpn.cn): the same schedule with rate 0.001; section
-       3.1's load-variance loss.
-Forward variants (the plain layer is the default of each): SiLU experts ([A] 3.2); Gaussian
+  [L]  "Mixture of Experts (MoE) 原理与工程落地全指南" (lpnh.cn), sections 2.2 (Gumbel noise
+       added to the logits, divided by a temperature, then softmax), 2.3 (a shared expert that
+       every token uses, plus the routed experts), 2.4 (the squared-usage balance loss and its
+       quantile-weighted form), 3.2 (experts Linear -> SiLU -> Linear), 3.3 (the temperature
+       schedule tau = max(0.5, 1.0 - 0.0001 * step)), 3.6 (load standard deviation and routing
+       entropy as monitored quantities).
+  [A]  "为什么92%的AI团队误用MoE？…" (aberweb.com), section 3.3: the same schedule with rate
+       0.001.
+  [M]  "MoE架构揭秘：参数规模≠计算量…" (mhpn.cn): section 3.1's load-variance loss.
+Forward variants (the plain layer is the default of each): SiLU experts ([L] 3.2); Gaussian
 router noise noise_std * N(0, 1) added to the logits ([G] 3.3; generator in philox.py); a
-shared expert whose output is added to every token's routed sum ([A] 2.3).
+shared expert whose output is added to every token's routed sum ([L] 2.3).
 
 Readings taken where the pages leave a step open:
   * top-k selects on the float32 scores s (logits, plus Gumbel noise, over tau); ties go to
@@ -176,7 +178,7 @@ def gelu(v: np.ndarray) -> np.ndarray:
 
 
 def silu(v: np.ndarray) -> np.ndarray:
-    """SiLU(v) = v * sigmoid(v) ([A] 3.2's nn.SiLU); the sigmoid is scipy's expit."""
+    """SiLU(v) = v * sigmoid(v) ([L] 3.2's nn.SiLU); the sigmoid is scipy's expit."""
     return v * expit(v)
 
 
@@ -327,13 +329,13 @@ def reweight(p: np.ndarray, final_idx: np.ndarray) -> np.ndarray:
 def routing_stats(counts: np.ndarray, p: np.ndarray) -> dict:
     """Load statistics of one batch, none with an outer coefficient (lambda):
 
-      usage_e    = counts_e / T (slots routed to e before capacity, over the tokens; [A] 2.4)
-      loss_sq    = sum_e usage_e^2                                   ([A] 2.4, standard form)
-      loss_quant = 0.5 Q50(usage) + 0.3 Q90(usage) + 0.2 Q99(usage)  ([A] 2.4, improved form);
+      usage_e    = counts_e / T (slots routed to e before capacity, over the tokens; [L] 2.4)
+      loss_sq    = sum_e usage_e^2                                   ([L] 2.4, standard form)
+      loss_quant = 0.5 Q50(usage) + 0.3 Q90(usage) + 0.2 Q99(usage)  ([L] 2.4, improved form);
                    Qq over the E experts, linear interpolation between order statistics
       loss_var   = sum_e (counts_e - mean_e counts)^2                ([M] 3.1)
-      usage_std  = population standard deviation of usage            ([A] 3.6)
-      entropy    = mean over tokens of -sum_e p ln p, 0 ln 0 = 0     ([A] 3.6)"""
+      usage_std  = population standard deviation of usage            ([L] 3.6)
+      entropy    = mean over tokens of -sum_e p ln p, 0 ln 0 = 0     ([L] 3.6)"""
     counts = np.asarray(counts, np.float64)
     p = np.asarray(p, np.float64)
     T = p.shape[0]
@@ -360,7 +362,7 @@ def routing_stats(counts: np.ndarray, p: np.ndarray) -> dict:
 
 # ---------------------------------------------------------------- whole layer
 def shared_expert(x, shared, act: str = "gelu"):
-    """The shared expert ([A] 2.3) on every token; ``shared`` = (W1s, b1s, W2s, b2s) or None."""
+    """The shared expert ([L] 2.3) on every token; ``shared`` = (W1s, b1s, W2s, b2s) or None."""
     if shared is None:
         return None
     W1s, b1s, W2s, b2s = shared
@@ -479,7 +481,7 @@ def brute_dense(x, Wg, bg, W1, b1, W2, b2, *, k, capacity_factor, tau=1.0, gumbe
 
 # ---------------------------------------------------------------- temperature schedule
 def temperature_at(step: int, tau0: float = 1.0, tau_min: float = 0.5, rate: float = 1e-4) -> float:
-    """tau_t = max(tau_min, tau0 - rate * t) ([A] 3.2: 0.5, 1.0, 1e-4; [M]: rate 1e-3)."""
+    """tau_t = max(tau_min, tau0 - rate * t) ([L] 3.3: 0.5, 1.0, 1e-4; [A] 3.3: rate 1e-3)."""
     return max(float(tau_min), float(tau0) - float(rate) * float(step))
 
 

@@ -5,7 +5,8 @@
 // back onto their tokens. Here each token gathers its own k rows instead, so no atomics are
 // needed and the sum order is fixed: float32 accumulation in j order, one final rounding.
 // Dropped slots (dest = -1) contribute exactly zero (the page's section 2.3 and 6.1). With a
-// shared expert (aberweb.com page, section 2.3) each token's sum starts from its output.
+// shared expert (lpnh.cn page, "Mixture of Experts（MoE）原理与工程落地全指南",
+// section 2.3) each token's sum starts from its output.
 #include "moe_common.h"
 #include "moe_kernels.h"
 

@@ -85,7 +85,8 @@ __device__ void write_stats(const int32_t* counts, const float* colsum, int E, i
 }
 
 // Load statistics of the batch from the expert counts (before capacity) and the sum of the
-// tokens' routing entropies (aberweb.com page on MoE misuse, sections 2.4 and 3.6; mhpn.cn
+// tokens' routing entropies (lpnh.cn page, "Mixture of Experts（MoE）原理与工程落地全指南",
+// sections 2.4 and 3.6; mhpn.cn
 // page on MoE architecture, section 3.1), in float64, rounded once to float32:
 //   out[0] = sum_e u_e^2 with u_e = counts_e / T
 //   out[1] = 0.5 Q50(u) + 0.3 Q90(u) + 0.2 Q99(u), Qq by linear interpolation between the

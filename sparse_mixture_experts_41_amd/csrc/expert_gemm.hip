@@ -18,6 +18,7 @@
 
 #include "moe_common.h"
 #include "moe_kernels.h"
+#include "tile_plan.h"
 
 namespace moe {
 
@@ -33,7 +34,7 @@ struct GemmArgs {
   int E, N, K;
   int R, C;               // rows of A/out and the capacity: segments outside them are skipped
   int splits;             // > 1: the tiles of the last, partial round of 256 are split along K into at
-                          // most this many parts (linear epilogue only); see tail_plan
+                          // most this many parts (linear epilogue only); see tile_plan.h
   void* out2;             // float side buffer of those parts past the first: dense 256 x 256 tiles
   const int32_t* rows;    // [R] or null: A row of expert-sorted row r is rows[r] (fused gather)
   int a_rows;             // rows of A when `rows` is set (a_rows * K * 2 < 2^31)
@@ -159,53 +160,25 @@ __device__ __forceinline__ TileScan scan_tiles(const GemmArgs& g, int BM, int ti
   return s;
 }
 
-// Tile t < total -> (e, mt, nt, mbase) as decode_tile gives them, and e's segment rows.
+// Tile t < total -> (e, mt, nt, mbase) and e's segment rows. Experts come in order, each
+// expert's tiles in the order of plan::tile_in_expert (column tiles outer, row tiles inner).
 __device__ __forceinline__ void locate_tile(const TileScan& s, int tile, int tiles_n, int& e, int& mt, int& nt,
                                             int& mbase, int& m_e) {
   const unsigned long long past = __ballot(s.cnt_incl > tile);
   e = __builtin_amdgcn_readfirstlane(static_cast<int>(__builtin_ctzll(past)));
   const int tm = __builtin_amdgcn_readlane(s.tm, e);
   const int t = tile - (__builtin_amdgcn_readlane(s.cnt_incl, e) - tm * tiles_n);
-  nt = t / tm;
-  mt = t - nt * tm;
+  plan::tile_in_expert(t, tm, tiles_n, mt, nt);
   mbase = __builtin_amdgcn_readlane(s.tm_incl, e) - tm;
   m_e = __builtin_amdgcn_readlane(s.rows, e);
 }
 
-// Tail split: the tiles of the whole rounds of 256 run unsplit; the L tiles of the last, partial
-// round are split along K into P parts (as many as fill the round, at most `max_parts`, each
-// at least 4 K steps), so the launch ends after about full/256 + 1/P rounds instead of a whole
-// extra round. Part 0 writes the output (with the bias); parts 1..P-1 write dense 256 x 256
-// float tiles to the side buffer, slot (tile - full) (P - 1) + part - 1, and
-// tail_fixup_kernel adds them in part order.
-struct TailPlan {
-  int full, L, P;
-};
-__device__ __forceinline__ TailPlan tail_plan(int n_tiles, int nk_total, int max_parts) {
-  const int rem = n_tiles % 256;
-  int P = rem > 0 ? 256 / rem : 1;
-  P = min(P, max_parts);
-  P = min(P, nk_total / 4);
-  if (max_parts <= 1 || rem == 0 || P < 2) return TailPlan{n_tiles, 0, 1};
-  return TailPlan{n_tiles - rem, rem, P};
-}
-constexpr int kTailMaxParts = 8;
+// Tile order, placement over the XCDs and the K split of the last, partial round: tile_plan.h.
+constexpr int kTailMaxParts = plan::kMaxParts;
 constexpr size_t kTailTile = 256 * 256;            // floats per side-buffer tile
 
-// The hardware hands workgroup b to XCD (b mod 8). Workgroups are renumbered so that each XCD
-// takes bundles of kBundle consecutive tiles (tiles that share an expert's operand panels, so
-// they meet in that XCD's L2), and bundles go round-robin over the 8 XCDs (so experts of very
-// different sizes still spread evenly over the chip). Covers [0, 8*kBundle*ceil(n/(8*kBundle))).
-constexpr int kBundle = 16;
-__device__ __forceinline__ int xcd_tile_id(int bid) {
-  const int x = bid & 7, j = bid >> 3;
-  return ((j / kBundle) * 8 + x) * kBundle + j % kBundle;
-}
-
-int round_grid(int n) {
-  const int g = 8 * kBundle;
-  return (n + g - 1) / g * g;
-}
+// Workgroups of a launch over at most n_max tiles (max_parts > 1: with the tail split).
+int plan_grid(int n_max, int max_parts) { return plan::grid_bound(n_max, max_parts); }
 
 // s_waitcnt with only vmcnt limited (gfx9 encoding: vmcnt bits [3:0] and [15:14]).
 template <int N>
@@ -338,22 +311,13 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 
   const int tiles_n = (g.N + BN - 1) / BN;
   const TileScan scan = scan_tiles(g, BM, tiles_n);
-  const int n_tiles = scan.total;
-  const TailPlan plan = tail_plan(n_tiles, g.K / BK, EPI == kEpiLinear && !g.wgrad ? g.splits : 1);
-  const int n_units = plan.full + plan.L * plan.P;
-  const int unit = xcd_tile_id(blockIdx.x);
-  if (unit >= n_units) return;
-  int tile = unit, kpart = 0, parts = 1;
-  if (unit >= plan.full) {
-    const int u = unit - plan.full;
-    tile = plan.full + u / plan.P;
-    kpart = u % plan.P;
-    parts = plan.P;
-  }
+  plan::Unit unit;
+  if (!plan::unit_of(blockIdx.x, scan.total, g.K / BK, EPI == kEpiLinear && !g.wgrad ? g.splits : 1, unit)) return;
   // uniform by construction; said so, so that the buffer resources stay in scalar registers
-  tile = __builtin_amdgcn_readfirstlane(tile);
-  kpart = __builtin_amdgcn_readfirstlane(kpart);
-  parts = __builtin_amdgcn_readfirstlane(parts);
+  const int tile = __builtin_amdgcn_readfirstlane(unit.tile);
+  const int kpart = __builtin_amdgcn_readfirstlane(unit.kpart);
+  const int parts = __builtin_amdgcn_readfirstlane(unit.parts);
+  const int side_slot = __builtin_amdgcn_readfirstlane(unit.side);
   int e, mt, nt, mbase, m_e;
   locate_tile(scan, tile, tiles_n, e, mt, nt, mbase, m_e);
   const int panel = __builtin_amdgcn_readfirstlane(mbase + mt);   // K-step-tiled layouts
@@ -365,8 +329,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int lda = g.lda ? g.lda : g.K, ldb = g.ldb ? g.ldb : g.K;
   const int K = g.wgrad ? (__builtin_amdgcn_readlane(scan.kept, e) + kWgradK - 1) / kWgradK * kWgradK : g.K;
   const size_t kofs = g.wgrad ? static_cast<size_t>(__builtin_amdgcn_readlane(scan.off, e)) : 0;
-  const int k_first = __builtin_amdgcn_readfirstlane((K / BK) * kpart / parts);
-  const int k_last = __builtin_amdgcn_readfirstlane((K / BK) * (kpart + 1) / parts);
+  int kf, kl;
+  plan::part_range(K / BK, kpart, parts, kf, kl);   // pair-aligned: K / BK is even here
+  const int k_first = __builtin_amdgcn_readfirstlane(kf);
+  const int k_last = __builtin_amdgcn_readfirstlane(kl);
   const int nk = k_last - k_first;           // K steps of this part
   const bool gathered = g.rows != nullptr;
   const bool a_tiled = g.a_tiled != 0;
@@ -506,8 +472,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     char* st2 = smem + (4 + wave) * 32 * PITCH;            // staged inputs of the activation
     // the tile's output block and its row pitch: the output (part 0) or a side-buffer tile
     const bool side = EPI == kEpiLinear && kpart > 0;
-    char* outb = side ? static_cast<char*>(g.out2) +
-                            ((static_cast<size_t>(tile - plan.full) * (plan.P - 1) + kpart - 1) * kTailTile) * 4
+    char* outb = side ? static_cast<char*>(g.out2) + static_cast<size_t>(side_slot) * kTailTile * 4
                       : static_cast<char*>(g.out) + (out_base + static_cast<size_t>(row0 + m0) * N + n0) * OB;
     const size_t pitch = side ? 256 : static_cast<size_t>(N);
     __syncthreads();                                       // every wave is done with the ring
@@ -956,7 +921,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(GemmArgs g) {
 
 // Adds the side-buffer parts of the split tail tiles to the output, parts 1, 2, ... in that
 // order after part 0 (already in the output). A work unit is kFixupRows rows of one split
-// tile; the fixed grid strides over the L * 256 / kFixupRows units so that the whole chip
+// tile (plan::split_tile); the fixed grid strides over the units so that the whole chip
 // shares the traffic, and each thread issues the loads of all parts before it adds.
 constexpr int kFixupRows = 8;
 constexpr int kFixupGrid = 1024;
@@ -964,17 +929,20 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs g) {
   constexpr int BM = 256, BN = 256, BK = 32, SLABS = BM / kFixupRows, RPP = 256 / (BN / 4);
   const int tiles_n = (g.N + BN - 1) / BN;
   const TileScan scan = scan_tiles(g, BM, tiles_n);
-  const TailPlan plan = tail_plan(scan.total, g.K / BK, g.splits);
+  const int nk_total = g.K / BK;
+  const int n_split = plan::split_tiles(scan.total, nk_total, g.splits);
   const int N = g.N;
   float* out = static_cast<float*>(g.out);
   const int c = (threadIdx.x % (BN / 4)) * 4;
-  for (int u = blockIdx.x; u < plan.L * SLABS; u += gridDim.x) {
-    const int s = u / SLABS, slab = u % SLABS;
+  for (int u = blockIdx.x; u < n_split * SLABS; u += gridDim.x) {
+    const int slab = u % SLABS;
+    int tile, P, side0;
+    plan::split_tile(u / SLABS, scan.total, nk_total, g.splits, tile, P, side0);
     int e, mt, nt, mbase, m_e;
-    locate_tile(scan, plan.full + s, tiles_n, e, mt, nt, mbase, m_e);
+    locate_tile(scan, tile, tiles_n, e, mt, nt, mbase, m_e);
     const int row0 = g.dense ? 0 : __builtin_amdgcn_readlane(scan.off, e);
     const int m0 = mt * BM, n0 = nt * BN;
-    const float* side = static_cast<const float*>(g.out2) + static_cast<size_t>(s) * (plan.P - 1) * kTailTile;
+    const float* side = static_cast<const float*>(g.out2) + static_cast<size_t>(side0) * kTailTile;
 #pragma unroll
     for (int j = 0; j < kFixupRows / RPP; ++j) {
       const int r = slab * kFixupRows + j * RPP + static_cast<int>(threadIdx.x) / (BN / 4);
@@ -982,14 +950,14 @@ __global__ __launch_bounds__(256) void tail_fixup_kernel(GemmArgs g) {
       floatx4 w[kTailMaxParts - 1];
 #pragma unroll
       for (int p = 1; p < kTailMaxParts; ++p)
-        if (p < plan.P)
+        if (p < P)
           w[p - 1] = __builtin_nontemporal_load(
               reinterpret_cast<const floatx4*>(side + (p - 1) * kTailTile + r * BN + c));
       floatx4* o = reinterpret_cast<floatx4*>(out + static_cast<size_t>(row0 + m0 + r) * N + n0 + c);
       floatx4 v = *o;
 #pragma unroll
       for (int p = 1; p < kTailMaxParts; ++p)
-        if (p < plan.P) {
+        if (p < P) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] += w[p - 1][q];
         }
@@ -1013,7 +981,7 @@ bool ffn_gathers(const FfnArgs& a) {
 
 int ffn_splits(const FfnArgs& a) { return (a.bf16 && a.C > 16) ? kTailMaxParts : 1; }
 
-size_t tail_side_floats() { return static_cast<size_t>(255) * kTailTile; }
+size_t tail_side_floats() { return static_cast<size_t>(plan::kSideSlots) * kTailTile; }
 
 bool ffn_h_tiled(int bf16, int C) { return bf16 && C > 16; }
 
@@ -1043,8 +1011,8 @@ static hipError_t launch_ffn(const GemmArgs& g1, const GemmArgs& g2, bool bf16, 
                        stream, g2);
     return hipGetLastError();
   }
-  const int grid1 = round_grid(tile_grid(R, E, C, 256, N1, 256));
-  const int grid2 = round_grid(tile_grid(R, E, C, 256, N2, 256) + (g2.splits > 1 ? 256 : 0));
+  const int grid1 = plan_grid(tile_grid(R, E, C, 256, N1, 256), 1);
+  const int grid2 = plan_grid(tile_grid(R, E, C, 256, N2, 256), g2.splits);
   // GEMM1's A (the token rows, gathered or a plain copy) is row-major: pair staging for it.
   // GEMM2's A (H) is K-step-tiled; its B (W2) is pair-staged when row-major, and packed weights
   // are K-step-tiled like H
@@ -1109,7 +1077,7 @@ static hipError_t launch_rows_gemm(const GemmArgs& g, bool bf16, int C, hipStrea
     hipLaunchKernelGGL(grouped_gemv_bf16_kernel<EPI>, dim3(g.E * ((g.N + GV_COLS - 1) / GV_COLS)), dim3(256), 0,
                        stream, g);
   } else {
-    const int grid = round_grid(tile_grid(g.R, g.E, C, 256, g.N, 256) + (g.splits > 1 ? 256 : 0));
+    const int grid = plan_grid(tile_grid(g.R, g.E, C, 256, g.N, 256), EPI == kEpiLinear ? g.splits : 1);
     // (pair staging of row-major A measured 1-2% slower on the dA product, whose B takes the
     // transpose reads: one-step stages here)
     if (bnm)
@@ -1201,7 +1169,7 @@ hipError_t launch_wgrad(const WgradArgs& a, hipStream_t stream) {
     const int grid = a.E * ((a.M + 15) / 16) * ((a.N + 15) / 16);
     hipLaunchKernelGGL(grouped_gemm_f32_kernel<kEpiLinear>, dim3(grid), dim3(256), 0, stream, g);
   } else {
-    const int grid = round_grid(a.E * ((a.M + 255) / 256) * ((a.N + 255) / 256));
+    const int grid = plan_grid(a.E * ((a.M + 255) / 256) * ((a.N + 255) / 256), 1);
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<kEpiLinear, 32, 4>), dim3(grid), dim3(256), 0, stream, g);
   }
   return hipGetLastError();

@@ -621,7 +621,8 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
     MOE_HIP(moe::launch_shared_ffn(sa, st), "shared_ffn");
   }
   if (ev) MOE_HIP(hipEventRecord(ev[5], st), "event");
-  // 5. combine (adding the two K halves of GEMM2 when it was split, from the shared output)
+  // 5. combine (each token's float32 sum starts from the shared expert's output, if any; the
+  // K parts of GEMM2's split tail tiles were already added by tail_fixup_kernel)
   MOE_HIP(moe::launch_combine(y_perm, y_shared, dest, w, D.T, D.d, D.k, D.R, D.bf16 ? 1 : 0, y, st),
           "combine");
   if (ev) MOE_HIP(hipEventRecord(ev[6], st), "event");

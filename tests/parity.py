@@ -5,11 +5,13 @@ Tolerances (one place, used by every GPU test):
   * routing indices, counts, kept, offsets, dest, perm, drop mask: bit-exact against the
     oracle re-routing from the GPU's own float32 scores;
   * logits: per token, max_e |z - z_ref| <= 1e-4 * max_e |z_ref|;
-  * bf16 outputs: sum|y - y_ref| / sum|y_ref| <= 5e-3, and
-    max(|y - y_ref| - half_ulp_bf16(y_ref)) <= 2e-2 * rms(y_ref): the bound covers the
-    computation error beyond the one rounding of the result to its bf16 storage, which on
-    its own reaches 2^-9 |y| and exceeds 2e-2 rms for outputs above about 10 rms (workloads
-    with many dropped tokens have a small rms);
+  * bf16 outputs: sum|y - y_ref| / sum|y_ref| <= 5e-3, and max|y - y_ref| <= 2e-2 * rms(y_ref)
+    (rms over all elements) on every element with |y_ref| <= 2.56 rms. Above that, the one
+    rounding of the output to bf16, up to 2^-8 |y_ref| at the bottom of a binade, can take
+    more than half of the bound by itself, so those elements may exceed it by at most half a
+    bf16 ulp of y_ref. They are counted (n_big; n_credited = those that needed the credit) and
+    reported with the raw max|err| / rms, the |y_ref| / rms where it occurs, the error beyond
+    the half ulp (the computation's own error) and the error against y_ref rounded to bf16;
   * float32 outputs: max|y - y_ref| <= 1e-5 * max|y_ref|;
   * weights w, P, L: relative 1e-5 (float32 softmax against the float64 one); f: relative 1e-6;
   * routing statistics: loss_sq, loss_quant, loss_var, usage_std (float64 functions of the
@@ -29,8 +31,13 @@ from workloads import MoEShape, bf16_bits_to_f32, make_inputs, make_shared_exper
 Z_REL = 1e-4
 BF16_MAX_RMS = 2e-2
 BF16_MEAN_REL = 5e-3
+BF16_BIG_RMS = 2.56     # |y_ref| / rms above which the half-ulp rounding credit applies (2^-8 * 2.56 = 1e-2)
 F32_REL = 1e-5
 W_REL = 1e-5
+
+# Output error statistics of every check_output call in this process, by label (the GPU test
+# session prints the named workloads' rows at its end).
+PARITY_TABLE: dict[str, dict] = {}
 
 
 def config_of(s: MoEShape):
@@ -79,6 +86,15 @@ class Problem:
             sh = make_shared_expert(shape, self.shared_d_ffn, bias_std)
             self.shared_host = tuple(host_values(sh[n], dt) for n in ("W1s", "b1s", "W2s", "b2s"))
             self.shared_dev = tuple(to_device(sh[n], dt) for n in ("W1s", "b1s", "W2s", "b2s"))
+
+    @property
+    def label(self) -> str:
+        """The shape's name, with the variant's non-default settings in brackets."""
+        parts = [n for n, on in (("silu", self.activation == "silu"), (f"noise{self.noise_std:g}", self.noise_std > 0),
+                                 (f"shared{self.shared_d_ffn}", self.shared_d_ffn > 0),
+                                 (self.drop_policy, self.drop_policy != "token"), ("stats", self.route_stats),
+                                 ("packed", self.packed_weights)) if on]
+        return self.shape.name + (f"[{','.join(parts)}]" if parts else "")
 
     @property
     def has_variant(self) -> bool:
@@ -179,24 +195,52 @@ def half_ulp_bf16(v: np.ndarray) -> np.ndarray:
     return np.where(a >= 2.0 ** -126, 2.0 ** (e - 8), 0.0)
 
 
+def bf16_rne(v: np.ndarray) -> np.ndarray:
+    """float64 values rounded to bf16 (8 significant bits, nearest, ties to even), as float64."""
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)                      # v = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(m * 256.0) / 256.0, e)
+
+
 def check_output(y_gpu, y_ref, dtype, label="", rms=None):
-    """``rms`` defaults to rms(y_ref) over the given elements."""
+    """``rms`` defaults to rms(y_ref) over the given elements. Records the statistics under
+    ``label`` in PARITY_TABLE."""
     y_gpu = np.asarray(y_gpu, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
     err = np.abs(y_gpu - y_ref)
     if dtype == "f32":
         bound = F32_REL * np.max(np.abs(y_ref))
         assert err.max() <= bound, f"{label}: max err {err.max():.3e} > {bound:.3e}"
-        return {"max_err": float(err.max())}
+        stats = {"max_err_over_max_ref": float(err.max() / max(np.max(np.abs(y_ref)), 1e-300)),
+                 "elements": int(err.size)}
+        if label:
+            PARITY_TABLE[label] = dict(stats, dtype="f32")
+        return stats
     rms = float(np.sqrt(np.mean(y_ref ** 2))) if rms is None else float(rms)
     mean_rel = float(err.sum() / max(np.abs(y_ref).sum(), 1e-300))
-    excess = err - half_ulp_bf16(y_ref)
+    bound = BF16_MAX_RMS * rms
+    big = np.abs(y_ref) > BF16_BIG_RMS * rms
+    excess = err - np.where(big, half_ulp_bf16(y_ref), 0.0)
     i = int(np.argmax(excess))
-    assert excess.flat[i] <= BF16_MAX_RMS * rms, (
-        f"{label}: error {err.flat[i]:.3e} at |y_ref| = {abs(y_ref.flat[i]):.3e} exceeds half a bf16 ulp by "
-        f"{excess.flat[i]:.3e} > {BF16_MAX_RMS} * rms {rms:.3e}")
+    assert excess.flat[i] <= bound, (
+        f"{label}: error {err.flat[i]:.3e} at |y_ref| = {abs(y_ref.flat[i]):.3e} ({abs(y_ref.flat[i]) / rms:.2f} rms)"
+        f" exceeds {BF16_MAX_RMS} * rms = {bound:.3e}" + (" after the half-ulp credit" if big.flat[i] else ""))
     assert mean_rel <= BF16_MEAN_REL, f"{label}: mean relative error {mean_rel:.3e}"
-    return {"max_err_over_rms": float(err.max() / rms) if rms > 0 else 0.0,
-            "max_excess_over_rms": float(excess.max() / rms) if rms > 0 else 0.0, "mean_rel": mean_rel}
+    j = int(np.argmax(err))
+    scale = rms if rms > 0 else 1.0
+    beyond = err - half_ulp_bf16(y_ref)
+    stats = {"max_err_over_rms": float(err.flat[j] / scale),
+             "at_abs_y_over_rms": float(abs(y_ref.flat[j]) / scale),
+             "max_err_small_over_rms": float(np.max(err[~big]) / scale) if (~big).any() else 0.0,
+             "beyond_half_ulp_over_rms": float(np.max(beyond) / scale),
+             "err_vs_bf16_ref_over_rms": float(np.max(np.abs(y_gpu - bf16_rne(y_ref))) / scale),
+             "mean_rel": mean_rel,
+             "n_big": int(big.sum()),
+             "n_credited": int(np.sum(big & (err > bound))),
+             "elements": int(err.size)}
+    if label:
+        PARITY_TABLE[label] = dict(stats, dtype="bf16")
+    return stats
 
 
 def check_forward_full(p: Problem, gpu: dict | None = None) -> dict:
@@ -212,33 +256,44 @@ def check_forward_full(p: Problem, gpu: dict | None = None) -> dict:
     dropped_all = np.all(ref["dest"] < 0, axis=1)
     if not p.shared_d_ffn:
         assert np.all(gpu["y"][dropped_all] == 0.0), "fully dropped tokens must give exactly 0"
-    stats = check_output(gpu["y"], ref["y"], sh.dtype, sh.name)
+    stats = check_output(gpu["y"], ref["y"], sh.dtype, p.label)
     stats.update(kept=int(chk["dispatch"]["kept"].sum()), drops=int(chk["dispatch"]["drops"].sum()),
                  fully_dropped=int(dropped_all.sum()))
     return stats
 
 
-def sample_rows(T: int, dest: np.ndarray, n_random: int = 48, seed: int = 0):
-    """Sorted sample rows, and the uniform-random subset (an unbiased sample for rms(y_ref))."""
+def sample_rows(T: int, dsp: dict, n_random: int = 48, seed: int = 0, tile_rows: int = 256):
+    """Sorted sample tokens, and the positions of their uniform-random subset (an unbiased
+    sample for rms(y_ref)). Besides the random tokens, the first and last 8, and some with
+    partly or fully dropped slots, the sample holds the source token of one random row of every
+    (expert, tile_rows-row tile) of the expert-sorted rows, so every row tile of the grouped
+    GEMMs has an output compared."""
     rng = np.random.default_rng(seed)
+    dest = dsp["dest"]
     rand = rng.choice(T, size=min(n_random, T), replace=False)
     rows = set(range(min(8, T))) | set(range(max(0, T - 8), T)) | set(rand.tolist())
     partial = np.flatnonzero(np.any(dest < 0, axis=1) & np.any(dest >= 0, axis=1))
     full = np.flatnonzero(np.all(dest < 0, axis=1))
     rows |= set(partial[:8].tolist()) | set(full[:8].tolist())
+    perm = dsp["perm"]
+    for e, (m, o) in enumerate(zip(dsp["kept"], dsp["offsets"])):
+        for r0 in range(0, int(m), tile_rows):
+            r = int(o) + r0 + int(rng.integers(0, min(tile_rows, int(m) - r0)))
+            rows.add(int(perm[r]))
     rows = np.array(sorted(rows), dtype=np.int64)
     return rows, np.searchsorted(rows, np.sort(rand))
 
 
-def check_forward_sampled(p: Problem, gpu: dict | None = None) -> dict:
-    """Whole-layer parity at full size: routing on every token, outputs on sampled tokens."""
+def check_forward_sampled(p: Problem, gpu: dict | None = None, n_random: int = 48) -> dict:
+    """Whole-layer parity at full size: routing on every token, outputs on sampled tokens
+    (sample_rows: one in every row tile of every expert, plus n_random uniform ones)."""
     sh = p.shape
     gpu = run_forward(p) if gpu is None else gpu
     z_ref = oracle.logits(p.host["x"], p.host["Wg"], p.host["bg"])
     check_logits(gpu["logits"], z_ref)
     check_scores(p, gpu["logits"], gpu["scores"])
     chk = check_routing(p, gpu)
-    rows, rand_pos = sample_rows(sh.T, chk["dispatch"]["dest"])
+    rows, rand_pos = sample_rows(sh.T, chk["dispatch"], n_random)
     ref = oracle.forward_rows(rows, *p.host_args(), k=sh.k, capacity_factor=sh.capacity_factor,
                               tau=sh.temperature, gumbel=sh.gumbel, seed=sh.seed, given_scores=gpu["scores"],
                               **p.oracle_kw())
@@ -246,7 +301,7 @@ def check_forward_sampled(p: Problem, gpu: dict | None = None) -> dict:
     if not p.shared_d_ffn:
         assert np.all(gpu["y"][rows][dropped_all] == 0.0)
     rms = np.sqrt(np.mean(ref["y_rows"][rand_pos] ** 2))      # rms(y_ref) over all tokens, estimated
-    stats = check_output(gpu["y"][rows], ref["y_rows"], sh.dtype, sh.name, rms=rms)
+    stats = check_output(gpu["y"][rows], ref["y_rows"], sh.dtype, p.label, rms=rms)
     stats.update(kept=int(chk["dispatch"]["kept"].sum()), drops=int(chk["dispatch"]["drops"].sum()),
                  rows=len(rows))
     return stats

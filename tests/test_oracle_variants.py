@@ -52,12 +52,12 @@ def test_gaussian_noise_is_standard_normal():
 
 
 def test_temperature_schedule_values():
-    # [A] 3.2: tau = max(0.5, 1.0 - 0.0001 * step)
+    # lpnh.cn page, section 3.3: tau = max(0.5, 1.0 - 0.0001 * step)
     assert oracle.temperature_at(0) == 1.0
     assert oracle.temperature_at(2500) == pytest.approx(0.75)
     assert oracle.temperature_at(5000) == pytest.approx(0.5)
     assert oracle.temperature_at(100_000) == 0.5
-    # [M]: the same floor with rate 0.001
+    # aberweb.com page, section 3.3: the same floor with rate 0.001
     assert oracle.temperature_at(250, rate=1e-3) == pytest.approx(0.75)
     assert oracle.temperature_at(600, rate=1e-3) == 0.5
 
