@@ -1,4 +1,4 @@
-"""ctypes view of libmoe.so (the C ABI declared in include/moe.h).
+"""ctypes view of libmoe.so (the C ABI declared in include/moe.h and include/moe_probe.h).
 
 Loading fails loudly when the library has not been built: there is no fallback path.
 """
@@ -41,6 +41,7 @@ MOE_ACT_GELU, MOE_ACT_SILU = 0, 1
 MOE_DROP_TOKEN_ORDER, MOE_DROP_RANDOM, MOE_DROP_REROUTE = 0, 1, 2
 MOE_ROUTE_STATS = 5
 MOE_WEIGHTS_LINEAR, MOE_WEIGHTS_PACKED = 0, 1
+MOE_PROBE_CHAINS = 16
 
 
 class MoeVariant(ctypes.Structure):
@@ -84,6 +85,8 @@ _SIGS = {
                                     ctypes.POINTER(MoeBackwardAux), _P, ctypes.c_size_t, _P]),
     "moe_pack_expert_weights": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _P, _P, _P]),
     "moe_temperature_at": (ctypes.c_float, [ctypes.c_int64, ctypes.c_float, ctypes.c_float, ctypes.c_float]),
+    "moe_probe_copy": (ctypes.c_int, [_P, _P, ctypes.c_size_t, _P]),
+    "moe_probe_mfma": (ctypes.c_int, [_P, ctypes.c_int64, ctypes.c_int64, _P]),
     "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "moe_last_error": (ctypes.c_char_p, []),
 }

@@ -1,6 +1,7 @@
 // C ABI of the MoE layer: argument validation, workspace carving and stage orchestration.
 // Every check happens before the first HIP call, so an invalid call enqueues nothing.
 #include "../../include/moe.h"
+#include "../../include/moe_probe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -674,6 +675,28 @@ moe_status moe_pack_expert_weights(int64_t E, int64_t rows, int64_t cols, const 
   const uintptr_t n = static_cast<uintptr_t>(E * rows * cols * 2);
   if (a < b + n && b < a + n) return fail(MOE_EINVAL, "W and W_packed overlap");
   MOE_HIP(moe::launch_pack_weights(W, W_packed, E, rows, cols, reinterpret_cast<hipStream_t>(stream)), "pack");
+  return MOE_OK;
+}
+
+moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, moe_stream_t stream) {
+  if (bytes < 16 || bytes % 16 != 0) return fail(MOE_EINVAL, "bytes must be a positive multiple of 16");
+  MOE_CHECK(need(src, 16, "src"));
+  MOE_CHECK(need(dst, 16, "dst"));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes) return fail(MOE_EINVAL, "src and dst overlap");
+  MOE_HIP(moe::launch_probe_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream)), "probe_copy");
+  return MOE_OK;
+}
+
+moe_status moe_probe_mfma(float* out, int64_t workgroups, int64_t iters, moe_stream_t stream) {
+  static_assert(MOE_PROBE_CHAINS == 16, "the header's chain count");
+  if (moe::probe_mfma_chains() != MOE_PROBE_CHAINS) return fail(MOE_EINVAL, "probe chain count mismatch");
+  if (workgroups < 1 || workgroups > (int64_t{1} << 20)) return fail(MOE_EINVAL, "workgroups must be in [1, 2^20]");
+  if (iters < 1 || iters > (int64_t{1} << 24)) return fail(MOE_EINVAL, "iters must be in [1, 2^24]");
+  MOE_CHECK(need(out, 4, "out"));
+  MOE_HIP(moe::launch_probe_mfma(out, static_cast<int>(workgroups), static_cast<int>(iters),
+                                 reinterpret_cast<hipStream_t>(stream)),
+          "probe_mfma");
   return MOE_OK;
 }
 

@@ -293,4 +293,10 @@ struct DxArgs {
 };
 hipError_t launch_dx(const DxArgs& a, int bf16, hipStream_t stream);
 
+// Peak probes (csrc/probe.hip): a plain device copy of `bytes` (a multiple of 16), and
+// `workgroups` x 256 threads of independent bf16 MFMA chains (probe_mfma_chains() per wave).
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+hipError_t launch_probe_mfma(float* out, int workgroups, int iters, hipStream_t stream);
+int probe_mfma_chains();
+
 }  // namespace moe

@@ -17,7 +17,7 @@ from ._lib import (BWD_STAGE_NAMES, MOE_BACKWARD_STAGES, MOE_FORWARD_STAGES, STA
 __all__ = ["make_config", "capacity", "workspace_size", "workspace", "route", "dispatch", "expert_ffn", "combine",
            "forward", "ForwardPlan", "StageEvents", "STAGE_NAMES", "MoeConfig", "make_variant", "workspace_size_ex",
            "temperature_at", "DROP_POLICIES", "ROUTE_STAT_NAMES", "TrainPlan", "BWD_STAGE_NAMES",
-           "MOE_BACKWARD_STAGES", "workspace_size_train"]
+           "MOE_BACKWARD_STAGES", "workspace_size_train", "probe_copy", "probe_mfma"]
 
 
 def _storage_dtype(cfg: MoeConfig) -> torch.dtype:
@@ -249,6 +249,22 @@ def pack_expert_weights(W, stream=None):
     _lib.check(_lib.load().moe_pack_expert_weights(int(E), int(rows), int(cols), _ptr(W), _ptr(out),
                                                     _stream(stream)))
     return out
+
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """moe_probe_copy: dst's bytes = src's bytes (contiguous device tensors of the same byte size,
+    a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _lib.check(_lib.load().moe_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def probe_mfma(out: torch.Tensor, workgroups: int, iters: int, stream=None) -> float:
+    """moe_probe_mfma into out (float32, workgroups * 256 elements); returns the flops issued."""
+    _expect(out, "out", (int(workgroups) * 256,), torch.float32)
+    _lib.check(_lib.load().moe_probe_mfma(_ptr(out), int(workgroups), int(iters), _stream(stream)))
+    return float(workgroups) * 4 * _lib.MOE_PROBE_CHAINS * iters * 16 * 16 * 32 * 2
 
 
 def workspace_size_ex(cfg: MoeConfig, variant) -> int:

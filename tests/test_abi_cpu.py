@@ -24,16 +24,22 @@ def lib():
     return _lib.load()
 
 
+HEADERS = sorted(os.path.join(ROOT, "include", n) for n in os.listdir(os.path.join(ROOT, "include"))
+                 if n.endswith(".h"))
+
+
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = _declared_functions()
     for n in ("moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward", "moe_capacity",
-              "moe_workspace_size", "moe_status_str", "moe_last_error"):
+              "moe_workspace_size", "moe_status_str", "moe_last_error", "moe_probe_copy", "moe_probe_mfma"):
         assert n in names
 
 
@@ -266,3 +272,17 @@ def test_training_entry_points_validate_on_the_host(lib):
     bad[15] = ctypes.c_size_t(1024)                                 # workspace too small
     assert lib.moe_backward(ctypes.byref(cfg), None, *bad) == MOE_EWORKSPACE
     assert lib.moe_backward(ctypes.byref(cfg), ctypes.byref(shared), *args) == MOE_EUNSUPPORTED
+
+
+def test_probes_reject_bad_arguments_before_any_launch(lib):
+    # every check runs before the first HIP call, so these return without touching a GPU
+    dummy = ctypes.c_void_p(1 << 20)
+    assert lib.moe_probe_copy(None, dummy, 1024, None) == MOE_EINVAL
+    assert lib.moe_probe_copy(dummy, ctypes.c_void_p((1 << 20) + 4096), 1000, None) == MOE_EINVAL   # not 16 k
+    assert lib.moe_probe_copy(dummy, ctypes.c_void_p((1 << 20) + 512), 1024, None) == MOE_EINVAL    # overlap
+    assert lib.moe_probe_copy(ctypes.c_void_p((1 << 20) + 8), ctypes.c_void_p(1 << 24), 1024, None) == MOE_EINVAL
+    assert lib.moe_probe_mfma(None, 4, 10, None) == MOE_EINVAL
+    assert lib.moe_probe_mfma(dummy, 0, 10, None) == MOE_EINVAL
+    assert lib.moe_probe_mfma(dummy, 4, 0, None) == MOE_EINVAL
+    assert lib.moe_probe_mfma(dummy, (1 << 20) + 1, 10, None) == MOE_EINVAL
+    assert b"iters" in lib.moe_last_error() or b"workgroups" in lib.moe_last_error()
