@@ -981,7 +981,12 @@ bool ffn_gathers(const FfnArgs& a) {
 
 int ffn_splits(const FfnArgs& a) { return (a.bf16 && a.C > 16) ? kTailMaxParts : 1; }
 
-size_t tail_side_floats() { return static_cast<size_t>(plan::kSideSlots) * kTailTile; }
+size_t tail_side_floats(int R, int E, int C, int N) {
+  // a split tail writes L (P - 1) side tiles: fewer than kSideSlots, and at most
+  // (kMaxParts - 1) per tile of the launch
+  const long long by_tiles = static_cast<long long>(kTailMaxParts - 1) * tile_grid(R, E, C, 256, N, 256);
+  return static_cast<size_t>(by_tiles < plan::kSideSlots ? by_tiles : plan::kSideSlots) * kTailTile;
+}
 
 bool ffn_h_tiled(int bf16, int C) { return bf16 && C > 16; }
 

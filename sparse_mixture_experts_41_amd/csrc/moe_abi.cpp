@@ -185,7 +185,7 @@ Layout layout_of(const Derived& D) {
   L.x_perm = take(R * static_cast<size_t>(D.d) * D.esize);
   L.H = take(moe::ffn_h_rows(static_cast<int>(R), static_cast<int>(E), clamp_c(D), D.bf16) * D.dff * D.esize);
   L.y_perm = take(R * static_cast<size_t>(D.d) * 4);
-  L.side = take(D.bf16 && clamp_c(D) > 16 ? moe::tail_side_floats() * 4 : 0);
+  L.side = take(D.bf16 && clamp_c(D) > 16 ? moe::tail_side_floats(D.R, D.E, clamp_c(D), D.d) * 4 : 0);
   L.Hs = take(D.dffs > 0 ? moe::ffn_h_rows(static_cast<int>(T), 1, static_cast<int>(T), D.bf16) * D.dffs * D.esize : 0);
   L.ys = take(D.dffs > 0 ? T * static_cast<size_t>(D.d) * 4 : 0);
   const bool random = D.policy == MOE_DROP_RANDOM, reroute = D.policy == MOE_DROP_REROUTE;

@@ -110,7 +110,7 @@ struct FfnArgs {
   const void* b2;         // [E,d] or null
   void* H;                // ffn_h_rows(R, E, C, bf16) x d_ffn: row-major, or tiled panels (ffn_h_tiled)
   float* y_perm;          // [R,d]
-  float* side;            // tail_side_floats() floats when ffn_splits() > 1: GEMM2's split-tail parts
+  float* side;            // tail_side_floats(R, E, C, d) floats when ffn_splits() > 1: GEMM2's split-tail parts
   int E, d, d_ffn, R, C;
   int bf16;
   int act;                // kActGelu or kActSilu
@@ -127,7 +127,7 @@ bool ffn_gathers(const FfnArgs& a);
 // GEMM2 result.
 int ffn_splits(const FfnArgs& a);
 // Floats of the side buffer of a tail-split product (255 dense 256 x 256 tiles).
-size_t tail_side_floats();
+size_t tail_side_floats(int R, int E, int C, int N);
 // Whether the hidden layer H between the two expert GEMMs is kept in K-step-tiled panels (the
 // bf16 MFMA path): the rows of each (expert, 256-row tile) form one panel of d_ffn/32 contiguous
 // 16 KB blocks of 256 rows x 32 columns, panels in the order of the experts' row tiles. Rows past
@@ -195,7 +195,7 @@ hipError_t launch_bwd_dact(const BwdDactArgs& a, hipStream_t stream);
 
 // dXp[r] = dA[r] W1_e (float, [R, d]); W1 [E, d_ffn, d] as given, W1T [E, d, d_ffn] its transpose
 // (read only when bwd_weights_transposed()). With bwd_dx_splits() > 1 the last round's tiles are
-// tail-split through `side` (tail_side_floats()).
+// tail-split through `side` (tail_side_floats(R, E, C, d)).
 struct BwdDxArgs {
   const void* dA;
   const void* W1;

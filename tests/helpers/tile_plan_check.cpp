@@ -5,7 +5,8 @@
 // For every launch size n (tiles), K depth (steps of 32) and split limit it checks:
 //   * every workgroup with work has bid < the host grid (grid_bound);
 //   * every tile is covered exactly once when unsplit, or by parts 0..P-1 exactly once each;
-//   * side slots are unique, below kSideSlots, -1 exactly for part 0, and the fixup kernel's
+//   * side slots are unique, below kSideSlots and (kMaxParts - 1) n (the side buffer's size),
+//     -1 exactly for part 0, and the fixup kernel's
 //     enumeration (split_tiles, split_tile) names every split tile once with the same slots;
 //   * the XCDs' work (workgroups with a unit, bid mod 8) differs by at most one bundle;
 //   * K parts tile [0, nk) in order; with an even nk (the bf16 MFMA path) each part starts on
@@ -45,7 +46,7 @@ static int check_launch(int n, int nk, int max_parts) {
     if (seen[static_cast<size_t>(u.tile) * kMaxParts + u.kpart]++) return fail("unit twice", n, nk, u.tile, u.kpart);
     if ((u.kpart == 0) != (u.side < 0)) return fail("side slot of part 0", n, nk, u.tile, u.side);
     if (u.side >= 0) {
-      if (u.side >= kSideSlots) return fail("side slot too large", n, nk, u.tile, u.side);
+      if (u.side >= kSideSlots || u.side >= (kMaxParts - 1) * n) return fail("side slot too large", n, nk, u.tile, u.side);
       if (side_used[u.side]++) return fail("side slot twice", n, nk, u.tile, u.side);
       side_tile[u.side] = u.tile;
       side_part[u.side] = u.kpart;
