@@ -150,6 +150,26 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
                        const moe_forward_aux* aux, void* ws, size_t ws_bytes,
                        moe_stream_t stream);
 
+/* moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the workspace is a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES inside the library instead of the caller's ws. Arguments
+ * and results as moe_forward; the caller still passes every input and output buffer.
+ *   - Uses the scratch of the calling thread's current device; `stream` must belong to it.
+ *     The first call on a device looks the array's address up there (no allocation); every
+ *     GPU the library runs on holds the array until the process ends.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (other
+ *     streams, other threads) race and must be serialised by the caller. Nothing in the
+ *     array needs to start at zero; it keeps the last call's intermediates.
+ *   - Calls no hipMalloc, hipFree or allocating library routine.
+ *   - MOE_EUNSUPPORTED when moe_workspace_size(cfg) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     (decode-sized batches and small layers fit; the named large layers do not), checked
+ *     before any HIP call; other errors as moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const void* Wg, const float* bg,
+                               const void* W1, const void* b1, const void* W2, const void* b2,
+                               void* y, float* f, float* P, float* L, int32_t* counts, int32_t* kept,
+                               const moe_forward_aux* aux, moe_stream_t stream);
+
 /* ---------------------------------------------------------------------------------------
  * Forward variants. A zeroed moe_variant is the plain layer above, and moe_forward_ex with
  * variant = NULL is moe_forward. Stage calls (moe_route ... moe_combine) take no variant.

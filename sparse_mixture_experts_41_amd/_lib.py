@@ -42,6 +42,7 @@ MOE_DROP_TOKEN_ORDER, MOE_DROP_RANDOM, MOE_DROP_REROUTE = 0, 1, 2
 MOE_ROUTE_STATS = 5
 MOE_WEIGHTS_LINEAR, MOE_WEIGHTS_PACKED = 0, 1
 MOE_PROBE_CHAINS = 16
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeVariant(ctypes.Structure):
@@ -75,6 +76,8 @@ _SIGS = {
     "moe_combine": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "moe_forward": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [_CFG, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                           ctypes.POINTER(MoeForwardAux), _P]),
     "moe_workspace_size_ex": (ctypes.c_int, [_CFG, _VAR, ctypes.POINTER(ctypes.c_size_t)]),
     "moe_forward_ex": (ctypes.c_int, [_CFG, _VAR, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                       ctypes.POINTER(MoeForwardAux), _P, ctypes.c_size_t, _P]),

@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "moe_kernels.h"
@@ -260,6 +261,30 @@ T* at(void* ws, size_t off) {
     const hipError_t e_ = (expr);                        \
     if (e_ != hipSuccess) return hip_fail(e_, where);    \
   } while (0)
+
+// The allocation-free forward's workspace: one file-scope device array, which every GPU the
+// library runs on holds until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory: its device address on each GPU is looked up once, with that GPU current,
+// and only that address is ever handed to kernels.
+__device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices] = {};
+
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  MOE_HIP(hipGetDevice(&dev), "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices) return fail(MOE_EUNSUPPORTED, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MOE_EHIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
 
 moe::RouterArgs router_args(const Derived& D, const void* x, const void* Wg, const float* bg, float* logits,
                             float* scores, int32_t* idx, float* w, float* probsum, int32_t* hist) {
@@ -652,6 +677,23 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const void* Wg, con
                        int32_t* counts, int32_t* kept, const moe_forward_aux* aux, void* ws, size_t ws_bytes,
                        moe_stream_t stream) {
   return forward_impl(cfg, nullptr, x, Wg, bg, W1, b1, W2, b2, y, f, P, L, counts, kept, aux, ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const void* Wg, const float* bg,
+                               const void* W1, const void* b1, const void* W2, const void* b2, void* y, float* f,
+                               float* P, float* L, int32_t* counts, int32_t* kept, const moe_forward_aux* aux,
+                               moe_stream_t stream) {
+  Derived D;
+  MOE_CHECK(check_config(cfg, &D));
+  const size_t need_bytes = layout_of(D).total;
+  if (need_bytes > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_EUNSUPPORTED, "this configuration needs " + std::to_string(need_bytes) +
+                                      " bytes of workspace; the static scratch of moe_forward_noalloc holds " +
+                                      std::to_string(static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES)));
+  void* ws = nullptr;
+  MOE_CHECK(scratch_of_current_device(&ws));
+  return forward_impl(cfg, nullptr, x, Wg, bg, W1, b1, W2, b2, y, f, P, L, counts, kept, aux, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_forward_ex(const moe_config* cfg, const moe_variant* variant, const void* x, const void* Wg,

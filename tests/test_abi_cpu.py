@@ -286,3 +286,15 @@ def test_probes_reject_bad_arguments_before_any_launch(lib):
     assert lib.moe_probe_mfma(dummy, 4, 0, None) == MOE_EINVAL
     assert lib.moe_probe_mfma(dummy, (1 << 20) + 1, 10, None) == MOE_EINVAL
     assert b"iters" in lib.moe_last_error() or b"workgroups" in lib.moe_last_error()
+
+
+def test_noalloc_rejects_a_large_workspace_before_any_hip_call(lib):
+    # the Mixtral-like layer needs far more workspace than the static scratch: refused up front
+    cfg = _cfg("mixtral_like")
+    n = ctypes.c_size_t()
+    assert lib.moe_workspace_size(ctypes.byref(cfg), ctypes.byref(n)) == MOE_OK
+    assert n.value > _lib.MOE_NOALLOC_SCRATCH_BYTES
+    p = ctypes.c_void_p(1 << 20)
+    st = lib.moe_forward_noalloc(ctypes.byref(cfg), p, p, None, p, None, p, None, p, p, p, p, p, p, None, None)
+    assert st == MOE_EUNSUPPORTED
+    assert b"static scratch" in lib.moe_last_error()
