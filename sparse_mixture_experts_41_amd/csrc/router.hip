@@ -11,8 +11,12 @@
 // MFMAs, reading each x row once, adds the four wave partials in a fixed order, and runs
 // softmax and top-k with four lanes per token row (the row lives in LDS). With fewer than 256
 // groups of 16 tokens, d is cut into K slices instead: slice partials go to a workspace and a
-// second kernel adds them in slice order before the same epilogue. Partial statistics (column
-// sums of p, expert histograms) are written per group of 16 tokens.
+// second kernel adds them in slice order before the same epilogue. With many groups and a
+// small W_g, a persistent streaming kernel instead gives each wave whole groups and keeps W_g
+// in LDS (router_stream_kernel). Partial statistics (column sums of p, expert histograms) are
+// written per group of 16 tokens.
+#include <type_traits>
+
 #include "moe_common.h"
 #include "moe_kernels.h"
 
@@ -148,7 +152,21 @@ __device__ __forceinline__ void group_partials(const float* rows, int ldr, uint6
 // Cross-lane steps are xor butterflies within each group of four lanes, so all four lanes of a
 // token hold identical values. Leaves p in `rows` (zero rows past nt); lane 4 t returns token
 // t's bitmask of chosen experts, the other lanes 0.
-__device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
+// The synchronisation of the epilogue's LDS row buffer: the workgroup barrier when the
+// workgroup's waves share the rows, or only a compiler fence when one wave owns them (a
+// wave's LDS accesses are processed in order, so its lanes see each other's earlier writes).
+template <bool WAVE>
+__device__ __forceinline__ void rows_sync() {
+  if constexpr (WAVE) {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+  } else {
+    __syncthreads();
+  }
+}
+
+template <bool WAVE>
+__device__ __forceinline__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
                                   float noise_std, uint32_t key0, uint32_t key1, float* __restrict__ logits,
                                   float* __restrict__ scores, int32_t* __restrict__ idx_out,
                                   float* __restrict__ w_out, int32_t* __restrict__ next_out, float& entropy) {
@@ -171,11 +189,11 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
       row[e] = s;
     }
   }
-  __syncthreads();
+  rows_sync<WAVE>();
   if (scores)
     for (int r = 0; r < nt; ++r)
       if (lane < E) scores[base + static_cast<size_t>(r) * E + lane] = rows[r * ldr + lane];
-  __syncthreads();
+  rows_sync<WAVE>();
   entropy = 0.0f;
   if (!valid) {
     for (int e = e0; e < e1; ++e) row[e] = 0.0f;
@@ -231,7 +249,7 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
   h += __shfl_xor(h, 1);
   h += __shfl_xor(h, 2);
   entropy = h;
-  __syncthreads();
+  rows_sync<WAVE>();
   float psel = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j)
@@ -251,19 +269,21 @@ __device__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, i
 }
 
 // One wave per 16-token group `grp`: epilogue (four lanes per token) and the group partials.
-// `rows` holds the group's logits with b_g added; rows past nt_tok are ignored.
-__device__ void group_finish(const RouterArgs& a, float* rows, int LDE, int t0, int nt_tok, int grp) {
+// `rows` holds the group's logits with b_g added; rows past nt_tok are ignored. WAVE: the
+// calling wave owns `rows` and its scratch (no workgroup barrier).
+template <bool WAVE = false>
+__device__ __forceinline__ void group_finish(const RouterArgs& a, float* rows, int LDE, int t0, int nt_tok, int grp) {
   const int lane = lane_id();
   const int E = a.E;
   float ent;
-  const uint64_t sel = quad_epilogue(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.noise, a.noise_std, a.key0, a.key1,
-                                     a.logits, a.scores, a.idx, a.w, a.idx_next, ent);
-  __syncthreads();
+  const uint64_t sel = quad_epilogue<WAVE>(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.noise, a.noise_std, a.key0,
+                                           a.key1, a.logits, a.scores, a.idx, a.w, a.idx_next, ent);
+  rows_sync<WAVE>();
   if (a.ent_part != nullptr) {               // the group's entropy sum, tokens in order
     __shared__ float ents[kWaves][kGroupTokens];
     float* en = ents[threadIdx.x >> 6];
     if ((lane & 3) == 0) en[lane >> 2] = ent;   // zero for tokens past nt_tok
-    __syncthreads();
+    rows_sync<WAVE>();
     if (lane == 0) {
       float sum = 0.0f;
 #pragma unroll
@@ -284,7 +304,7 @@ __device__ void group_finish(const RouterArgs& a, float* rows, int LDE, int t0, 
   __shared__ uint64_t masks[kWaves][kGroupTokens];
   uint64_t* mk = masks[threadIdx.x >> 6];
   if ((lane & 3) == 0) mk[lane >> 2] = sel;   // zero for tokens past nt_tok
-  __syncthreads();
+  rows_sync<WAVE>();
   if (lane < E) {
     int c = 0;
 #pragma unroll
@@ -393,6 +413,141 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a, float* _
   const int nt_w = min(kGroupTokens, nt_tok - wave * kGroupTokens);
   if (wave >= MT || nt_w <= 0) return;
   group_finish(a, rows + wave * kGroupTokens * LDE, LDE, t0 + wave * kGroupTokens, nt_w, blockIdx.x * MT + wave);
+}
+
+// Streaming bf16 router for many token groups. A persistent grid in which each wave owns whole
+// 16-token groups over all of d (wave slot s of S takes groups s, s + S, ...), so waves never
+// wait for one another. W_g is staged in LDS once per workgroup (E rows, row pitch 2d + 16
+// bytes, which spreads the 16 rows of a fragment read over the banks) and supplies every
+// group's B fragments, so only x streams from HBM. A wave's loads come in batches of NB chunks
+// of 64 along d, double-buffered: the next batch (the next group's first, after a group's
+// last) is issued before the current one is multiplied, which keeps the next group's rows in
+// flight during this group's epilogue. A lane's two 16-byte pieces of a chunk are k offsets
+// 8 g and 32 + 8 g (its lane group g): each load instruction reads 64 contiguous bytes of
+// each of 16 rows, and A and B use the same k order. Rows past the last token re-read the
+// last token; they only feed rows that are not kept.
+constexpr int kStreamWg = 68 * 1024;     // W_g bytes in LDS (two workgroups per CU)
+
+template <int NT, int NB, int WCAP>
+__global__ __launch_bounds__(256) void router_stream_kernel(RouterArgs a) {
+  constexpr int LDE = 16 * NT + 1;
+  __shared__ __attribute__((aligned(16))) char wlds[WCAP];
+  __shared__ float rows_all[kWaves][kGroupTokens * LDE];
+  const int wave = threadIdx.x >> 6, lane = lane_id();
+  const int d = a.d, E = a.E, T = a.T;
+  const int ng = (T + kGroupTokens - 1) / kGroupTokens;
+  const int pitch = 2 * d + 16;
+  const int nchunk = d / 64;
+  const int nbat = (nchunk + NB - 1) / NB;          // batches per group
+  const int S = gridDim.x * kWaves;
+  const int slot = blockIdx.x * kWaves + wave;
+  const int r16 = lane & 15, g = lane >> 4;
+  const u16* __restrict__ x = static_cast<const u16*>(a.x);
+  // the wave's batch q: group slot + (q / nbat) S, chunks [NB (q % nbat), ...); loads past the
+  // wave's last batch re-read it (the count of loads in flight stays the same every step)
+  const int my_groups = slot < ng ? (ng - 1 - slot) / S + 1 : 0;
+  const int nq = my_groups * nbat;
+  bf16x8 av[2][NB][2];
+  // buffers are chosen by compile-time constants (a runtime index would put av in scratch)
+  auto issue = [&](int q, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int qq = q < nq ? q : nq - 1;
+    const int grp = slot + (qq / nbat) * S, b = qq % nbat;
+    const int t = min(grp * kGroupTokens + r16, T - 1);
+    const u16* row = x + static_cast<size_t>(t) * d + 8 * g;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int c = min(b * NB + i, nchunk - 1);
+      av[buf][i][0] = *reinterpret_cast<const bf16x8*>(row + c * 64);
+      av[buf][i][1] = *reinterpret_cast<const bf16x8*>(row + c * 64 + 32);
+    }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (nq > 0) issue(0, B0{});
+  // stage W_g: 16-byte pieces, row e at e * pitch, eight loads in flight per thread
+  {
+    const int per_row = d / 8, n = E * per_row;
+    const u16* __restrict__ Wg = static_cast<const u16*>(a.Wg);
+    for (int i0 = threadIdx.x; i0 < n; i0 += 8 * 256) {
+      u32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + 256 * j;
+        if (i < n) {
+          const int e = i / per_row, c = i - e * per_row;
+          v[j] = *reinterpret_cast<const u32x4*>(Wg + static_cast<size_t>(e) * d + c * 8);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + 256 * j;
+        if (i < n) {
+          const int e = i / per_row, c = i - e * per_row;
+          *reinterpret_cast<u32x4*>(wlds + e * pitch + c * 16) = v[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (nq == 0) return;
+  // B fragment of tile n: row e = 16 n + r16 (zero past E), k offset 8 g (+ 32) in the chunk
+  int boff[NT];
+  bool bvalid[NT];
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    const int e = 16 * n + r16;
+    bvalid[n] = e < E;
+    boff[n] = (bvalid[n] ? e : 0) * pitch + 16 * g;
+  }
+  float* rows = rows_all[wave];
+  floatx4 acc[NT];
+  auto step = [&](int q, auto buf_c) {
+    constexpr int buf = decltype(buf_c)::value;
+    const int b = q % nbat;
+    if (b == 0) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int c = b * NB + i;
+      if (c < nchunk) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int n = 0; n < NT; ++n) {
+            const bf16x8 bv = bvalid[n] ? *reinterpret_cast<const bf16x8*>(wlds + boff[n] + c * 128 + 64 * h)
+                                        : bf16x8{};
+            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[buf][i][h], bv, acc[n], 0, 0, 0);
+          }
+      }
+    }
+    if (b == nbat - 1) {                     // the group's logits are complete: epilogue
+      const int grp = slot + (q / nbat) * S;
+      const int t0 = grp * kGroupTokens;
+      // C layout of a 16x16 tile: lane holds column r16, rows 4 g + i
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 16 * n + r16;
+          if (e < E) rows[(4 * g + i) * LDE + e] = acc[n][i] + (a.bg != nullptr ? a.bg[e] : 0.0f);
+        }
+      group_finish<true>(a, rows, LDE, t0, min(kGroupTokens, T - t0), grp);
+    }
+  };
+  int q = 0;
+  for (; q + 1 < nq; q += 2) {
+    issue(q + 1, B1{});
+    step(q, B0{});
+    issue(q + 2, B0{});
+    step(q + 1, B1{});
+  }
+  if (q < nq) {
+    issue(q + 1, B1{});                      // keeps the loads in flight uniform; unused
+    step(q, B0{});
+  }
 }
 
 // Sums the KS slice partials of one 16-token group in slice order (all 256 threads, every load
@@ -509,12 +664,37 @@ int router_slices(int T, int d, int E) {
   return ks < 1 ? 1 : (ks > kMaxSlices ? kMaxSlices : ks);
 }
 
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// The bytes of W_g in LDS with the streaming router's padded row pitch.
+static size_t stream_wg_bytes(const RouterArgs& a) { return static_cast<size_t>(a.E) * (2 * a.d + 16); }
+
 template <int NT>
 static hipError_t launch_router_bf16(const RouterArgs& a, float* zpart, hipStream_t stream) {
   // keep about 8 chunks' worth of operand registers per lane: 2 (x) + 2 NT (W_g) per chunk
   constexpr int NB = NT == 1 ? 8 : (NT == 2 ? 4 : 2);
   const int ng = (a.T + kGroupTokens - 1) / kGroupTokens;
   const int KS = router_slices(a.T, a.d, a.E);
+  const int cus = device_cus();
+  // W_g up to 68 KB (two workgroups per CU): measured 93 -> 79 us on 65536 tokens, d = 2048,
+  // E = 16. With one workgroup per CU (W_g up to 132 KB) it measured no faster than the
+  // per-group kernel below (16384 tokens, d = 1024, E = 64: 43 vs 46 us), so it is not used.
+  if (KS == 1 && ng >= 4 * cus && stream_wg_bytes(a) <= static_cast<size_t>(kStreamWg)) {
+    const int grid = min(2 * cus, (ng + kWaves - 1) / kWaves);
+    hipLaunchKernelGGL((router_stream_kernel<NT, 8, kStreamWg>), dim3(grid), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   if (KS == 1) {
     if constexpr (NT >= 3) {
       if (ng >= 4 * 256) {                   // large E and enough tokens: 64 tokens per workgroup

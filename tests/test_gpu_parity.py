@@ -56,6 +56,11 @@ SMALL = {
     # d_ffn = 8192: GEMM1 over 32 column panels with pair-staged A rows read through the
     # permutation, two row panels per expert
     "wide_ffn": (MoEShape("wide_ffn", T=600, d=128, E=3, k=2, d_ffn=8192, capacity_factor=1.0, wg_std=None), 0.05),
+    # the streaming router (W_g in LDS, waves owning whole 16-token groups): 2501 groups over
+    # 2048 wave slots, so some waves take two groups; a last group of 3 tokens; E = 12 pads the
+    # expert tile; Gumbel noise at tau = 0.6
+    "router_stream": (MoEShape("router_stream", T=40003, d=128, E=12, k=2, d_ffn=64, capacity_factor=1.0,
+                               temperature=0.6, gumbel=True, seed=11, wg_std=None), 0.1),
     # GEMM2 over K = 8192 (256 K steps) on 40 row tiles: each XCD's 5 tiles are split into 6 K
     # parts of 42 or 44 steps, pair-staged W2 rows ending exactly at the end of W2
     "split_p6": (MoEShape("split_p6", T=4800, d=256, E=8, k=2, d_ffn=8192, capacity_factor=1.25), 0.05),
