@@ -7,8 +7,9 @@
 One step is one moe_forward call (router + softmax + top-k, capacity dispatch, grouped expert
 GEMMs with GeLU, combine and the balance statistic) over one batch of seeded synthetic input
 already resident in HBM. Per workload: W untimed warm-up steps, then K cold-cache steps (each
-preceded by a 1 GiB write that evicts L2 and the 256 MB MALL, timed with HIP events recorded
-by moe_forward on its stream), then K warm steps back to back between two device
+preceded by a 1 GiB write that evicts L2 and the 256 MB MALL and a 512 MiB read that leaves
+them clean, timed with HIP events recorded by moe_forward on its stream), then K warm steps
+back to back between two device
 synchronisations. Prints one JSON line for the headline workload (the largest one by default):
   value          tokens/s of the whole layer from the median cold step (T tokens per step);
   warm           the back-to-back figures beside it;
@@ -49,6 +50,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 HEADLINE = "gumbel_longtail"
 OTHERS = "mixtral_like,switch_skew,decode,tiny_fp32"
 FLUSH_BYTES = 1 << 30
+SCRUB_BYTES = 1 << 29
 # default size of the CPU oracle's sample (tokens): about 10-30 s of host work
 CPU_SAMPLE = {"gumbel_longtail": 16384, "mixtral_like": 4096, "switch_skew": 16384, "decode": 128, "tiny_fp32": 256}
 
@@ -375,17 +377,21 @@ def measure_workload(shape, args, ops, torch, variant_args=None, capacity_factor
     for _ in range(args.warmup):
         plan.run()
     torch.cuda.synchronize()
-    # cold: each step follows a 1 GiB write (L2 and the MALL hold none of its inputs)
+    # cold: each step follows a 1 GiB write (L2 and the MALL hold none of its inputs), then a
+    # 512 MiB read, so that the write's dirty lines are written back before the step starts
+    # rather than during its first kernel
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda")
     events = [ops.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         flush.fill_(i & 255)
+        scrub.sum()
         plan.run(events=events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    del flush
+    del flush, scrub
     cold_stage = [ev.accumulate() for ev in events]
     for ev in events:
         ev.close()
@@ -591,7 +597,7 @@ def main() -> int:
                                    "route_stats": args.route_stats}} if head.with_variant else {})},
         "timing": {"headline": "median of the K cold-cache steps (HIP events around moe_forward)",
                    "cold_step_ms": head.cold_step_ms, "host_ms_per_cold_iteration_incl_flush": head.cold_host_ms,
-                   "flush_bytes": FLUSH_BYTES},
+                   "flush_bytes": FLUSH_BYTES, "scrub_read_bytes": SCRUB_BYTES},
         "warm": {"tokens_per_s": T / (head.warm_ms * 1e-3), "ms_per_step": head.warm_ms,
                  "stage_ms": head.warm_stage_mean},
         "roofline": roof,
