@@ -760,16 +760,20 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 // ---------------------------------------------------------------------------------------
 // bf16 grouped GEMV-like kernel for experts with at most 16 rows (decode-sized batches): the
 // weights are streamed from HBM exactly once, straight into v_mfma_f32_16x16x32_bf16 operands.
-// Workgroup = one expert x 128 output columns; each wave owns 2 tiles of 16 columns over the
-// full K. K goes in chunks of 64: lane group g (16 lanes) takes elements [kc + 16 g, kc + 16 g
-// + 16) of its row as two 8-element pieces, and MFMA step i takes piece i of both operands (the
-// k order of A and B agrees); each load instruction then covers 16 rows x 64 bytes. GV_BATCH
-// chunks of loads are issued ahead of their MFMAs. Rows past the expert's segment are read
-// from its last row: they only feed output rows that are never stored.
-constexpr int GV_COLS = 128, GV_BATCH = 4;
+// Workgroup = one expert x GV_COLS output columns (two 16-column tiles); its 4 waves split K
+// into 4 contiguous ranges of 64-element chunks, so each wave's chain of dependent loads is a
+// quarter of the row and four times as many workgroups share the stream. Within a chunk, lane
+// group g (16 lanes) takes elements [16 g, 16 g + 16) of its row as two 8-element pieces, and
+// MFMA step i takes piece i of both operands (the k order of A and B agrees); each load
+// instruction covers 16 rows x 64 bytes. A wave issues the loads of GV_BATCH chunks before their
+// MFMAs. The four partial tiles are added in wave order through LDS (a fixed order), and wave 0
+// applies the epilogue. Rows past the expert's segment are read from its last row: they only
+// feed output rows that are never stored.
+constexpr int GV_COLS = 32, GV_BATCH = 4;
 
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
+  __shared__ floatx4 part[kWaves][2][kWave];
   const int nblk_n = (g.N + GV_COLS - 1) / GV_COLS;
   const int e = blockIdx.x / nblk_n, nb = blockIdx.x - e * nblk_n;
   const int m_e = segment_rows(g, e);
@@ -778,7 +782,7 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
   const int N = g.N, K = g.K;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, grp = lane >> 4;
-  const int nbase = nb * GV_COLS + wave * 32;
+  const int nbase = nb * GV_COLS;
   const int ar = row0 + (r16 < m_e ? r16 : m_e - 1);
   const u16* __restrict__ ap = static_cast<const u16*>(g.A) +
                                static_cast<size_t>(g.rows != nullptr ? g.rows[ar] : ar) * K + 16 * grp;
@@ -794,38 +798,70 @@ __global__ __launch_bounds__(256) void grouped_gemv_bf16_kernel(GemmArgs g) {
                              (n % 256) * 32 + 16 * (grp & 1)
                        : (static_cast<size_t>(e) * N + n) * K + 16 * grp);
   }
+  // this wave's chunks of 64: [c0, c1)
+  const int nch = K / 64;
+  const int c0 = nch * wave / kWaves, c1 = nch * (wave + 1) / kWaves;
   floatx4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  int kc = 0;
-  for (; kc + GV_BATCH * 64 <= K; kc += GV_BATCH * 64) {
+  int c = c0;
+  for (; c + GV_BATCH <= c1; c += GV_BATCH) {
     bf16x8 a[GV_BATCH][2], b[GV_BATCH][2][2];
 #pragma unroll
-    for (int c = 0; c < GV_BATCH; ++c) {
+    for (int i = 0; i < GV_BATCH; ++i) {
+      const size_t kc = static_cast<size_t>(c + i) * 64;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        b[c][t][0] = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc + c * 64) * kstep);
-        b[c][t][1] = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc + c * 64) * kstep + 8);
+        b[i][t][0] = *reinterpret_cast<const bf16x8*>(bp[t] + kc * kstep);
+        b[i][t][1] = *reinterpret_cast<const bf16x8*>(bp[t] + kc * kstep + 8);
       }
-      a[c][0] = *reinterpret_cast<const bf16x8*>(ap + kc + c * 64);
-      a[c][1] = *reinterpret_cast<const bf16x8*>(ap + kc + c * 64 + 8);
+      a[i][0] = *reinterpret_cast<const bf16x8*>(ap + kc);
+      a[i][1] = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
     }
 #pragma unroll
-    for (int c = 0; c < GV_BATCH; ++c)
+    for (int i = 0; i < GV_BATCH; ++i)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][0], b[c][t][0], acc[t], 0, 0, 0);
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c][1], b[c][t][1], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][0], b[i][t][0], acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][1], b[i][t][1], acc[t], 0, 0, 0);
       }
   }
-  for (; kc < K; kc += 64) {
-    const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap + kc);
-    const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
+  if (c < c1) {                              // the last 1..GV_BATCH-1 chunks, loads all issued first
+    bf16x8 a[GV_BATCH - 1][2], b[GV_BATCH - 1][2][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc) * kstep);
-      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(bp[t] + static_cast<size_t>(kc) * kstep + 8);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[t], 0, 0, 0);
-      acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[t], 0, 0, 0);
+    for (int i = 0; i < GV_BATCH - 1; ++i) {
+      if (c + i < c1) {
+        const size_t kc = static_cast<size_t>(c + i) * 64;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          b[i][t][0] = *reinterpret_cast<const bf16x8*>(bp[t] + kc * kstep);
+          b[i][t][1] = *reinterpret_cast<const bf16x8*>(bp[t] + kc * kstep + 8);
+        }
+        a[i][0] = *reinterpret_cast<const bf16x8*>(ap + kc);
+        a[i][1] = *reinterpret_cast<const bf16x8*>(ap + kc + 8);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < GV_BATCH - 1; ++i)
+      if (c + i < c1)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][0], b[i][t][0], acc[t], 0, 0, 0);
+          acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i][1], b[i][t][1], acc[t], 0, 0, 0);
+        }
+  }
+  part[wave][0][lane] = acc[0];
+  part[wave][1][lane] = acc[1];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {              // partial sums added in wave order
+    floatx4 v = part[0][t][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const floatx4 o = part[w][t][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += o[i];
+    }
+    acc[t] = v;
   }
   // C layout of the 16x16 tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
 #pragma unroll
