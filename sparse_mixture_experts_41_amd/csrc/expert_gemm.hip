@@ -161,7 +161,8 @@ __device__ __forceinline__ TileScan scan_tiles(const GemmArgs& g, int BM, int ti
 }
 
 // Tile t < total -> (e, mt, nt, mbase) and e's segment rows. Experts come in order, each
-// expert's tiles in the order of plan::tile_in_expert (column tiles outer, row tiles inner).
+// expert's tiles in the order of plan::tile_in_expert (blocks of 4 column tiles, row tiles outer
+// and column tiles inner within a block).
 __device__ __forceinline__ void locate_tile(const TileScan& s, int tile, int tiles_n, int& e, int& mt, int& nt,
                                             int& mbase, int& m_e) {
   const unsigned long long past = __ballot(s.cnt_incl > tile);

@@ -2,8 +2,15 @@
 // workgroup of a launch takes. Plain integer arithmetic with no HIP dependence, compiled into
 // the kernels and, on the host, into the CPU test that enumerates it.
 //
-// Order. Experts come in order; within an expert, column tiles are outermost and row tiles
-// innermost, so the workgroups that share one weight panel are adjacent.
+// Order. Experts come in order; within an expert, the column tiles form blocks of kColBlock
+// (the last block may be narrower), blocks come in order, and inside a block the row tiles are
+// outer and its column tiles inner. A bundle of kBundle = 16 consecutive tiles then covers 4 row
+// tiles x 4 column tiles: 4 row panels and 4 weight panels for 16 tiles, where column tiles
+// outermost (16 row tiles of one weight panel) needed 17. Measured on MI355X against that order:
+// the GEMMs' L2 misses (FETCH_SIZE) fell from 8.0 / 8.6 GB to 4.8 / 4.8 GB per launch on the
+// long-tail layer (65536 tokens, d 2048, d_ffn 8192), and its GEMM1 and GEMM2 ran 2.2% and 2.7%
+// faster (Mixtral-like layer unchanged, switch-style -1%); blocks of 2 columns timed the same
+// and blocks of 8 about 1% slower.
 //
 // Placement. The hardware hands workgroup b to XCD (b mod 8). Workgroups are renumbered so that
 // each XCD takes bundles of kBundle consecutive tiles (tiles that share an expert's operand
@@ -39,10 +46,20 @@ constexpr int kSideSlots = 255;   // side tiles a split tail can need: L (P - 1)
 MOE_PLAN_FN int imin(int a, int b) { return a < b ? a : b; }
 
 // Tile t (0 <= t < tm * tn) of one expert with tm row tiles and tn column tiles -> (mt, nt).
+constexpr int kColBlock = 4;
+
 MOE_PLAN_FN void tile_in_expert(int t, int tm, int tn, int& mt, int& nt) {
-  (void)tn;
-  nt = t / tm;
-  mt = t - nt * tm;
+  const int full = tn / kColBlock * kColBlock;     // column tiles in whole blocks
+  const int span = tm * kColBlock;                 // tiles of one whole block
+  if (t < full * tm) {
+    const int cb = t / span, r = t - cb * span;
+    mt = r / kColBlock;
+    nt = cb * kColBlock + (r - mt * kColBlock);
+  } else {                                         // the last block: tn - full columns
+    const int rest = tn - full, r = t - full * tm;
+    mt = r / rest;
+    nt = full + (r - mt * rest);
+  }
 }
 
 // Workgroup b -> its position in the tile order (bundles of kBundle, round-robin over XCDs).

@@ -12,7 +12,9 @@
 //   * K parts tile [0, nk) in order; with an even nk (the bf16 MFMA path) each part starts on
 //     an even step and has an even length, at least 4 steps when split (so a pair load never
 //     reaches past its part);
-//   * tile_in_expert is a bijection onto the tm x tn tiles of an expert.
+//   * tile_in_expert is a bijection onto the tm x tn tiles of an expert, and inside the whole
+//     blocks of kColBlock column tiles each run of kColBlock consecutive tiles is one row tile
+//     over consecutive column tiles.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -116,6 +118,11 @@ int main() {
         tile_in_expert(t, tm, tn, mt, nt);
         if (mt < 0 || mt >= tm || nt < 0 || nt >= tn) return fail("tile_in_expert range", tm, tn, t, mt);
         if (hit[static_cast<size_t>(mt) * tn + nt]++) return fail("tile_in_expert twice", tm, tn, mt, nt);
+        if (t < tn / kColBlock * kColBlock * tm && t % kColBlock > 0) {
+          int mp = -1, np = -1;
+          tile_in_expert(t - 1, tm, tn, mp, np);
+          if (mp != mt || np + 1 != nt) return fail("tile_in_expert block", tm, tn, t, mt);
+        }
       }
     }
   std::printf("ok\n");
