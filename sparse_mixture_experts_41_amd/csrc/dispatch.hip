@@ -5,10 +5,13 @@
 // token index), counted per expert, and each expert keeps only the first C = ceil(c k T / E)
 // of its slots; the rest are dropped and contribute nothing. The page's version sorts the
 // slots; here the same order comes from a counting sort that needs no sort at all:
-//   per-group histograms (16 tokens per group, written by the router or by the histogram
-//   kernel) -> a one-workgroup scan giving, for every (group, expert), the number of earlier
-//   slots of that expert -> a slot's rank among its expert's slots is that base plus the
-//   number of lower lanes of its 16-lane group that chose the same expert (wave ballot).
+//   per-group histograms (kGroupTokens = 16 tokens per group, written by the router or by the
+//   histogram kernel) -> a scan giving, for every (group, expert), the number of earlier
+//   slots of that expert (one workgroup; for many groups two levels: one wave per chunk of
+//   kScanChunk groups writes the bases within its chunk and the chunk's totals, then one
+//   workgroup scans the chunk totals) ->
+//   a slot's rank among its expert's slots is its group's base plus the number of lower lanes
+//   of its 16-lane group that chose the same expert (wave ballot).
 // A token never picks an expert twice, so ranks are unique and the result is bit-exact.
 #include "moe_common.h"
 #include "moe_kernels.h"
@@ -18,6 +21,39 @@ namespace moe {
 namespace {
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanChunk = 16;               // groups per chunk of the two-level scan
+
+// The bases buffer of a scan, scan_bases_ints(ng, E) 4-byte entries, nc = ceil(ng / kScanChunk):
+//   [0, ng E)            group bases: slots of the expert in earlier groups of the same chunk
+//   [ng E, +nc E)        chunk bases: slots of the expert in earlier chunks
+//   [+nc E)              slots per (chunk, expert); [+nc E) float probability sums per
+//                        (chunk, expert); [+nc) float entropy sums per chunk
+// The base of (group, expert) is its group base plus its chunk's base (group_base).
+struct ScanRegion {
+  int32_t* gbase;
+  int32_t* cbase;
+  int32_t* ctot;
+  float* cps;
+  float* cent;
+  int nc;
+};
+
+__host__ __device__ inline ScanRegion scan_region(int32_t* bb, int ng, int E) {
+  ScanRegion r;
+  r.nc = (ng + kScanChunk - 1) / kScanChunk;
+  const size_t ge = static_cast<size_t>(ng) * E, ce = static_cast<size_t>(r.nc) * E;
+  r.gbase = bb;
+  r.cbase = bb + ge;
+  r.ctot = bb + ge + ce;
+  r.cps = reinterpret_cast<float*>(bb + ge + 2 * ce);
+  r.cent = reinterpret_cast<float*>(bb + ge + 3 * ce);
+  return r;
+}
+
+__device__ __forceinline__ int group_base(const int32_t* __restrict__ bb, int ng, int E, int grp, int e) {
+  return bb[static_cast<size_t>(grp) * E + e] +
+         bb[static_cast<size_t>(ng) * E + static_cast<size_t>(grp / kScanChunk) * E + e];
+}
 
 __device__ __forceinline__ int pow2_at_least(int v) {
   int p = 1;
@@ -138,8 +174,72 @@ __device__ void write_route_stats(const int* tot, int E, int T, float ent_sum, f
   }
 }
 
+// First level of the scan: wave c takes the groups [c kScanChunk, +kScanChunk), lane e expert
+// e. All of the lane's histogram entries (and probability partials, entropy partials) are
+// loaded before any is used; the group bases within the chunk are the running sums in
+// ascending group order, and the chunk's float sums add the groups in that order too. hist may
+// be null (probability sums only), as may psum and ent.
+__global__ __launch_bounds__(kWave) void scan_chunks_kernel(const int32_t* __restrict__ hist,
+                                                            const float* __restrict__ psum,
+                                                            const float* __restrict__ ent, int ng, int E,
+                                                            int32_t* __restrict__ bb) {
+  const ScanRegion r = scan_region(bb, ng, E);
+  const int c = blockIdx.x, lane = threadIdx.x;
+  const int g0 = c * kScanChunk, n = min(kScanChunk, ng - g0);
+  if (lane < E) {
+    // unconditional loads at clamped rows, issued back to back; rows past n are not used
+    int h[kScanChunk];
+    float p[kScanChunk];
+    if (hist != nullptr) {
+#pragma unroll
+      for (int u = 0; u < kScanChunk; ++u) h[u] = hist[static_cast<size_t>(g0 + min(u, n - 1)) * E + lane];
+    }
+    if (psum != nullptr) {
+#pragma unroll
+      for (int u = 0; u < kScanChunk; ++u) p[u] = psum[static_cast<size_t>(g0 + min(u, n - 1)) * E + lane];
+    }
+    if (hist != nullptr) {
+      int run = 0;
+#pragma unroll
+      for (int u = 0; u < kScanChunk; ++u)
+        if (u < n) {
+          r.gbase[static_cast<size_t>(g0 + u) * E + lane] = run;
+          run += h[u];
+        }
+      r.ctot[static_cast<size_t>(c) * E + lane] = run;
+    }
+    if (psum != nullptr) {
+      float s = 0.0f;
+#pragma unroll
+      for (int u = 0; u < kScanChunk; ++u)
+        if (u < n) s += p[u];
+      r.cps[static_cast<size_t>(c) * E + lane] = s;
+    }
+  }
+  if (ent != nullptr && lane == 0) {
+    float q[kScanChunk];
+#pragma unroll
+    for (int u = 0; u < kScanChunk; ++u) q[u] = ent[g0 + min(u, n - 1)];
+    float s = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kScanChunk; ++u)
+      if (u < n) s += q[u];
+    r.cent[c] = s;
+  }
+}
+
 // Counts, capacity truncation, expert offsets and the per-(group, expert) base ranks, plus the
-// balance statistics when the probability partials are given. One workgroup.
+// balance statistics when the probability partials are given. One workgroup: thread (g, e)
+// takes expert e over the contiguous run of `chunk` groups of thread group g. With R > 0
+// (chunk <= R <= kScanRegs, R a power of two, chosen by the launcher) all of a thread's R
+// histogram entries and probability partials are loaded at once into registers: the kernel
+// then makes one round trip to memory, where the general path (R = 0) makes one per batch of
+// 8 and per pass (histogram, bases, probability partials). Both paths add every float in the
+// same order (a thread's run in ascending groups, then a pairwise tree over the thread
+// groups), so the statistics do not depend on the path.
+constexpr int kScanRegs = 16;
+
+template <int R>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __shared__ int ilds[kScanThreads];
   __shared__ float flds[kScanThreads];
@@ -152,46 +252,90 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   const int chunk = (ng + G - 1) / G;
   const int e = threadIdx.x % E2, g = threadIdx.x / E2;
   const int b0 = g * chunk, b1 = min(ng, b0 + chunk);
+  const bool stats = a.probsum_part != nullptr && !a.bases_only;   // uniform
+  constexpr bool in_regs = R > 0;
+  constexpr int NR = R > 0 ? R : 1;
+  int v[NR];
   int s = 0;
-  if (e < E) {
+  float ps = 0.0f;
+  if (in_regs && ng > 0) {
+    // unconditional loads at clamped (in-bounds) positions, issued back to back; entries past
+    // the thread's run or past E are zeroed afterwards
+    float p[NR];
+    const int ec = e < E ? e : E - 1;
+#pragma unroll
+    for (int u = 0; u < NR; ++u) v[u] = a.hist[static_cast<size_t>(min(b0 + u, ng - 1)) * E + ec];
+    if (stats) {
+#pragma unroll
+      for (int u = 0; u < NR; ++u) p[u] = a.probsum_part[static_cast<size_t>(min(b0 + u, ng - 1)) * E + ec];
+    }
+#pragma unroll
+    for (int u = 0; u < NR; ++u) {
+      v[u] = (e < E && b0 + u < b1) ? v[u] : 0;
+      s += v[u];
+    }
+    if (stats) {
+#pragma unroll
+      for (int u = 0; u < NR; ++u)
+        if (e < E && b0 + u < b1) ps += p[u];
+    }
+  } else if (!in_regs && e < E) {
     int b = b0;
     for (; b + 8 <= b1; b += 8) {            // eight independent loads in flight, added in order
-      int v[8];
+      int w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.hist[static_cast<size_t>(b + u) * E + e];
+      for (int u = 0; u < 8; ++u) w[u] = a.hist[static_cast<size_t>(b + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 8; ++u) s += w[u];
     }
     for (; b < b1; ++b) s += a.hist[static_cast<size_t>(b) * E + e];
   }
   ilds[threadIdx.x] = s;
+  if (in_regs && stats) flds[threadIdx.x] = ps;
   __syncthreads();
   for (int off = 1; off < G; off <<= 1) {    // inclusive scan over the thread groups
-    const int v = g >= off ? ilds[threadIdx.x - off * E2] : 0;
+    const int x = g >= off ? ilds[threadIdx.x - off * E2] : 0;
     __syncthreads();
-    ilds[threadIdx.x] += v;
+    ilds[threadIdx.x] += x;
     __syncthreads();
+  }
+  if (in_regs && stats) {                    // column sums: pairwise tree over the thread groups
+    for (int h = G >> 1; h > 0; h >>= 1) {   // G is a power of two
+      if (g < h) flds[threadIdx.x] += flds[threadIdx.x + h * E2];
+      __syncthreads();
+    }
+    if (g == 0 && e < E) csum[e] = flds[e];
   }
   if (e < E) {
     const int pre = ilds[threadIdx.x] - s;
     if (g == G - 1) tot[e] = pre + s;
     int run = pre;
-    int b = b0;
-    for (; b + 8 <= b1; b += 8) {
-      int v[8];
+    if (in_regs) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.hist[static_cast<size_t>(b + u) * E + e];
+      for (int u = 0; u < NR; ++u)
+        if (b0 + u < b1) {
+          a.blockbase[static_cast<size_t>(b0 + u) * E + e] = run;
+          run += v[u];
+        }
+    } else {
+      int b = b0;
+      for (; b + 8 <= b1; b += 8) {
+        int w[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a.blockbase[static_cast<size_t>(b + u) * E + e] = run;
-        run += v[u];
+        for (int u = 0; u < 8; ++u) w[u] = a.hist[static_cast<size_t>(b + u) * E + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          a.blockbase[static_cast<size_t>(b + u) * E + e] = run;
+          run += w[u];
+        }
+      }
+      for (; b < b1; ++b) {
+        a.blockbase[static_cast<size_t>(b) * E + e] = run;
+        run += a.hist[static_cast<size_t>(b) * E + e];
       }
     }
-    for (; b < b1; ++b) {
-      a.blockbase[static_cast<size_t>(b) * E + e] = run;
-      run += a.hist[static_cast<size_t>(b) * E + e];
-    }
   }
+  for (int i = threadIdx.x; i < a.zero_n; i += kScanThreads) a.zero_bases[i] = 0;
   __syncthreads();
   if (a.bases_only) return;                  // uniform over the workgroup
   if (threadIdx.x < kWave) {                 // wave 0: one expert per lane, exclusive scan of kept
@@ -212,8 +356,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
       a.offsets[ee] = incl - kp;
     }
   }
-  if (a.probsum_part != nullptr) {
-    blocked_colsum(a.probsum_part, ng, E, csum, flds);   // contains __syncthreads
+  if (stats) {
+    if (!in_regs) blocked_colsum(a.probsum_part, ng, E, csum, flds);   // contains __syncthreads
     if (threadIdx.x < E) a.colsum[threadIdx.x] = csum[threadIdx.x];
     write_stats(tot, csum, E, a.k, a.T, a.f, a.P, a.L, prod);
   }
@@ -282,7 +426,7 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
   if (!valid) return;
   const uint64_t below = (1ull << lane) - 1ull;
   const uint64_t gmask = 0xFFFFull << (lane & ~(kGroupTokens - 1));   // this lane's 16-lane group
-  const int grp = t / kGroupTokens;
+  const int grp = t / kGroupTokens, ng = (T + kGroupTokens - 1) / kGroupTokens;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
     if (j < k) {
@@ -291,7 +435,7 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
         dest[static_cast<size_t>(t) * k + j] = -1;
         continue;
       }
-      const int r = blockbase[static_cast<size_t>(grp) * E + e] + __popcll(emask[e] & below & gmask);
+      const int r = group_base(blockbase, ng, E, grp, e) + __popcll(emask[e] & below & gmask);
       int dst = -1;
       if (r < C) {
         dst = offsets[e] + r;
@@ -456,7 +600,7 @@ __global__ __launch_bounds__(64) void reroute_rank_kernel(const int32_t* __restr
       const int e = ch[j];
       int c = -1;
       if (e >= 0) {
-        const int r = blockbase1[static_cast<size_t>(grp) * E + e] + __popcll(emask[e] & below & gmask);
+        const int r = group_base(blockbase1, ng, E, grp, e) + __popcll(emask[e] & below & gmask);
         if (r >= C) {
           const int e2 = idx_next[static_cast<size_t>(t) * k + m];
           ++m;
@@ -522,7 +666,7 @@ __global__ __launch_bounds__(64) void permute_reroute_kernel(
   if (!valid) return;
   const uint64_t below = (1ull << lane) - 1ull;
   const uint64_t gmask = 0xFFFFull << (lane & ~(kGroupTokens - 1));
-  const int grp = t / kGroupTokens;
+  const int grp = t / kGroupTokens, ng = (T + kGroupTokens - 1) / kGroupTokens;
   bool moved = false;
 #pragma unroll
   for (int j = 0; j < kMaxK; ++j) {
@@ -531,12 +675,12 @@ __global__ __launch_bounds__(64) void permute_reroute_kernel(
       if (cd[j] >= 0) {
         const int e2 = cd[j];
         moved = true;
-        const int r2 = blockbase2[static_cast<size_t>(grp) * E + e2] + __popcll(emask2[e2] & below & gmask);
+        const int r2 = group_base(blockbase2, ng, E, grp, e2) + __popcll(emask2[e2] & below & gmask);
         const int k1 = kept1[e2];
         if (r2 < C - k1) dst = offsets[e2] + k1 + r2;
       } else if (ch[j] >= 0) {
         const int e = ch[j];
-        const int r = blockbase1[static_cast<size_t>(grp) * E + e] + __popcll(emask[e] & below & gmask);
+        const int r = group_base(blockbase1, ng, E, grp, e) + __popcll(emask[e] & below & gmask);
         if (r < C) dst = offsets[e] + r;
       }
       if (dst >= 0) perm[dst] = t;
@@ -586,14 +730,84 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint8_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_colsum(const float* part, int ng, int E, float* out, hipStream_t stream) {
-  hipLaunchKernelGGL(colsum_kernel, dim3(1), dim3(kScanThreads), 0, stream, part, ng, E, out);
+// Whether a scan over ng groups takes two levels: when one workgroup's threads would hold more
+// than kScanRegs groups each (more than 1024 groups for 16 experts, 256 for 64). There the
+// single workgroup makes one round trip to memory per batch of 8 groups and per pass, which
+// costs more than a second launch (measured on MI355X: 4096 groups of 16 experts 22.6 ->
+// 16.9 us, 1024 groups of 64 experts 20.7 -> 16.1 us; at 256 groups of 8 experts the second
+// launch made it 10 -> 17 us). With one level the scan writes absolute group bases and zero
+// chunk bases.
+static int scan_run(int ng, int E) {         // groups per thread of the one-workgroup scan
+  int e2 = 1;
+  while (e2 < E) e2 <<= 1;
+  const int G = kScanThreads / e2;
+  return (ng + G - 1) / G;
+}
+
+static bool scan_two_level(int ng, int E) { return scan_run(ng, E) > kScanRegs; }
+
+// scan_kernel with the smallest R that holds a thread's run (0: the general path).
+static hipError_t launch_scan_kernel(const ScanArgs& a, hipStream_t stream) {
+  const int run = scan_run(a.ng, a.E);
+  const dim3 g(1), b(kScanThreads);
+  if (run <= 1)
+    hipLaunchKernelGGL(scan_kernel<1>, g, b, 0, stream, a);
+  else if (run <= 2)
+    hipLaunchKernelGGL(scan_kernel<2>, g, b, 0, stream, a);
+  else if (run <= 4)
+    hipLaunchKernelGGL(scan_kernel<4>, g, b, 0, stream, a);
+  else if (run <= 8)
+    hipLaunchKernelGGL(scan_kernel<8>, g, b, 0, stream, a);
+  else if (run <= kScanRegs)
+    hipLaunchKernelGGL(scan_kernel<kScanRegs>, g, b, 0, stream, a);
+  else
+    hipLaunchKernelGGL(scan_kernel<0>, g, b, 0, stream, a);
+  return hipGetLastError();
+}
+
+size_t scan_bases_ints(int ng, int E) {
+  const size_t nc = (static_cast<size_t>(ng) + kScanChunk - 1) / kScanChunk;
+  return static_cast<size_t>(ng) * E + 3 * nc * E + nc;
+}
+
+// The same two-level order as the scan's probability sums: per chunk, then over the chunks.
+hipError_t launch_colsum(const float* part, int ng, int E, int32_t* bases, float* out, hipStream_t stream) {
+  if (!scan_two_level(ng, E)) {
+    hipLaunchKernelGGL(colsum_kernel, dim3(1), dim3(kScanThreads), 0, stream, part, ng, E, out);
+    return hipGetLastError();
+  }
+  const ScanRegion r = scan_region(bases, ng, E);
+  hipLaunchKernelGGL(scan_chunks_kernel, dim3(r.nc), dim3(kWave), 0, stream, nullptr, part, nullptr, ng, E, bases);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(colsum_kernel, dim3(1), dim3(kScanThreads), 0, stream, r.cps, r.nc, E, out);
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a);
-  return hipGetLastError();
+  const ScanRegion r = scan_region(a.blockbase, a.ng, a.E);
+  if (!scan_two_level(a.ng, a.E)) {
+    ScanArgs b = a;
+    b.zero_bases = r.cbase;
+    b.zero_n = r.nc * a.E;
+    return launch_scan_kernel(b, stream);
+  }
+  const bool stats = a.probsum_part != nullptr && !a.bases_only;
+  hipLaunchKernelGGL(scan_chunks_kernel, dim3(r.nc), dim3(kWave), 0, stream, a.hist,
+                     stats ? a.probsum_part : nullptr, a.route_stats != nullptr ? a.ent_part : nullptr, a.ng, a.E,
+                     a.blockbase);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // second level: the same scan over the chunk totals, its bases the chunk bases
+  ScanArgs b = a;
+  b.zero_bases = nullptr;
+  b.zero_n = 0;
+  b.hist = r.ctot;
+  b.ng = r.nc;
+  b.blockbase = r.cbase;
+  b.probsum_part = stats ? r.cps : nullptr;
+  b.ent_part = a.route_stats != nullptr ? r.cent : nullptr;
+  return launch_scan_kernel(b, stream);
 }
 
 hipError_t launch_stats(const int32_t* counts, const float* colsum, int E, int k, int T, float* f, float* P,

@@ -172,7 +172,7 @@ Layout layout_of(const Derived& D) {
   const size_t T = D.T, E = D.E, k = D.k, ng = D.ng, R = D.R;
   L.probsum = take(ng * E * 4);
   L.hist = take(ng * E * 4);
-  L.blockbase = take(ng * E * 4);
+  L.blockbase = take(moe::scan_bases_ints(static_cast<int>(ng), static_cast<int>(E)) * 4);
   L.colsum = take(E * 4);
   const int ks = D.bf16 ? moe::router_slices(D.T, D.d, D.E) : 1;
   L.zpart = take(ks > 1 ? static_cast<size_t>(ks) * T * E * 4 : 0);
@@ -194,7 +194,7 @@ Layout layout_of(const Derived& D) {
   L.idx_next = take(reroute ? T * k * 4 : 0);
   L.cand = take(reroute ? T * k * 4 : 0);
   L.hist2 = take(random || reroute ? ng * E * 4 : 0);
-  L.blockbase2 = take(random || reroute ? ng * E * 4 : 0);
+  L.blockbase2 = take(random || reroute ? moe::scan_bases_ints(static_cast<int>(ng), static_cast<int>(E)) * 4 : 0);
   L.kept1 = take(reroute ? E * 4 : 0);
   L.thresh = take(random ? E * 8 : 0);
   const size_t d = D.d, dff = D.dff, es = D.esize;
@@ -349,7 +349,8 @@ moe_status moe_route(const moe_config* cfg, const void* x, const void* Wg, const
   const moe::RouterArgs a = router_args(D, x, Wg, bg, logits, scores, topk_idx, topk_w, at<float>(ws, L.probsum),
                                         at<int32_t>(ws, L.hist));
   MOE_HIP(moe::launch_router(a, at<float>(ws, L.zpart), st), "router");
-  MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.ng, D.E, prob_colsum, st), "colsum");
+  MOE_HIP(moe::launch_colsum(at<float>(ws, L.probsum), D.ng, D.E, at<int32_t>(ws, L.blockbase), prob_colsum, st),
+          "colsum");
   return MOE_OK;
 }
 

@@ -38,8 +38,11 @@ hipError_t launch_router(const RouterArgs& a, float* zpart, hipStream_t stream);
 // Per-group expert histogram of top-k indices ([ng,E], 16 tokens per group).
 hipError_t launch_histogram(const int32_t* idx, int T, int E, int k, int32_t* hist, hipStream_t stream);
 
-// Fixed-order column sums of per-group partials [ng,E] -> [E].
-hipError_t launch_colsum(const float* part, int ng, int E, float* out, hipStream_t stream);
+// Column sums of part [ng,E] in the order of the scan's probability sums; `bases` is a scan
+// bases buffer of scan_bases_ints(ng, E) entries, used as scratch.
+hipError_t launch_colsum(const float* part, int ng, int E, int32_t* bases, float* out, hipStream_t stream);
+// 4-byte entries of a scan's bases buffer (group bases, then the chunk level of the scan).
+size_t scan_bases_ints(int ng, int E);
 
 struct ScanArgs {
   const int32_t* hist;    // [ng,E]
@@ -48,7 +51,7 @@ struct ScanArgs {
   int32_t* counts;        // [E]
   int32_t* kept;          // [E]
   int32_t* offsets;       // [E]
-  int32_t* blockbase;     // [ng,E] earlier slots of each expert before each group
+  int32_t* blockbase;     // [scan_bases_ints(ng,E)] bases buffer: earlier slots of each expert before each group
   // optional statistics (all null or all set)
   const float* probsum_part;  // [ng,E]
   float* colsum;          // [E]
@@ -62,6 +65,10 @@ struct ScanArgs {
   // routing statistics (both null or both set): ent_part [ng] -> route_stats [MOE_ROUTE_STATS]
   const float* ent_part;
   float* route_stats;
+  // set by launch_scan: zero_n entries at zero_bases are cleared (the chunk bases of a
+  // one-level scan)
+  int32_t* zero_bases;
+  int zero_n;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
 

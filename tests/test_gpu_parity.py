@@ -89,11 +89,21 @@ def test_exact_ties_route_to_lowest_index():
     check_forward_full(p, gpu)
 
 
-def test_stages_match_forward_and_oracle():
+STAGE_SHAPES = {
+    "one_level_scan": MoEShape("stages", T=900, d=128, E=6, k=2, d_ffn=256, capacity_factor=0.8, temperature=0.8,
+                               gumbel=True, seed=99),
+    # 313 groups of 64 experts: the scan and the route stage's column sums take two levels
+    "two_level_scan": MoEShape("stages2", T=5000, d=64, E=64, k=2, d_ffn=64, capacity_factor=0.8, temperature=0.8,
+                               gumbel=True, seed=98, wg_std=None),
+}
+
+
+@pytest.mark.parametrize("which", sorted(STAGE_SHAPES))
+def test_stages_match_forward_and_oracle(which):
     """moe_route -> moe_dispatch -> moe_expert_ffn -> moe_combine: bitwise equal to moe_forward,
     and each stage checked against the oracle on its own inputs."""
-    shape = MoEShape("stages", T=900, d=128, E=6, k=2, d_ffn=256, capacity_factor=0.8, temperature=0.8,
-                     gumbel=True, seed=99)
+    shape = STAGE_SHAPES[which]
+    print(f"[gpu] stages {which} {shape}", flush=True)
     p = Problem(shape, bias_std=0.05)
     cfg = p.cfg
     x, Wg, bg, W1, b1, W2, b2 = p.args()

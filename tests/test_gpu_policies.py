@@ -7,7 +7,8 @@ the final experts when rerouting) and outputs to the tolerances of tests/parity.
 the MFMA GEMM, GEMV and float32 expert paths, all four router kernels (one-kernel 16-token,
 K-sliced, 64-token wide, float32), ragged token counts, heavy skew (one expert far over
 capacity), k = E (no next expert), k = 8 of 64 experts, noise and temperature (scores differ
-from logits), and the full-size layers on sampled rows.
+from logits), token counts that take the scan's two-level path, and the full-size layers on
+sampled rows.
 """
 import numpy as np
 import pytest
@@ -47,6 +48,14 @@ CASES = {
                               seed=5, wg_std=None), 0.0, "token", True, 0.0),
     "stats_f32": (S("stats_f32", T=256, d=128, E=4, k=2, d_ffn=512, capacity_factor=1.25, dtype="f32"), 0.0,
                   "token", True, 0.0),
+    # enough 16-token groups for the two-level scan (more than 256 groups of 64 experts, 1024 of
+    # 16), with a ragged last chunk
+    "random_two_level": (S("random_two_level", T=5000, d=64, E=64, k=2, d_ffn=64, capacity_factor=0.8,
+                           wg_std=None, seed=11), 0.05, "random", True, 0.0),
+    "reroute_two_level": (S("reroute_two_level", T=5000, d=64, E=64, k=2, d_ffn=64, capacity_factor=0.7,
+                            wg_std=None, seed=12), 0.0, "reroute", True, 0.0),
+    "stats_two_level_e16": (S("stats_two_level_e16", T=17000, d=64, E=16, k=2, d_ffn=64, capacity_factor=1.0,
+                              seed=13), 0.0, "token", True, 0.0),
 }
 
 
