@@ -485,7 +485,7 @@ def rooflines(m: Measured, shared_d_ffn: int = 0) -> dict:
         out["roofline"] = None                          # launch-latency-bound correctness path
     ng = (T + 15) // 16
     router_bytes = T * d * sx + E * d * sx + T * E * 4 + T * k * 8 + ng * E * 8
-    gather_fused = path == "gemm" and T * d * 2 < 2 ** 31
+    gather_fused = path == "gemv" or (path == "gemm" and T * d * 2 < 2 ** 31)
     dispatch_bytes = T * k * 4 + T * k * 4 + kept * 4 + (0 if gather_fused else 2 * kept * d * sx)
     combine_bytes = kept * d * 4 + T * k * 8 + T * d * sx
     disp_ms = st["scan"] + st["permute_gather"]

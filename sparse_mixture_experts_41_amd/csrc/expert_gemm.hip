@@ -1016,7 +1016,8 @@ int tile_grid(int R, int E, int C, int BM, int N, int BN) {
 }  // namespace
 
 bool ffn_gathers(const FfnArgs& a) {
-  return a.bf16 && a.C > 16 && static_cast<long long>(a.T) * a.d * 2 < (1ll << 31);
+  // the GEMV (C <= 16) forms 64-bit row addresses; the MFMA kernel's buffer offsets are 32-bit
+  return a.bf16 && (a.C <= 16 || static_cast<long long>(a.T) * a.d * 2 < (1ll << 31));
 }
 
 int ffn_splits(const FfnArgs& a) { return (a.bf16 && a.C > 16) ? kTailMaxParts : 1; }
@@ -1082,7 +1083,7 @@ hipError_t launch_expert_ffn(const FfnArgs& a, hipStream_t stream, hipEvent_t ev
               nullptr, 0, 0};
   if (ffn_h_tiled(a.bf16, a.C)) g2.a_tiled = 1;   // GEMM1 runs the MFMA kernel: H is tiled
   g1.b_tiled = g2.b_tiled = a.w_packed;          // bf16 only, d and d_ffn multiples of 256
-  if (a.bf16 && a.C > 16 && a.rows != nullptr) {   // GEMM1 reads the token rows of x directly
+  if (a.bf16 && a.rows != nullptr) {   // GEMM1 (or the GEMV) reads the token rows of x directly
     g1.A = a.x;
     g1.rows = a.rows;
     g1.a_rows = a.T;

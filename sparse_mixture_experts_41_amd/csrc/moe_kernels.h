@@ -126,7 +126,8 @@ struct FfnArgs {
                           // d_ffn multiples of 256)
 };
 // Whether GEMM1 can read the token rows of x through the permutation instead of a gathered
-// copy: the bf16 MFMA path with x addressable by 32-bit buffer offsets.
+// copy: the bf16 GEMV path (C <= 16), and the bf16 MFMA path with x addressable by 32-bit
+// buffer offsets.
 bool ffn_gathers(const FfnArgs& a);
 // Most K parts a tile of the last, partial round of GEMM2 is split into (1 = no tail split):
 // kTailMaxParts on the bf16 MFMA path, 1 elsewhere. Part 0 writes y_perm, the other parts

@@ -169,7 +169,11 @@ template <bool WAVE>
 __device__ __forceinline__ uint64_t quad_epilogue(float* rows, int ldr, int t0, int nt, int E, int k, float tau, int noise,
                                   float noise_std, uint32_t key0, uint32_t key1, float* __restrict__ logits,
                                   float* __restrict__ scores, int32_t* __restrict__ idx_out,
-                                  float* __restrict__ w_out, int32_t* __restrict__ next_out, float& entropy) {
+                                  float* __restrict__ w_out, int32_t* __restrict__ next_out, bool want_entropy,
+                                  float& entropy) {
+  // the per-expert loops unrolled by 4 so that their LDS reads pipeline; not in the streaming
+  // kernel (WAVE), whose in-flight operand loads leave no registers for it
+  constexpr int UNR = WAVE ? 1 : 4;
   const int lane = lane_id();
   const size_t base = static_cast<size_t>(t0) * E;
   for (int r = 0; r < nt; ++r)               // E <= 64: one coalesced row per step
@@ -181,6 +185,7 @@ __device__ __forceinline__ uint64_t quad_epilogue(float* rows, int ldr, int t0, 
   const bool valid = tl < nt;
   if (valid && (noise != kNoiseNone || tau != 1.0f)) {
     const int t = t0 + tl;
+#pragma unroll UNR
     for (int e = e0; e < e1; ++e) {
       float s = row[e];
       if (noise != kNoiseNone)
@@ -210,6 +215,7 @@ __device__ __forceinline__ uint64_t quad_epilogue(float* rows, int ldr, int t0, 
     if (j < jmax) {
       int best = -1;
       float bv = 0.0f;
+#pragma unroll UNR
       for (int e = e0; e < e1; ++e) {
         const float v = row[e];
         const bool take = !((used >> e) & 1ull) && (best < 0 || v > bv);
@@ -232,6 +238,7 @@ __device__ __forceinline__ uint64_t quad_epilogue(float* rows, int ldr, int t0, 
   }
   const float mx = row[idx[0]];
   float sum = 0.0f;
+#pragma unroll UNR
   for (int e = e0; e < e1; ++e) {
     const float ex = __expf(row[e] - mx);
     row[e] = ex;
@@ -241,13 +248,16 @@ __device__ __forceinline__ uint64_t quad_epilogue(float* rows, int ldr, int t0, 
   sum += __shfl_xor(sum, 2);
   const float inv = 1.0f / sum;
   float h = 0.0f;                            // -sum p ln p over this lane's experts (0 ln 0 = 0)
+#pragma unroll UNR
   for (int e = e0; e < e1; ++e) {
     const float pe = row[e] * inv;
     row[e] = pe;
-    h -= pe > 0.0f ? pe * __logf(pe) : 0.0f;
+    if (want_entropy) h -= pe > 0.0f ? pe * __logf(pe) : 0.0f;
   }
-  h += __shfl_xor(h, 1);
-  h += __shfl_xor(h, 2);
+  if (want_entropy) {
+    h += __shfl_xor(h, 1);
+    h += __shfl_xor(h, 2);
+  }
   entropy = h;
   rows_sync<WAVE>();
   float psel = 0.0f;
@@ -277,7 +287,8 @@ __device__ __forceinline__ void group_finish(const RouterArgs& a, float* rows, i
   const int E = a.E;
   float ent;
   const uint64_t sel = quad_epilogue<WAVE>(rows, LDE, t0, nt_tok, E, a.k, a.tau, a.noise, a.noise_std, a.key0,
-                                           a.key1, a.logits, a.scores, a.idx, a.w, a.idx_next, ent);
+                                           a.key1, a.logits, a.scores, a.idx, a.w, a.idx_next,
+                                           a.ent_part != nullptr, ent);
   rows_sync<WAVE>();
   if (a.ent_part != nullptr) {               // the group's entropy sum, tokens in order
     __shared__ float ents[kWaves][kGroupTokens];
@@ -314,16 +325,19 @@ __device__ __forceinline__ void group_finish(const RouterArgs& a, float* rows, i
 }
 
 // bf16 router: one workgroup per MT groups of 16 tokens over all of d (or over one K slice,
-// SPLIT). The chunks of 64 along d are dealt round-robin to the 4 waves; each wave issues the
+// SPLIT). The chunks of 64 along d are dealt round-robin to the WV waves; each wave issues the
 // loads of NB chunks before their MFMAs and accumulates MT x NT tiles of
-// v_mfma_f32_16x16x32_bf16 (x rows as A, W_g rows as B, both K-contiguous). The four wave
-// partials are added in LDS in wave order, the bias is added, and wave w runs the epilogue of
-// group w. MT = 4 cuts the W_g traffic per token by four when E is large.
-template <int NT, int NB, int MT, bool SPLIT>
-__global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a, float* __restrict__ zpart) {
+// v_mfma_f32_16x16x32_bf16 (x rows as A, W_g rows as B, both K-contiguous). The wave partials
+// are added in LDS in wave order, the bias is added, and wave w runs the epilogue of group w.
+// MT = 4 cuts the W_g traffic per token by four when E is large. WV = 8 (when the grid is at
+// most one workgroup per CU) keeps twice the loads in flight per CU.
+template <int NT, int NB, int MT, bool SPLIT, int WV = kWaves>
+__global__ __launch_bounds__(kWave * WV) void router_bf16_kernel(RouterArgs a, float* __restrict__ zpart) {
+  static_assert(MT <= kWaves && (WV == 4 || WV == 8), "group_finish's scratch is indexed by wave < kWaves");
   constexpr int TB = kGroupTokens * MT;
   constexpr int LDR = 16 * NT + 1, LDE = kMaxE + 1;
-  __shared__ float red[4][TB * LDR];
+  constexpr int NTH = kWave * WV;
+  __shared__ float red[WV][TB * LDR];
   __shared__ float rows[TB * LDE];
   const int wave = threadIdx.x >> 6, lane = lane_id();
   const int t0 = blockIdx.x * TB;
@@ -355,12 +369,12 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a, float* _
     for (int n = 0; n < NT; ++n) acc[m][n] = floatx4{0.f, 0.f, 0.f, 0.f};
   // chunk c covers k in [64c, 64c + 64): lane group g takes k 64c + 16g + [0, 16) as two
   // 8-element pieces, and MFMA step h uses piece h of both operands (same k order on A and B)
-  for (int c0 = wave; c0 < nchunk; c0 += 4 * NB) {
+  for (int c0 = wave; c0 < nchunk; c0 += WV * NB) {
     bf16x8 av[NB][MT][2], bv[NB][NT][2];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int kc = (c0 + 4 * i) * 64;
-      if (c0 + 4 * i < nchunk) {
+      const int kc = (c0 + WV * i) * 64;
+      if (c0 + WV * i < nchunk) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           av[i][m][0] = *reinterpret_cast<const bf16x8*>(ap[m] + kc);
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a, float* _
     }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      if (c0 + 4 * i < nchunk) {
+      if (c0 + WV * i < nchunk) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -394,19 +408,23 @@ __global__ __launch_bounds__(256) void router_bf16_kernel(RouterArgs a, float* _
 #pragma unroll
       for (int i = 0; i < 4; ++i) red[wave][(m * 16 + 4 * g + i) * LDR + n * 16 + r16] = acc[m][n][i];
   __syncthreads();
+  // the wave partials of element l, added in wave order
+  auto wave_sum = [&](int l) {
+    float z = red[0][l];
+#pragma unroll
+    for (int w = 1; w < WV; ++w) z += red[w][l];
+    return z;
+  };
   if (SPLIT) {   // slice partial sums to zpart[ks][t][e]; router_finish_kernel does the rest
-    for (int o = threadIdx.x; o < nt_tok * E; o += 256) {
+    for (int o = threadIdx.x; o < nt_tok * E; o += NTH) {
       const int row = o / E, col = o - row * E;
-      const int l = row * LDR + col;
-      zpart[(static_cast<size_t>(ks) * a.T + t0 + row) * E + col] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+      zpart[(static_cast<size_t>(ks) * a.T + t0 + row) * E + col] = wave_sum(row * LDR + col);
     }
     return;
   }
-  for (int o = threadIdx.x; o < TB * E; o += 256) {
+  for (int o = threadIdx.x; o < TB * E; o += NTH) {
     const int row = o / E, col = o - row * E;
-    const int l = row * LDR + col;
-    rows[row * LDE + col] =
-        (((red[0][l] + red[1][l]) + red[2][l]) + red[3][l]) + (a.bg != nullptr ? a.bg[col] : 0.0f);
+    rows[row * LDE + col] = wave_sum(row * LDR + col) + (a.bg != nullptr ? a.bg[col] : 0.0f);
   }
   __syncthreads();
   // wave w finishes group w; waves without a group leave (the remaining barriers count the rest)
@@ -696,14 +714,22 @@ static hipError_t launch_router_bf16(const RouterArgs& a, float* zpart, hipStrea
     return hipGetLastError();
   }
   if (KS == 1) {
+    // at most one workgroup per CU: 8 waves each, twice the loads in flight per CU
     if constexpr (NT >= 3) {
       if (ng >= 4 * 256) {                   // large E and enough tokens: 64 tokens per workgroup
-        hipLaunchKernelGGL((router_bf16_kernel<NT, 2, 4, false>), dim3((ng + 3) / 4), dim3(256), 0, stream, a,
-                           nullptr);
+        const int grid = (ng + 3) / 4;
+        if (grid <= cus)
+          hipLaunchKernelGGL((router_bf16_kernel<NT, 2, 4, false, 8>), dim3(grid), dim3(8 * kWave), 0, stream, a,
+                             nullptr);
+        else
+          hipLaunchKernelGGL((router_bf16_kernel<NT, 2, 4, false>), dim3(grid), dim3(256), 0, stream, a, nullptr);
         return hipGetLastError();
       }
     }
-    hipLaunchKernelGGL((router_bf16_kernel<NT, NB, 1, false>), dim3(ng), dim3(256), 0, stream, a, nullptr);
+    if (ng <= cus)
+      hipLaunchKernelGGL((router_bf16_kernel<NT, NB, 1, false, 8>), dim3(ng), dim3(8 * kWave), 0, stream, a, nullptr);
+    else
+      hipLaunchKernelGGL((router_bf16_kernel<NT, NB, 1, false>), dim3(ng), dim3(256), 0, stream, a, nullptr);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((router_bf16_kernel<NT, NB, 1, true>), dim3(ng, KS), dim3(256), 0, stream, a, zpart);
