@@ -443,7 +443,10 @@ __global__ __launch_bounds__(kWave * WV) void router_bf16_kernel(RouterArgs a, f
 // flight during this group's epilogue. A lane's two 16-byte pieces of a chunk are k offsets
 // 8 g and 32 + 8 g (its lane group g): each load instruction reads 64 contiguous bytes of
 // each of 16 rows, and A and B use the same k order. Rows past the last token re-read the
-// last token; they only feed rows that are not kept.
+// last token; they only feed rows that are not kept. Wave slot s takes a group's batches in
+// the order s, s + 1, ... (mod the batches per group), so that the waves running at one time
+// read different column ranges of their rows (rows d * 2 bytes apart): 76 -> 70 us on 65536
+// tokens of d = 2048 against every wave starting at column 0.
 constexpr int kStreamWg = 68 * 1024;     // W_g bytes in LDS (two workgroups per CU)
 
 template <int NT, int NB, int WCAP>
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(256) void router_stream_kernel(RouterArgs a) {
   auto issue = [&](int q, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
     const int qq = q < nq ? q : nq - 1;
-    const int grp = slot + (qq / nbat) * S, b = qq % nbat;
+    const int grp = slot + (qq / nbat) * S, b = (qq % nbat + slot) % nbat;
     const int t = min(grp * kGroupTokens + r16, T - 1);
     const u16* row = x + static_cast<size_t>(t) * d + 8 * g;
 #pragma unroll
@@ -522,8 +525,8 @@ __global__ __launch_bounds__(256) void router_stream_kernel(RouterArgs a) {
   floatx4 acc[NT];
   auto step = [&](int q, auto buf_c) {
     constexpr int buf = decltype(buf_c)::value;
-    const int b = q % nbat;
-    if (b == 0) {
+    const int p = q % nbat, b = (p + slot) % nbat;   // position p in the group, batch b of d
+    if (p == 0) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) acc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(256) void router_stream_kernel(RouterArgs a) {
           }
       }
     }
-    if (b == nbat - 1) {                     // the group's logits are complete: epilogue
+    if (p == nbat - 1) {                     // the group's logits are complete: epilogue
       const int grp = slot + (q / nbat) * S;
       const int t0 = grp * kGroupTokens;
       // C layout of a 16x16 tile: lane holds column r16, rows 4 g + i
