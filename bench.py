@@ -265,7 +265,7 @@ def train_step(args, shape, cfg, tensors, variant, ops, torch) -> int:
         "backward_ms": bwd_ms,
         "backward_gemm_tflops": tflops,
         "backward_gemm_frac": {n: v / PEAK_BF16_TFLOPS for n, v in tflops.items()},
-        "training_flops_frac": 6.0 * d * dff * kept / ((fwd_ms + bwd_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "training_flops_frac": 12.0 * d * dff * kept / ((fwd_ms + bwd_ms) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "stage_ms": fst,
         "backward_stage_ms": bst,
         "cpu_baseline": None,
