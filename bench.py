@@ -52,7 +52,7 @@ OTHERS = "mixtral_like,switch_skew,decode,tiny_fp32"
 FLUSH_BYTES = 1 << 30
 SCRUB_BYTES = 1 << 29
 # default size of the CPU oracle's sample (tokens): about 10-30 s of host work
-CPU_SAMPLE = {"gumbel_longtail": 16384, "mixtral_like": 4096, "switch_skew": 16384, "decode": 128, "tiny_fp32": 256}
+CPU_SAMPLE = {"gumbel_longtail": 32768, "mixtral_like": 4096, "switch_skew": 16384, "decode": 128, "tiny_fp32": 256}
 
 
 def _args():
