@@ -13,6 +13,8 @@ back to back between two device
 synchronisations. Prints one JSON line for the headline workload (the largest one by default):
   value          tokens/s of the whole layer from the median cold step (T tokens per step);
   warm           the back-to-back figures beside it;
+  row_major      the headline workload again with W1 and W2 in nn.Linear's layout, as a caller
+                 hands them over (the headline packs them once, before its warm-up);
   stage_ms       per-stage medians of the cold steps;
   roofline       the headline's dominant expert GEMM kernel: algorithmic flops (2 d d_ffn per
                  kept row) over its mean cold-step duration, against the bf16 dense MFMA peak;
@@ -315,15 +317,18 @@ class Measured:
     pass
 
 
-def measure_workload(shape, args, ops, torch, variant_args=None, capacity_factor=None) -> Measured:
-    """Inputs, plan, W warm-up steps, K cold steps (events), K warm steps (host clock)."""
+def measure_workload(shape, args, ops, torch, variant_args=None, capacity_factor=None, arrays=None,
+                     weights=None) -> Measured:
+    """Inputs (or the given arrays of the same shape), plan, W warm-up steps, K cold steps
+    (events), K warm steps (host clock). `weights` overrides args.weights."""
     import numpy as np
 
     from workloads import make_inputs, make_shared_expert
 
     if capacity_factor is not None:
         shape = shape.with_(capacity_factor=capacity_factor)
-    arrays = make_inputs(shape)
+    if arrays is None:
+        arrays = make_inputs(shape)
 
     def dev(a):
         if a is None:
@@ -356,7 +361,7 @@ def measure_workload(shape, args, ops, torch, variant_args=None, capacity_factor
                    if with_variant else None)
         m.train = (cfg, tensors, variant)
         return m
-    m.packed = (args.weights == "packed" and shape.dtype == "bf16" and shape.d % 256 == 0
+    m.packed = ((weights or args.weights) == "packed" and shape.dtype == "bf16" and shape.d % 256 == 0
                 and shape.d_ffn % 256 == 0)
     m.pack_ms = None
     if m.packed:
@@ -558,6 +563,20 @@ def main() -> int:
     launches = [{"workload": shape.name, "forwards": head.forwards, "warmup": args.warmup, "cold": args.steps,
                  "warm": args.steps}]
     entry = workload_entry(head, args.shared_d_ffn)
+    # the headline workload again with the expert weights in nn.Linear's layout, as the caller
+    # hands them over (the headline packs them once before its warm-up)
+    row_major = None
+    if head.packed:
+        rm = measure_workload(head.shape, args, ops, torch, variant_args=args, arrays=head.arrays,
+                              weights="row-major")
+        launches.append({"workload": f"{shape.name} (row-major weights)", "forwards": rm.forwards,
+                         "warmup": args.warmup, "cold": args.steps, "warm": args.steps})
+        rm_entry = workload_entry(rm, args.shared_d_ffn)
+        row_major = {"tokens_per_s": shape.T / (rm.cold_ms * 1e-3), "ms_per_step": rm.cold_ms,
+                     "warm_ms_per_step": rm.warm_ms, "stage_ms": rm.cold_stage_median,
+                     "grouped_gemm": rm_entry.get("grouped_gemm")}
+        del rm
+        torch.cuda.empty_cache()
     traffic = None
     if entry.get("roofline") and not head.with_variant and args.capacity_factor is None:
         traffic_path = args.traffic or os.path.join(ROOT, "profiles", f"traffic_{shape.name}.json")
@@ -610,6 +629,7 @@ def main() -> int:
         "stage_ms": head.cold_stage_median,
         "stage_ms_mean": head.cold_stage_mean,
         "pack_ms": head.pack_ms,
+        "row_major": row_major,
         "counts_minmax": entry["counts_minmax"],
         "measured_peaks": peaks,
         "workloads": others,
@@ -687,6 +707,10 @@ def summarize_trace(trace_dir: str, bench_log: str | None) -> str:
     for l in line["launches"]:
         w = l["workload"]
         entry = line if w == line["config"]["workload"] else line["workloads"].get(w, {})
+        if w.endswith("(row-major weights)") and line.get("row_major"):
+            rmj = line["row_major"]
+            entry = {"stage_ms": rmj["stage_ms"], "grouped_gemm": rmj["grouped_gemm"], "roofline": line["roofline"],
+                     "config": line["config"]}
         stage = (line.get("stage_ms_mean") if w == line["config"]["workload"] else None) or entry.get("stage_ms", {})
         roof = entry.get("roofline")
         gg = entry.get("grouped_gemm") or {}
