@@ -528,9 +528,9 @@ def main() -> int:
         print(json.dumps(summarize_counters(args.summarize_counters.split(","), args.workload, args.weights), indent=1))
         return 0
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(no collectives or sharding are implemented: the layer's expert-parallel sharding is a design "
-              "only).", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the library has no "
+              "collectives or sharding (expert-parallel sharding of the layer is described, not implemented).",
+              file=sys.stderr)
         return 2
 
     import torch

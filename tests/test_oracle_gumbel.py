@@ -58,7 +58,7 @@ def test_philox_matches_rocrand_library(tmp_path_factory):
     rows = []
     for i in range(400):
         c = [int(v) for v in rng.integers(0, 2 ** 32, size=4)]
-        c[1] &= (1 << 30) - 1                     # the driver's offset form needs c1 < 2^30
+        c[1] &= (1 << 30) - 1                     # the helper's (offset, subsequence) form needs c1 < 2^30
         k = [int(v) for v in rng.integers(0, 2 ** 32, size=2)]
         if i < 3:
             c, k = [[0, 0, 0, 0], [i, 5, 0, 0], [65535, 15, 0, 0]][i], [[0, 0], [0, 0], [0, 0]][i]
