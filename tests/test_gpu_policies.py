@@ -56,6 +56,9 @@ CASES = {
                             wg_std=None, seed=12), 0.0, "reroute", True, 0.0),
     "stats_two_level_e16": (S("stats_two_level_e16", T=17000, d=64, E=16, k=2, d_ffn=64, capacity_factor=1.0,
                               seed=13), 0.0, "token", True, 0.0),
+    # 257 groups of 64 experts: the first count that takes two levels, its last chunk one group
+    "random_two_level_edge": (S("random_two_level_edge", T=4112, d=64, E=64, k=2, d_ffn=64, capacity_factor=0.9,
+                                wg_std=None, seed=14), 0.0, "random", True, 0.0),
 }
 
 
