@@ -202,9 +202,10 @@ def bf16_rne(v: np.ndarray) -> np.ndarray:
     return np.ldexp(np.round(m * 256.0) / 256.0, e)
 
 
-def check_output(y_gpu, y_ref, dtype, label="", rms=None):
+def check_output(y_gpu, y_ref, dtype, label="", rms=None, bound_rms=None):
     """``rms`` defaults to rms(y_ref) over the given elements. Records the statistics under
-    ``label`` in PARITY_TABLE."""
+    ``label`` in PARITY_TABLE. ``bound_rms`` replaces the 2e-2 of the max-error bound (bf16;
+    only check_forward_full's bf16-H case sets it, and the table records it)."""
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     err = np.abs(y_gpu - y_ref)
@@ -218,13 +219,13 @@ def check_output(y_gpu, y_ref, dtype, label="", rms=None):
         return stats
     rms = float(np.sqrt(np.mean(y_ref ** 2))) if rms is None else float(rms)
     mean_rel = float(err.sum() / max(np.abs(y_ref).sum(), 1e-300))
-    bound = BF16_MAX_RMS * rms
+    bound = (BF16_MAX_RMS if bound_rms is None else bound_rms) * rms
     big = np.abs(y_ref) > BF16_BIG_RMS * rms
     excess = err - np.where(big, half_ulp_bf16(y_ref), 0.0)
     i = int(np.argmax(excess))
     assert excess.flat[i] <= bound, (
         f"{label}: error {err.flat[i]:.3e} at |y_ref| = {abs(y_ref.flat[i]):.3e} ({abs(y_ref.flat[i]) / rms:.2f} rms)"
-        f" exceeds {BF16_MAX_RMS} * rms = {bound:.3e}" + (" after the half-ulp credit" if big.flat[i] else ""))
+        f" exceeds {bound / max(rms, 1e-300):.4f} * rms = {bound:.3e}" + (" after the half-ulp credit" if big.flat[i] else ""))
     assert mean_rel <= BF16_MEAN_REL, f"{label}: mean relative error {mean_rel:.3e}"
     j = int(np.argmax(err))
     scale = rms if rms > 0 else 1.0
@@ -238,13 +239,45 @@ def check_output(y_gpu, y_ref, dtype, label="", rms=None):
              "n_big": int(big.sum()),
              "n_credited": int(np.sum(big & (err > bound))),
              "elements": int(err.size)}
+    if bound_rms is not None:
+        stats["bf16_h_bound_rms"] = float(bound_rms)
     if label:
         PARITY_TABLE[label] = dict(stats, dtype="bf16")
     return stats
 
 
-def check_forward_full(p: Problem, gpu: dict | None = None) -> dict:
-    """Whole-layer parity on every token (sizes the oracle finishes in seconds)."""
+def bf16_h_arithmetic(p: Problem, ref: dict) -> np.ndarray:
+    """The oracle's layer output with the one extra rounding the bf16 path makes by design: H,
+    the expert's hidden activation and the second GEMM's MFMA operand, rounded to bf16 (float64
+    elsewhere, y not rounded). Built from the oracle's own steps on the oracle's dispatch; for
+    plain problems (no shared expert)."""
+    assert p.shared_d_ffn == 0
+    h, act = p.host, {"gelu": oracle.gelu, "silu": oracle.silu}[p.activation]
+    x_perm, kept, offsets = ref["x_perm"], ref["kept"], ref["offsets"]
+    y_perm = np.zeros((x_perm.shape[0], p.shape.d), dtype=np.float64)
+    for e in range(p.shape.E):
+        n, lo = int(kept[e]), int(offsets[e])
+        if n == 0:
+            continue
+        pre = x_perm[lo:lo + n] @ np.asarray(h["W1"][e], np.float64).T
+        if h["b1"] is not None:
+            pre = pre + np.asarray(h["b1"][e], np.float64)
+        ye = bf16_rne(act(pre)) @ np.asarray(h["W2"][e], np.float64).T
+        if h["b2"] is not None:
+            ye = ye + np.asarray(h["b2"][e], np.float64)
+        y_perm[lo:lo + n] = ye
+    return oracle.combine(y_perm, ref["dest"], ref["w"])
+
+
+def check_forward_full(p: Problem, gpu: dict | None = None, h_margin: float | None = None) -> dict:
+    """Whole-layer parity on every token (sizes the oracle finishes in seconds).
+
+    With ``h_margin`` (bf16 only), the output is also compared with bf16_h_arithmetic: every
+    element within half a bf16 ulp of it plus h_margin * rms (the float32-against-float64
+    accumulation and an occasional H rounded the other way). The 2e-2 rms bound against the
+    oracle leaves half of itself to the output's own rounding and half to the computation;
+    where the bf16 H alone takes the layer further than that half from the oracle (by h_err
+    rms), the bound becomes h_err + 1e-2 rms, and the case is recorded as such."""
     sh = p.shape
     gpu = run_forward(p) if gpu is None else gpu
     z_ref = oracle.logits(p.host["x"], p.host["Wg"], p.host["bg"])
@@ -256,7 +289,18 @@ def check_forward_full(p: Problem, gpu: dict | None = None) -> dict:
     dropped_all = np.all(ref["dest"] < 0, axis=1)
     if not p.shared_d_ffn:
         assert np.all(gpu["y"][dropped_all] == 0.0), "fully dropped tokens must give exactly 0"
-    stats = check_output(gpu["y"], ref["y"], sh.dtype, p.label)
+    bound_rms = None
+    if h_margin is not None and sh.dtype == "bf16":
+        y_h = bf16_h_arithmetic(p, ref)
+        rms = float(np.sqrt(np.mean(ref["y"] ** 2)))
+        scale = rms if rms > 0 else 1.0
+        beyond = np.abs(np.asarray(gpu["y"], np.float64) - y_h) - half_ulp_bf16(y_h)
+        assert beyond.max() <= h_margin * scale, (
+            f"{p.label}: {beyond.max() / scale:.4f} rms beyond half an ulp of the bf16-H arithmetic")
+        h_err = float(np.max(np.abs(y_h - ref["y"]))) / scale
+        if h_err > BF16_MAX_RMS / 2:
+            bound_rms = h_err + BF16_MAX_RMS / 2
+    stats = check_output(gpu["y"], ref["y"], sh.dtype, p.label, bound_rms=bound_rms)
     stats.update(kept=int(chk["dispatch"]["kept"].sum()), drops=int(chk["dispatch"]["drops"].sum()),
                  fully_dropped=int(dropped_all.sum()))
     return stats
