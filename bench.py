@@ -89,6 +89,9 @@ def _args():
     ap.add_argument("--lam", type=float, default=0.01, help="weight of the balance loss in the training step")
     ap.add_argument("--weights", choices=("packed", "row-major"), default="packed",
                     help="expert weight layout of the timed forwards (packed where the shape allows it)")
+    ap.add_argument("--no-row-major", action="store_true",
+                    help="skip the headline's second measurement with row-major weights (the traffic "
+                         "counter runs use this: both layouts' GEMM1 launches share one kernel name)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the probe copy kernel over this many MiB (3 times) and exit: the "
                          "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -566,7 +569,7 @@ def main() -> int:
     # the headline workload again with the expert weights in nn.Linear's layout, as the caller
     # hands them over (the headline packs them once before its warm-up)
     row_major = None
-    if head.packed:
+    if head.packed and not args.no_row_major:
         rm = measure_workload(head.shape, args, ops, torch, variant_args=args, arrays=head.arrays,
                               weights="row-major")
         launches.append({"workload": f"{shape.name} (row-major weights)", "forwards": rm.forwards,
