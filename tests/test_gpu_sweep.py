@@ -13,13 +13,18 @@ bf16 (the second GEMM's MFMA operand): within half an ulp of y plus H_MARGIN rms
 check that carries a case where the bf16 H by itself is further than 1e-2 rms from the oracle
 (the computation's half of the 2e-2 bound; a single dominant expert per token at k = 7 puts
 some rows at 4.5 rms), where the bound against the oracle becomes that distance plus 1e-2.
+
+test_backward_sweep draws 12 more shapes the same way for the training pass (moe_forward_train +
+moe_backward) under every capacity policy, both activations, Gaussian router noise and the
+balance term, with the backward tests' tolerances.
 """
 import numpy as np
 import pytest
 
-from workloads import MoEShape
+import oracle
+from workloads import MoEShape, make_upstream_grad
 
-from .parity import Problem, check_forward_full
+from .parity import Problem, backward_errors, check_forward_full, host_values, run_train
 
 pytestmark = pytest.mark.gpu
 
@@ -59,3 +64,55 @@ def test_sweep(i):
     print(f"[gpu] sweep {i}: {shape} bias={bias}", flush=True)
     res = check_forward_full(Problem(shape, bias_std=bias), h_margin=H_MARGIN)
     print(f"[gpu]   sweep {i}: {res}", flush=True)
+
+
+def _backward_shapes(n: int = 12, seed: int = 20261204):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f32 = i % 4 == 3
+        E = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 31, 64]))
+        k = int(rng.integers(1, min(8, E) + 1))
+        T = int(rng.choice([1, 7, 64, 300, 1000, 2100]))
+        if f32:
+            T = min(T, 400)
+            d, dff = 8 * int(rng.integers(1, 17)), 8 * int(rng.integers(1, 25))
+        else:
+            d, dff = 64 * int(rng.integers(1, 9)), 64 * int(rng.integers(1, 9))
+        cf = float(rng.choice([0.5, 1.0, 1.25, 2.0]))
+        act = str(rng.choice(["gelu", "silu"]))
+        policy = str(rng.choice(["token", "random", "reroute"]))
+        noise = float(rng.choice([0.0, 0.0, 0.3]))
+        gumbel = noise == 0.0 and bool(rng.integers(0, 2))
+        tau = float(rng.choice([1.0, 0.8]))
+        lam = float(rng.choice([0.0, 0.01, 0.3]))
+        bias = float(rng.choice([0.0, 0.05]))
+        shape = MoEShape(f"bwd_sweep{i}", T=T, d=d, E=E, k=k, d_ffn=dff, capacity_factor=cf, temperature=tau,
+                         gumbel=gumbel, dtype="f32" if f32 else "bf16", seed=2000 + i, wg_std=0.02)
+        out.append((shape, bias, act, noise, policy, lam))
+    return out
+
+
+BACKWARD_SHAPES = _backward_shapes()
+# relative Frobenius error and max error over max |ref| per gradient (the backward tests' bounds)
+BACKWARD_TOL = {"f32": (3e-6, 6e-6), "bf16": (1.5e-2, 3e-2)}
+
+
+@pytest.mark.parametrize("i", range(len(BACKWARD_SHAPES)))
+def test_backward_sweep(i):
+    shape, bias, act, noise, policy, lam = BACKWARD_SHAPES[i]
+    print(f"[gpu] backward sweep {i}: {shape} bias={bias} act={act} noise={noise} policy={policy} lam={lam}",
+          flush=True)
+    p = Problem(shape, bias_std=bias, activation=act, noise_std=noise, drop_policy=policy)
+    dy_arr = make_upstream_grad(shape)
+    gpu = run_train(p, dy_arr, lam)
+    ref = oracle.backward(*p.host_args(), host_values(dy_arr, shape.dtype), k=shape.k,
+                          capacity_factor=shape.capacity_factor, lam=lam, tau=shape.temperature, gumbel=shape.gumbel,
+                          seed=shape.seed, given_scores=gpu["scores"], act=act, noise_std=noise, policy=policy)
+    np.testing.assert_array_equal(gpu["dest"], ref["dest"], err_msg="dest")
+    errs = backward_errors(gpu, ref)
+    print(f"[gpu]   backward sweep {i}: " + ", ".join(f"{k} {v[0]:.2e}/{v[1]:.2e}" for k, v in errs.items()),
+          flush=True)
+    fro, mx = BACKWARD_TOL[shape.dtype]
+    for key, (e_fro, e_max) in errs.items():
+        assert e_fro <= fro and e_max <= mx, f"{key}: relative Frobenius {e_fro:.3e}, max {e_max:.3e}"
