@@ -390,33 +390,49 @@ def measure_workload(shape, args, ops, torch, variant_args=None, capacity_factor
     # rather than during its first kernel
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.int32, device="cuda")
+    # K cold steps with moe_forward's per-stage events (the stage breakdown and the GEMM
+    # durations), then K cold steps timed by two events around the call alone: the step time.
+    # Each stage event adds a few microseconds to the step it splits.
     events = [ops.StageEvents() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     for i in range(args.steps):
         flush.fill_(i & 255)
         scrub.sum()
         plan.run(events=events[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    del flush, scrub
     cold_stage = [ev.accumulate() for ev in events]
     for ev in events:
         ev.close()
-    # warm: back to back
-    wev = [ops.StageEvents() for _ in range(args.steps)]
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        flush.fill_(i & 255)
+        scrub.sum()
+        pairs[i][0].record()
+        plan.run()
+        pairs[i][1].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del flush, scrub
+    # warm: back to back, host clock (no events), then with the stage events for the breakdown
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for i in range(args.steps):
-        plan.run(events=wev[i])
+        plan.run()
     torch.cuda.synchronize()
     t3 = time.perf_counter()
+    wev = [ops.StageEvents() for _ in range(args.steps)]
+    for i in range(args.steps):
+        plan.run(events=wev[i])
+    torch.cuda.synchronize()
     warm_stage = [ev.accumulate() for ev in wev]
     for ev in wev:
         ev.close()
     names = ops.STAGE_NAMES
-    m.cold_step_ms = [sum(s) for s in cold_stage]
+    m.cold_step_ms = [a.elapsed_time(b) for a, b in pairs]
     m.cold_ms = _median(m.cold_step_ms)
+    m.cold_staged_ms = _median([sum(s) for s in cold_stage])
     m.cold_stage_median = {n: _median([s[i] for s in cold_stage]) for i, n in enumerate(names)}
     m.cold_stage_mean = {n: sum(s[i] for s in cold_stage) / len(cold_stage) for i, n in enumerate(names)}
     m.cold_host_ms = (t1 - t0) * 1e3 / args.steps
@@ -426,7 +442,7 @@ def measure_workload(shape, args, ops, torch, variant_args=None, capacity_factor
     m.counts = plan.out["counts"].cpu().numpy()
     m.kept_e = plan.out["kept"].cpu().numpy()
     m.C = ops.capacity(cfg)
-    m.forwards = args.warmup + 2 * args.steps
+    m.forwards = args.warmup + 4 * args.steps
     if m.route_stats is not None:
         m.route_stats_values = dict(zip(ops.ROUTE_STAT_NAMES, m.route_stats.cpu().tolist()))
     del plan
@@ -514,6 +530,7 @@ def workload_entry(m: Measured, shared_d_ffn: int = 0) -> dict:
                     "capacity_factor": sh.capacity_factor, "temperature": sh.temperature, "gumbel": sh.gumbel,
                     "dtype": sh.dtype, "weights": "packed" if m.packed else "row-major", "capacity": m.C},
          "tokens_per_s": sh.T / (m.cold_ms * 1e-3), "ms_per_step": m.cold_ms,
+         "ms_per_step_with_stage_events": m.cold_staged_ms,
          "warm": {"tokens_per_s": sh.T / (m.warm_ms * 1e-3), "ms_per_step": m.warm_ms},
          "stage_ms": m.cold_stage_median,
          "counts_minmax": [int(m.counts.min()), int(m.counts.max())]}
@@ -621,8 +638,9 @@ def main() -> int:
                    **({"variant": {"activation": args.activation, "noise_std": args.noise_std,
                                    "shared_d_ffn": args.shared_d_ffn, "drop_policy": args.drop_policy,
                                    "route_stats": args.route_stats}} if head.with_variant else {})},
-        "timing": {"headline": "median of the K cold-cache steps (HIP events around moe_forward)",
+        "timing": {"headline": "median of K cold-cache steps, each timed by two HIP events around moe_forward",
                    "cold_step_ms": head.cold_step_ms, "host_ms_per_cold_iteration_incl_flush": head.cold_host_ms,
+                   "ms_per_step_with_stage_events": head.cold_staged_ms,
                    "flush_bytes": FLUSH_BYTES, "scrub_read_bytes": SCRUB_BYTES},
         "warm": {"tokens_per_s": T / (head.warm_ms * 1e-3), "ms_per_step": head.warm_ms,
                  "stage_ms": head.warm_stage_mean},
