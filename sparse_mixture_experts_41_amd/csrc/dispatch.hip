@@ -239,6 +239,13 @@ __global__ __launch_bounds__(kWave) void scan_chunks_kernel(const int32_t* __res
 // groups), so the statistics do not depend on the path.
 constexpr int kScanRegs = 16;
 
+// One wave's 64-token block of the stable permutation (defined below with the drop policies).
+template <bool RANDOM>
+__device__ void permute_block(const int32_t* __restrict__ idx, const int32_t* __restrict__ blockbase,
+                              const int32_t* __restrict__ offsets, int T, int E, int k, int C,
+                              const uint64_t* __restrict__ thresh, uint32_t key0, uint32_t key1,
+                              int32_t* __restrict__ dest, int32_t* __restrict__ perm, int blk);
+
 template <int R>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
   __shared__ int ilds[kScanThreads];
@@ -366,6 +373,14 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ScanArgs a) {
     blocked_colsum(a.ent_part, ng, 1, csum, flds);
     write_route_stats(tot, E, a.T, csum[0], a.route_stats, prod);
   }
+  if (a.perm_idx != nullptr) {               // uniform: the token-order permutation, fused
+    // the bases and offsets this workgroup wrote are visible to all its waves past the barrier
+    __syncthreads();
+    const int nblk = (a.T + kBlockTokens - 1) / kBlockTokens;
+    for (int blk = threadIdx.x / kWave; blk < nblk; blk += kScanThreads / kWave)
+      permute_block<false>(a.perm_idx, a.blockbase, a.offsets, a.T, E, a.k, a.C, nullptr, 0u, 0u, a.perm_dest,
+                           a.perm_out, blk);
+  }
 }
 
 __global__ __launch_bounds__(64) void stats_kernel(const int32_t* __restrict__ counts, const float* __restrict__ colsum,
@@ -392,17 +407,15 @@ __device__ __forceinline__ bool kept_at_random(int t, int e, const uint64_t* __r
 
 // One wave per 64 tokens: stable ranks by wave ballot within each 16-token group, capacity
 // test, dest and perm. RANDOM: only the slots kept by random dropping take part, ranked in
-// token order among themselves (blockbase counts kept slots only).
+// token order among themselves (blockbase counts kept slots only). Every lane of the wave runs
+// the ballots and shuffles; lane e keeps the block's mask of the lanes that chose expert e, and
+// each lane fetches the masks of its own experts from those lanes.
 template <bool RANDOM>
-__global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__ idx,
-                                                    const int32_t* __restrict__ blockbase,
-                                                    const int32_t* __restrict__ offsets, int T, int E, int k,
-                                                    int C, const uint64_t* __restrict__ thresh, uint32_t key0,
-                                                    uint32_t key1, int32_t* __restrict__ dest,
-                                                    int32_t* __restrict__ perm) {
-  __shared__ uint64_t emask[kMaxE];
+__device__ void permute_block(const int32_t* __restrict__ idx, const int32_t* __restrict__ blockbase,
+                              const int32_t* __restrict__ offsets, int T, int E, int k, int C,
+                              const uint64_t* __restrict__ thresh, uint32_t key0, uint32_t key1,
+                              int32_t* __restrict__ dest, int32_t* __restrict__ perm, int blk) {
   const int lane = lane_id();
-  const int blk = blockIdx.x;
   const int t = blk * kBlockTokens + lane;
   const bool valid = t < T;
   int ch[kMaxK];
@@ -418,11 +431,15 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
       }
     }
   }
+  uint64_t mine = 0ull;
   for (int e = 0; e < E; ++e) {
     const uint64_t b = __ballot(static_cast<int>((sel >> e) & 1ull));
-    if (lane == 0) emask[e] = b;
+    if (lane == e) mine = b;
   }
-  __syncthreads();
+  uint64_t emask[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) emask[j] = __shfl(mine, ch[j] >= 0 ? ch[j] : 0);
   if (!valid) return;
   const uint64_t below = (1ull << lane) - 1ull;
   const uint64_t gmask = 0xFFFFull << (lane & ~(kGroupTokens - 1));   // this lane's 16-lane group
@@ -435,7 +452,7 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
         dest[static_cast<size_t>(t) * k + j] = -1;
         continue;
       }
-      const int r = group_base(blockbase, ng, E, grp, e) + __popcll(emask[e] & below & gmask);
+      const int r = group_base(blockbase, ng, E, grp, e) + __popcll(emask[j] & below & gmask);
       int dst = -1;
       if (r < C) {
         dst = offsets[e] + r;
@@ -444,6 +461,16 @@ __global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__
       dest[static_cast<size_t>(t) * k + j] = dst;
     }
   }
+}
+
+template <bool RANDOM>
+__global__ __launch_bounds__(64) void permute_kernel(const int32_t* __restrict__ idx,
+                                                    const int32_t* __restrict__ blockbase,
+                                                    const int32_t* __restrict__ offsets, int T, int E, int k,
+                                                    int C, const uint64_t* __restrict__ thresh, uint32_t key0,
+                                                    uint32_t key1, int32_t* __restrict__ dest,
+                                                    int32_t* __restrict__ perm) {
+  permute_block<RANDOM>(idx, blockbase, offsets, T, E, k, C, thresh, key0, key1, dest, perm, blockIdx.x);
 }
 
 // Random dropping, selection: one workgroup per expert finds the C-th smallest key among the
@@ -802,6 +829,7 @@ hipError_t launch_scan(const ScanArgs& a, hipStream_t stream) {
   ScanArgs b = a;
   b.zero_bases = nullptr;
   b.zero_n = 0;
+  b.perm_idx = nullptr;
   b.hist = r.ctot;
   b.ng = r.nc;
   b.blockbase = r.cbase;
@@ -822,6 +850,28 @@ hipError_t launch_permute(const int32_t* idx, const int32_t* blockbase, const in
   hipLaunchKernelGGL(permute_kernel<false>, dim3(nblk), dim3(64), 0, stream, idx, blockbase, offsets, T, E, k, C,
                      nullptr, 0u, 0u, dest, perm);
   return hipGetLastError();
+}
+
+// The token-order permutation runs in the scan kernel itself when the scan takes one level and
+// the tokens are at most one 64-token block per wave of it (kScanThreads / 64 blocks): one launch
+// and one launch gap fewer on decode-sized batches.
+static bool scan_fuses_permute(const ScanArgs& a) {
+  return !a.bases_only && !scan_two_level(a.ng, a.E) &&
+         (a.T + kBlockTokens - 1) / kBlockTokens <= kScanThreads / kWave;
+}
+
+hipError_t launch_scan_permute(const ScanArgs& a, const int32_t* idx, int32_t* dest, int32_t* perm,
+                               hipStream_t stream) {
+  if (scan_fuses_permute(a)) {
+    ScanArgs b = a;
+    b.perm_idx = idx;
+    b.perm_dest = dest;
+    b.perm_out = perm;
+    return launch_scan(b, stream);
+  }
+  hipError_t err = launch_scan(a, stream);
+  if (err != hipSuccess) return err;
+  return launch_permute(idx, a.blockbase, a.offsets, a.T, a.E, a.k, a.C, dest, perm, stream);
 }
 
 hipError_t launch_select_random(const int32_t* idx, const int32_t* counts, int T, int E, int k, int C, uint32_t key0,

@@ -384,8 +384,7 @@ moe_status moe_dispatch(const moe_config* cfg, const int32_t* topk_idx, const vo
   s.kept = kept;
   s.offsets = offsets;
   s.blockbase = blockbase;
-  MOE_HIP(moe::launch_scan(s, st), "scan");
-  MOE_HIP(moe::launch_permute(topk_idx, blockbase, offsets, D.T, D.E, D.k, s.C, dest, perm, st), "permute");
+  MOE_HIP(moe::launch_scan_permute(s, topk_idx, dest, perm, st), "scan + permute");
   MOE_HIP(moe::launch_gather(x, perm, kept, offsets, D.E, D.R, static_cast<int>(D.d * D.esize), x_perm, st),
           "gather");
   return MOE_OK;
@@ -558,7 +557,13 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
   s.L = L;
   s.ent_part = ent;
   s.route_stats = D.stats ? variant->route_stats : nullptr;
-  MOE_HIP(moe::launch_scan(s, st), "scan");
+  // token order: the permutation follows the scan directly (in the scan kernel itself for small
+  // batches); the other policies need their second pass first
+  const bool token_order = D.policy != MOE_DROP_RANDOM && !reroute;
+  if (token_order)
+    MOE_HIP(moe::launch_scan_permute(s, idx, dest, perm, st), "scan + permute");
+  else
+    MOE_HIP(moe::launch_scan(s, st), "scan");
   if (ev) MOE_HIP(hipEventRecord(ev[2], st), "event");
   // 3a'. capacity policies: the rows the surviving slots take (second scan over them)
   int32_t* hist2 = at<int32_t>(ws, Lw.hist2);
@@ -599,8 +604,6 @@ moe_status forward_impl(const moe_config* cfg, const moe_variant* variant, const
     MOE_HIP(moe::launch_permute_reroute(idx, at<int32_t>(ws, Lw.cand), blockbase, blockbase2, kept1, offsets,
                                         scores != nullptr ? scores : logits, D.T, D.E, D.k, C, dest, perm, w, st),
             "permute_reroute");
-  } else {
-    MOE_HIP(moe::launch_permute(idx, blockbase, offsets, D.T, D.E, D.k, C, dest, perm, st), "permute");
   }
   // 4. experts
   fa.x_perm = x_perm;

@@ -69,8 +69,17 @@ struct ScanArgs {
   // one-level scan)
   int32_t* zero_bases;
   int zero_n;
+  // set by launch_scan_permute when the token-order permutation runs in the scan kernel:
+  // slots idx [T,k] -> dest [T,k], perm (as launch_permute with C and the bases above)
+  const int32_t* perm_idx;
+  int32_t* perm_dest;
+  int32_t* perm_out;
 };
 hipError_t launch_scan(const ScanArgs& a, hipStream_t stream);
+// launch_scan, then the token-order permutation (launch_permute with a.C), fused into the scan
+// kernel where the batch is small enough.
+hipError_t launch_scan_permute(const ScanArgs& a, const int32_t* idx, int32_t* dest, int32_t* perm,
+                               hipStream_t stream);
 
 // Random capacity dropping: thresh[e] = the largest kept key (priority << 32 | token) of expert
 // e (all ones when within capacity); a slot is kept iff its key <= thresh[its expert].
