@@ -11,7 +11,9 @@
 //   kScanChunk groups writes the bases within its chunk and the chunk's totals, then one
 //   workgroup scans the chunk totals) ->
 //   a slot's rank among its expert's slots is its group's base plus the number of lower lanes
-//   of its 16-lane group that chose the same expert (wave ballot).
+//   of its 16-lane group that chose the same expert (wave ballot). Under token-order dropping,
+//   a batch of at most one 64-token block per scan wave is ranked by the one-level scan
+//   kernel's own waves after its last barrier (one launch fewer).
 // A token never picks an expert twice, so ranks are unique and the result is bit-exact.
 #include "moe_common.h"
 #include "moe_kernels.h"
