@@ -440,10 +440,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const int l16 = lane & 15, lg = lane >> 4;
   const int slot = (lg ^ chunk_swizzle(l16)) * 16;   // rows 16 i + l16: same swizzle as row l16
-  const int a_frag = (wm * 128 + l16) * ROWB + slot;
-  const int a_frag_ap = (wm * 128 + l16) * PAIRB;    // paired A: row of the pair buffer; swizzle l16 mod 8
-  const int b_frag_bp = (wn * 128 + l16) * PAIRB;    // paired B
-  const int b_frag = (wn * 128 + l16) * ROWB + slot;
+  // Wave tiles: a 2 x 2 grid of 128 x 128 (rows wm*128.., columns wn*128..), or, on a WIDE tile
+  // (at most 128 segment rows), rows 0..127 and columns wave*64.. for every wave, so that all
+  // four SIMDs multiply where the 2 x 2 grid would leave the lower two waves without rows.
+  auto wave_rows = [&](auto wide) { return decltype(wide)::value ? 0 : wm * 128; };
+  auto wave_cols = [&](auto wide) { return decltype(wide)::value ? wave * 64 : wn * 128; };
   // BNM transpose reads: lane (group lg, 4u + q) reads k-rows 8 lg + 4 h + u of block j at the
   // 8 bytes of columns wn*128 + 16 j + 4 q; the swizzle depends on u and lg only (not on h)
   const int tr_u = (lane & 15) >> 2, tr_q = lane & 3;
@@ -459,13 +460,17 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   // (bf16) or 32 lanes (float) store each row's 256 or 512 contiguous bytes, so every store
   // covers whole cache lines. N is a multiple of 64, so each 16-byte piece lies wholly inside
   // or outside [0, N). Only the NI row blocks the wave multiplied can hold segment rows.
-  auto epilogue = [&](auto ni_const, auto bias_const, auto pre_const) {
+  auto epilogue = [&](auto ni_const, auto bias_const, auto pre_const, auto wide_const) {
     constexpr int NI = decltype(ni_const)::value;
     constexpr bool BIAS = decltype(bias_const)::value;
     constexpr bool PRE = decltype(pre_const)::value;       // also store the activation's input
+    constexpr bool WIDE = decltype(wide_const)::value;
+    constexpr int WC = WIDE ? 64 : 128;                    // columns of the wave tile
+    constexpr int NJ = WC / 16;                            // its 16-column MFMA blocks
+    const int rbase = wave_rows(wide_const), cbase = wave_cols(wide_const);
     constexpr int OB = EPI == kEpiLinear ? 4 : 2;         // output bytes per element
     constexpr int PITCH = 128 * OB + 16;                   // bytes per staged row (padded)
-    constexpr int CPRW = 128 * OB / 16;                    // 16-byte pieces per row
+    constexpr int CPRW = WC * OB / 16;                     // 16-byte pieces per row
     constexpr int RPW = 64 / CPRW;                         // rows per wave store
     static_assert((EPI == kEpiLinear ? 4 : 8) * 32 * PITCH <= NS * STAGE, "epilogue staging fits the operand ring");
     static_assert(4 * 32768 <= NS * STAGE, "the gradient epilogue's act_in blocks fit the operand ring");
@@ -483,8 +488,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int it = 0; it < 32 / RPW; ++it) {
         const int rr = it * RPW + lane / CPRW, pc = lane % CPRW;
-        const int rl = wm * 128 + i * 32 + rr;
-        const int cl = wn * 128 + pc * (16 / OB);
+        const int rl = rbase + i * 32 + rr;
+        const int cl = cbase + pc * (16 / OB);
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * PITCH + pc * 16);
         if (m0 + rl < m_e && n0 + cl < N) {
           u32x4* dst = reinterpret_cast<u32x4*>(base + (static_cast<size_t>(rl) * bpitch + cl) * OB);
@@ -504,10 +509,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
     auto rows_out_tiled = [&](const char* stage, int i) {
       char* pbase = static_cast<char*>(g.out) + static_cast<size_t>(panel) * (N / BK) * TILE;
 #pragma unroll
-      for (int it = 0; it < 8; ++it) {
+      for (int it = 0; it < WC / 16; ++it) {
         const int j = it >> 1, rr = 16 * (it & 1) + (lane & 15), pc = lane >> 4;
-        const int rl = wm * 128 + i * 32 + rr;             // row within the tile = row of the panel
-        const int cb = n0 + wn * 128 + 32 * j;             // first column of the chunk
+        const int rl = rbase + i * 32 + rr;                // row within the tile = row of the panel
+        const int cb = n0 + cbase + 32 * j;                // first column of the chunk
         const u32x4 v = *reinterpret_cast<const u32x4*>(stage + rr * PITCH + (32 * j + 8 * pc) * OB);
         if (m0 + rl < m_e && cb < N)
           __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(pbase + static_cast<size_t>(cb / BK) * TILE +
@@ -519,14 +524,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int rl = 16 * h + l16;                      // row within the 32-row block
           const int cl = j * 16 + 4 * lg;                   // column within the wave tile
           float o[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u)   // one addition either way: GeLU then needs no canonicalisation
             o[u] = acc[2 * i + h][j][u] +
-                   (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + wn * 128 + cl + u, N - 1), true)
+                   (BIAS ? load_bias(g.bias, static_cast<size_t>(e) * N + min(n0 + cbase + cl + u, N - 1), true)
                          : 0.0f);
           char* dst = st + rl * PITCH + cl * OB;
           if constexpr (EPI != kEpiLinear) {
@@ -629,11 +634,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
   // The wave multiplies only the 32-row blocks of its 128 rows that hold segment rows (2 or 4
   // of them; rows past the segment are never stored). Every wave still issues its share of
   // the loads and takes every barrier.
-  auto mainloop = [&](auto ni_const) {
+  auto mainloop = [&](auto ni_const, auto wide_const) {
     constexpr int NI = decltype(ni_const)::value;
     constexpr int NR = 2 * NI;                         // 16-row MFMA blocks multiplied
+    constexpr bool WIDE = decltype(wide_const)::value;
+    constexpr int NJ = WIDE ? 4 : 8;                   // 16-column MFMA blocks of the wave tile
+    const int rbase = wave_rows(wide_const), cbase = wave_cols(wide_const);
+    const int a_frag = (rbase + l16) * ROWB + slot;
+    const int a_frag_ap = (rbase + l16) * PAIRB;       // paired A: row of the pair buffer; swizzle l16 mod 8
+    const int b_frag_bp = (cbase + l16) * PAIRB;       // paired B
+    const int b_frag = (cbase + l16) * ROWB + slot;
     // A fragments single-buffered (row i's next one is read once row i's MFMAs are issued), B
-    // fragments double-buffered by step parity (the next ones are read during rows 0..3)
+    // fragments double-buffered by step parity (the next ones are read during rows 0..NJ/2-1)
     bf16x8 fa[8], fb[2][8];
     auto rd_a = [&](int st, int i) {
       if constexpr (AP)
@@ -680,9 +692,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
           issue1(s + NS - 1, i);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           if (i < NR) mfma_16x16x32<FIRST>(acc[i][j], fb[F][j], fa[i]);
-          if (NR > 0 && i < 4 && (j == 1 || j == 3)) rd_b(s + 1, F ^ 1, 2 * i + (j == 3));
+          if (NR > 0 && i < NJ / 2 && (j == 1 || j == 3)) rd_b(s + 1, F ^ 1, 2 * i + (j == 3));
         }
         if (i < NR) rd_a(s + 1, i);         // past the last step this reads unused data
       }
@@ -712,7 +724,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if (i < NR) rd_a(0, i);
-      if (NR > 0) rd_b(0, 0, i);
+      if (NR > 0 && i < NJ) rd_b(0, 0, i);
     }
     using F0 = std::integral_constant<int, 0>;
     using F1 = std::integral_constant<int, 1>;
@@ -729,33 +741,45 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < NR; ++i)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+      for (int j = 0; j < NJ; ++j) asm volatile("" : "+a"(acc[i][j]));
     wait_vmcnt<0>();     // the trailing re-loads must land before the workgroup's LDS is released
     if constexpr (is_grad_epi(EPI)) {
       grad_epilogue(ni_const);
       return;
     }
-    if constexpr (EPI == kEpiGelu || EPI == kEpiSilu) {
+    if constexpr (!WIDE && (EPI == kEpiGelu || EPI == kEpiSilu)) {
       if (g.pre != nullptr) {
         if (add_bias)
-          epilogue(ni_const, std::true_type{}, std::true_type{});
+          epilogue(ni_const, std::true_type{}, std::true_type{}, wide_const);
         else
-          epilogue(ni_const, std::false_type{}, std::true_type{});
+          epilogue(ni_const, std::false_type{}, std::true_type{}, wide_const);
         return;
       }
     }
     if (add_bias)
-      epilogue(ni_const, std::true_type{}, std::false_type{});
+      epilogue(ni_const, std::true_type{}, std::false_type{}, wide_const);
     else
-      epilogue(ni_const, std::false_type{}, std::false_type{});
+      epilogue(ni_const, std::false_type{}, std::false_type{}, wide_const);
   };
+  // A tile with at most 128 segment rows runs WIDE (the forward products only: not the N-major
+  // B operand, the gradient epilogues, the weight-gradient mode or a training forward storing
+  // its pre-activations). Uniform per workgroup.
+  if constexpr (!BNM && !is_grad_epi(EPI)) {
+    if (!g.wgrad && g.pre == nullptr && m_e - m0 <= 128) {
+      if (m_e - m0 > 64)
+        mainloop(std::integral_constant<int, 4>{}, std::true_type{});
+      else
+        mainloop(std::integral_constant<int, 2>{}, std::true_type{});
+      return;
+    }
+  }
   const int valid = m_e - m0 - wm * 128;     // segment rows in this wave's 128 rows
   if (valid > 64)
-    mainloop(std::integral_constant<int, 4>{});
+    mainloop(std::integral_constant<int, 4>{}, std::false_type{});
   else if (valid > 0)
-    mainloop(std::integral_constant<int, 2>{});
+    mainloop(std::integral_constant<int, 2>{}, std::false_type{});
   else
-    mainloop(std::integral_constant<int, 0>{});
+    mainloop(std::integral_constant<int, 0>{}, std::false_type{});
 }
 
 // ---------------------------------------------------------------------------------------
