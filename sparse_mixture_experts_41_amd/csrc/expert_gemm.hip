@@ -256,7 +256,8 @@ __device__ __forceinline__ void barrier_no_lds_wait() { asm volatile("s_barrier"
 // ---------------------------------------------------------------------------------------
 // bf16 grouped GEMM C[r, n] = sum_k A[r, k] B_e[n, k] over each expert's row segment.
 // 256 x 256 workgroup tile, 4 waves in a 2x2 grid of 128 x 128 wave tiles, each an 8x8 grid of
-// v_mfma_f32_16x16x32_bf16 blocks (256 accumulators per lane). The 16x16x32 form moves a quarter
+// v_mfma_f32_16x16x32_bf16 blocks (256 accumulators per lane); a forward tile with at most 128
+// segment rows runs WIDE instead, the 4 waves side by side over rows 0..127 (128 x 64 each). The 16x16x32 form moves a quarter
 // of the accumulator data per flop that 32x32x16 does and runs at a higher clock under load.
 // The MFMAs are written as inline asm with each accumulator tied to one AGPR quad (destination
 // = srcC): left to itself the compiler shuffles these 64 accumulators between register files.
