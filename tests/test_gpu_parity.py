@@ -64,6 +64,13 @@ SMALL = {
     # GEMM2 over K = 8192 (256 K steps) on 40 row tiles: each XCD's 5 tiles are split into 6 K
     # parts of 42 or 44 steps, pair-staged W2 rows ending exactly at the end of W2
     "split_p6": (MoEShape("split_p6", T=4800, d=256, E=8, k=2, d_ffn=8192, capacity_factor=1.25), 0.05),
+    # C = 119: every row tile holds at most 128 rows and runs WIDE (the four waves side by side,
+    # 64 columns each), some at most 64; d = 320 and d_ffn = 192 leave waves with part or none
+    # of their columns inside N; biases set
+    "wide_tiles": (MoEShape("wide_tiles", T=1900, d=320, E=32, k=2, d_ffn=192, capacity_factor=1.0), 0.1),
+    # WIDE tiles under the tail split: GEMM2 has 4 tiles, each cut into 8 K parts written to the
+    # side buffer and added by the fixup kernel
+    "wide_split": (MoEShape("wide_split", T=200, d=256, E=4, k=2, d_ffn=2048, capacity_factor=1.0), 0.05),
 }
 
 
