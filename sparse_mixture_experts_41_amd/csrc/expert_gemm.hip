@@ -748,7 +748,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       grad_epilogue(ni_const);
       return;
     }
-    if constexpr (!WIDE && (EPI == kEpiGelu || EPI == kEpiSilu)) {
+    if constexpr (EPI == kEpiGelu || EPI == kEpiSilu) {
       if (g.pre != nullptr) {
         if (add_bias)
           epilogue(ni_const, std::true_type{}, std::true_type{}, wide_const);
@@ -763,10 +763,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(GemmArgs g) {
       epilogue(ni_const, std::false_type{}, std::false_type{}, wide_const);
   };
   // A tile with at most 128 segment rows runs WIDE (the forward products only: not the N-major
-  // B operand, the gradient epilogues, the weight-gradient mode or a training forward storing
-  // its pre-activations). Uniform per workgroup.
+  // B operand, the gradient epilogues or the weight-gradient mode). Uniform per workgroup.
   if constexpr (!BNM && !is_grad_epi(EPI)) {
-    if (!g.wgrad && g.pre == nullptr && m_e - m0 <= 128) {
+    if (!g.wgrad && m_e - m0 <= 128) {
       if (m_e - m0 > 64)
         mainloop(std::integral_constant<int, 4>{}, std::true_type{});
       else
