@@ -169,10 +169,19 @@ def test_dispatch_from_given_indices_is_bit_exact():
     np.testing.assert_array_equal(out["x_perm"].float().cpu().numpy()[:n], p.host["x"][ref["perm"]])
 
 
-def test_forward_is_deterministic():
-    shape = MoEShape("det", T=2048, d=256, E=8, k=2, d_ffn=512, capacity_factor=1.0, gumbel=True,
-                     temperature=0.5)
-    p = Problem(shape)
+DET_SHAPES = {
+    "full_tiles": MoEShape("det", T=2048, d=256, E=8, k=2, d_ffn=512, capacity_factor=1.0, gumbel=True,
+                           temperature=0.5),
+    # about 125 rows per expert: WIDE GEMM tiles, and the permutation fused into the scan
+    "wide_fused": MoEShape("det_wide", T=1000, d=192, E=16, k=2, d_ffn=320, capacity_factor=1.0, gumbel=True,
+                           temperature=0.7),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DET_SHAPES))
+def test_forward_is_deterministic(name):
+    shape = DET_SHAPES[name]
+    p = Problem(shape, bias_std=0.05)
     a = run_forward(p)
     b = run_forward(p)
     for key in a:
