@@ -249,24 +249,29 @@ def check_output(y_gpu, y_ref, dtype, label="", rms=None, bound_rms=None):
 def bf16_h_arithmetic(p: Problem, ref: dict) -> np.ndarray:
     """The oracle's layer output with the one extra rounding the bf16 path makes by design: H,
     the expert's hidden activation and the second GEMM's MFMA operand, rounded to bf16 (float64
-    elsewhere, y not rounded). Built from the oracle's own steps on the oracle's dispatch; for
-    plain problems (no shared expert)."""
-    assert p.shared_d_ffn == 0
+    elsewhere, y not rounded). Built from the oracle's own steps on the oracle's dispatch and
+    weights; a shared expert's hidden layer is rounded the same way and its output added."""
     h, act = p.host, {"gelu": oracle.gelu, "silu": oracle.silu}[p.activation]
+
+    def ffn_h(rows, W1e, b1e, W2e, b2e):
+        pre = rows @ np.asarray(W1e, np.float64).T
+        if b1e is not None:
+            pre = pre + np.asarray(b1e, np.float64)
+        out = bf16_rne(act(pre)) @ np.asarray(W2e, np.float64).T
+        return out + np.asarray(b2e, np.float64) if b2e is not None else out
+
     x_perm, kept, offsets = ref["x_perm"], ref["kept"], ref["offsets"]
     y_perm = np.zeros((x_perm.shape[0], p.shape.d), dtype=np.float64)
     for e in range(p.shape.E):
         n, lo = int(kept[e]), int(offsets[e])
         if n == 0:
             continue
-        pre = x_perm[lo:lo + n] @ np.asarray(h["W1"][e], np.float64).T
-        if h["b1"] is not None:
-            pre = pre + np.asarray(h["b1"][e], np.float64)
-        ye = bf16_rne(act(pre)) @ np.asarray(h["W2"][e], np.float64).T
-        if h["b2"] is not None:
-            ye = ye + np.asarray(h["b2"][e], np.float64)
-        y_perm[lo:lo + n] = ye
-    return oracle.combine(y_perm, ref["dest"], ref["w"])
+        y_perm[lo:lo + n] = ffn_h(x_perm[lo:lo + n], h["W1"][e], None if h["b1"] is None else h["b1"][e],
+                                  h["W2"][e], None if h["b2"] is None else h["b2"][e])
+    y = oracle.combine(y_perm, ref["dest"], ref["w"])
+    if p.shared_host is not None:
+        y = y + ffn_h(np.asarray(h["x"], np.float64), *p.shared_host)
+    return y
 
 
 def check_forward_full(p: Problem, gpu: dict | None = None, h_margin: float | None = None) -> dict:

@@ -14,6 +14,11 @@ check that carries a case where the bf16 H by itself is further than 1e-2 rms fr
 (the computation's half of the 2e-2 bound; a single dominant expert per token at k = 7 puts
 some rows at 4.5 rms), where the bound against the oracle becomes that distance plus 1e-2.
 
+test_variant_sweep draws 16 more with the forward variants combined at random: SiLU or GeLU
+experts, Gaussian router noise, a shared expert, the three capacity policies, routing statistics
+and packed expert weights, under the same checks (the bf16-H arithmetic includes the shared
+expert's own rounded hidden layer).
+
 test_backward_sweep draws 12 more shapes the same way for the training pass (moe_forward_train +
 moe_backward) under every capacity policy, both activations, Gaussian router noise and the
 balance term, with the backward tests' tolerances.
@@ -116,3 +121,45 @@ def test_backward_sweep(i):
     fro, mx = BACKWARD_TOL[shape.dtype]
     for key, (e_fro, e_max) in errs.items():
         assert e_fro <= fro and e_max <= mx, f"{key}: relative Frobenius {e_fro:.3e}, max {e_max:.3e}"
+
+
+def _variant_shapes(n: int = 16, seed: int = 20261205):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        f32 = i % 4 == 3
+        E = int(rng.choice([2, 4, 7, 8, 16, 33, 64]))
+        k = int(rng.integers(1, min(8, E) + 1))
+        T = int(rng.choice([5, 64, 300, 1000, 2500]))
+        packed = False
+        if f32:
+            T = min(T, 600)
+            d, dff = 8 * int(rng.integers(2, 25)), 8 * int(rng.integers(2, 33))
+            ds = int(rng.choice([0, 0, 8 * int(rng.integers(1, 33))]))
+        else:
+            packed = bool(rng.integers(0, 2))
+            unit = 256 if packed else 64
+            d, dff = unit * int(rng.integers(1, 4 if packed else 9)), unit * int(rng.integers(1, 4 if packed else 9))
+            ds = int(rng.choice([0, 0, 64 * int(rng.integers(1, 9))]))
+        noise = float(rng.choice([0.0, 0.0, 0.3]))
+        gumbel = noise == 0.0 and bool(rng.integers(0, 2))
+        shape = MoEShape(f"var_sweep{i}", T=T, d=d, E=E, k=k, d_ffn=dff,
+                         capacity_factor=float(rng.choice([0.5, 0.8, 1.0, 1.5])),
+                         temperature=float(rng.choice([1.0, 0.7])), gumbel=gumbel, dtype="f32" if f32 else "bf16",
+                         seed=3000 + i, wg_std=0.02)
+        opts = dict(bias_std=float(rng.choice([0.0, 0.05])), activation=str(rng.choice(["gelu", "silu"])),
+                    noise_std=noise, shared_d_ffn=ds, drop_policy=str(rng.choice(["token", "random", "reroute"])),
+                    route_stats=bool(rng.integers(0, 2)), packed_weights=packed)
+        out.append((shape, opts))
+    return out
+
+
+VARIANT_SHAPES = _variant_shapes()
+
+
+@pytest.mark.parametrize("i", range(len(VARIANT_SHAPES)))
+def test_variant_sweep(i):
+    shape, opts = VARIANT_SHAPES[i]
+    print(f"[gpu] variant sweep {i}: {shape} {opts}", flush=True)
+    res = check_forward_full(Problem(shape, **opts), h_margin=H_MARGIN)
+    print(f"[gpu]   variant sweep {i}: {res}", flush=True)
