@@ -78,7 +78,10 @@ typedef struct moe_config {
 } moe_config;
 
 /* Number of kernel stages of moe_forward (route, scan, permute+gather, expert GEMM1+GeLU,
- * expert GEMM2, combine); moe_forward_aux.stage_events takes MOE_FORWARD_STAGES + 1 events. */
+ * expert GEMM2, combine); moe_forward_aux.stage_events takes MOE_FORWARD_STAGES + 1 events.
+ * Under token-order dropping the permutation is recorded in the scan stage (for batches of at
+ * most 1024 tokens it runs inside the scan kernel), so the third stage holds only the gather,
+ * which the bf16 expert paths usually fuse into their operand loads: it can be empty. */
 #define MOE_FORWARD_STAGES 6
 
 /* Optional extra outputs of moe_forward. Every pointer may be NULL. */
